@@ -1,0 +1,317 @@
+"""ctypes binding of libatlas (include/atlas.h), with the same entry-point names.
+
+Argument marshalling only: tensors are checked for device, dtype, layout and
+shape, their sizes are filled into the C argument structs, and the call runs
+on torch's current HIP stream.  Every step of the computation runs in the HIP
+kernels of libatlas.so; if the library is missing, importing this module
+raises -- there is no other implementation behind these names.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+import torch
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libatlas.so")
+
+ATLAS_OK = 0
+ATLAS_ERR_NULL = 1
+ATLAS_ERR_SHAPE = 2
+ATLAS_ERR_RANGE = 3
+ATLAS_ERR_UNSUPPORTED = 4
+ATLAS_ERR_WORKSPACE = 5
+ATLAS_ERR_POOL = 6
+ATLAS_ERR_NONFINITE = 7
+ATLAS_ERR_DEVICE = 8
+
+ATLAS_DTYPE_F32 = 0
+ATLAS_DTYPE_BF16 = 1
+
+ABI_VERSION = 1
+
+_DTYPES = {torch.float32: ATLAS_DTYPE_F32, torch.bfloat16: ATLAS_DTYPE_BF16}
+
+
+class AttnArgs(ctypes.Structure):
+    _fields_ = [
+        ("dtype", ctypes.c_int32),
+        ("batch", ctypes.c_int32),
+        ("q_len", ctypes.c_int32),
+        ("num_q_heads", ctypes.c_int32),
+        ("num_kv_heads", ctypes.c_int32),
+        ("head_dim", ctypes.c_int32),
+        ("page_size", ctypes.c_int32),
+        ("num_phys_pages", ctypes.c_int32),
+        ("max_pages_per_seq", ctypes.c_int32),
+        ("split_tokens", ctypes.c_int32),
+        ("scale", ctypes.c_float),
+        ("reserved0", ctypes.c_int32),
+        ("head_map", ctypes.POINTER(ctypes.c_int32)),
+        ("q", ctypes.c_void_p),
+        ("k_pages", ctypes.c_void_p),
+        ("v_pages", ctypes.c_void_p),
+        ("page_table", ctypes.c_void_p),
+        ("context_lens", ctypes.c_void_p),
+        ("window", ctypes.c_void_p),
+        ("sink_tokens", ctypes.c_void_p),
+        ("softcap", ctypes.c_void_p),
+        ("out", ctypes.c_void_p),
+        ("lse", ctypes.c_void_p),
+        ("workspace", ctypes.c_void_p),
+        ("workspace_bytes", ctypes.c_size_t),
+    ]
+
+
+class RegenJob(ctypes.Structure):
+    _fields_ = [("seq", ctypes.c_int32), ("logical_page", ctypes.c_int32),
+                ("phys_page", ctypes.c_int32)]
+
+
+class RegenArgs(ctypes.Structure):
+    _fields_ = [
+        ("seed", ctypes.c_uint64),
+        ("layer", ctypes.c_int32),
+        ("dtype", ctypes.c_int32),
+        ("num_kv_heads", ctypes.c_int32),
+        ("head_dim", ctypes.c_int32),
+        ("page_size", ctypes.c_int32),
+        ("num_phys_pages", ctypes.c_int32),
+        ("num_jobs", ctypes.c_int32),
+        ("reserved0", ctypes.c_int32),
+        ("jobs", ctypes.c_void_p),
+        ("k_pages", ctypes.c_void_p),
+        ("v_pages", ctypes.c_void_p),
+    ]
+
+
+EXPORTS = ("atlas_abi_version", "atlas_status_str", "atlas_last_error",
+           "atlas_decode_workspace_bytes", "atlas_prefill_workspace_bytes",
+           "atlas_attend_decode", "atlas_attend_prefill", "atlas_regenerate_pages")
+
+
+def _load():
+    if not os.path.exists(LIB_PATH):
+        raise ImportError(f"libatlas.so is not built ({LIB_PATH}); run __graft_entry__.build() "
+                          "or python exact_paged_causal_amd/build.py")
+    lib = ctypes.CDLL(LIB_PATH)
+    lib.atlas_abi_version.restype = ctypes.c_int32
+    lib.atlas_abi_version.argtypes = []
+    lib.atlas_status_str.restype = ctypes.c_char_p
+    lib.atlas_status_str.argtypes = [ctypes.c_int32]
+    lib.atlas_last_error.restype = ctypes.c_char_p
+    lib.atlas_last_error.argtypes = []
+    for name in ("atlas_decode_workspace_bytes", "atlas_prefill_workspace_bytes"):
+        fn = getattr(lib, name)
+        fn.restype = ctypes.c_size_t
+        fn.argtypes = [ctypes.POINTER(AttnArgs)]
+    for name in ("atlas_attend_decode", "atlas_attend_prefill"):
+        fn = getattr(lib, name)
+        fn.restype = ctypes.c_int32
+        fn.argtypes = [ctypes.POINTER(AttnArgs), ctypes.c_void_p]
+    lib.atlas_regenerate_pages.restype = ctypes.c_int32
+    lib.atlas_regenerate_pages.argtypes = [ctypes.POINTER(RegenArgs), ctypes.c_void_p]
+    if lib.atlas_abi_version() != ABI_VERSION:
+        raise ImportError(f"libatlas ABI {lib.atlas_abi_version()} != binding ABI {ABI_VERSION}")
+    return lib
+
+
+lib = _load()
+
+
+class AtlasError(RuntimeError):
+    def __init__(self, status: int, where: str):
+        self.status = status
+        detail = lib.atlas_last_error().decode()
+        super().__init__(f"{where}: {lib.atlas_status_str(status).decode()} ({status}): {detail}")
+
+
+def atlas_abi_version() -> int:
+    return int(lib.atlas_abi_version())
+
+
+def atlas_status_str(status: int) -> str:
+    return lib.atlas_status_str(status).decode()
+
+
+def atlas_last_error() -> str:
+    return lib.atlas_last_error().decode()
+
+
+def _ptr(t):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _stream(stream):
+    if stream is None:
+        stream = torch.cuda.current_stream()
+    return ctypes.c_void_p(stream.cuda_stream)
+
+
+def _check(t, name, dtype=None, device=None, ndim=None):
+    if not isinstance(t, torch.Tensor):
+        raise TypeError(f"{name} must be a torch.Tensor")
+    if not t.is_cuda:
+        raise ValueError(f"{name} must be on the GPU")
+    if device is not None and t.device != device:
+        raise ValueError(f"{name} is on {t.device}, expected {device}")
+    if dtype is not None and t.dtype != dtype:
+        raise ValueError(f"{name} has dtype {t.dtype}, expected {dtype}")
+    if ndim is not None and t.dim() != ndim:
+        raise ValueError(f"{name} must have {ndim} dims, got {tuple(t.shape)}")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+
+
+def make_attn_args(q, k_pages, v_pages, page_table, context_lens, scale, *, head_map=None,
+                   window=None, sink_tokens=None, softcap=None, out=None, lse=None,
+                   workspace=None, split_tokens=0):
+    """Fill an AttnArgs from tensors (q [B][q_len][Hq][D], arenas
+    [num_phys][Hkv][P][D], page_table [B][max_pages] int32, context_lens [B]
+    int32).  Returns (args, keepalive)."""
+    if q.dtype not in _DTYPES:
+        raise ValueError(f"q dtype {q.dtype} unsupported (float32 or bfloat16)")
+    dev = q.device
+    _check(q, "q", ndim=4)
+    _check(k_pages, "k_pages", q.dtype, dev, 4)
+    _check(v_pages, "v_pages", q.dtype, dev, 4)
+    _check(page_table, "page_table", torch.int32, dev, 2)
+    _check(context_lens, "context_lens", torch.int32, dev, 1)
+    B, q_len, hq, d = q.shape
+    num_phys, hkv, P, dk = k_pages.shape
+    if v_pages.shape != k_pages.shape or dk != d:
+        raise ValueError("k_pages/v_pages shapes must match [num_phys][Hkv][P][D] with q's D")
+    if page_table.shape[0] != B or context_lens.shape[0] != B:
+        raise ValueError("page_table and context_lens need one row per sequence")
+    for name, t, dt in (("window", window, torch.int32), ("sink_tokens", sink_tokens, torch.int32),
+                        ("softcap", softcap, torch.float32)):
+        if t is not None:
+            _check(t, name, dt, dev, 1)
+            if t.shape[0] != B:
+                raise ValueError(f"{name} needs one entry per sequence")
+    if out is not None:
+        _check(out, "out", torch.float32, dev, 4)
+        if tuple(out.shape) != (B, q_len, hq, d):
+            raise ValueError("out must be [B][q_len][Hq][D] float32")
+    if lse is not None:
+        _check(lse, "lse", torch.float32, dev, 3)
+        if tuple(lse.shape) != (B, q_len, hq):
+            raise ValueError("lse must be [B][q_len][Hq] float32")
+    keep = []
+    hm_ptr = None
+    if head_map is not None:
+        hm = (ctypes.c_int32 * hq)(*[int(x) for x in head_map])
+        if len(head_map) != hq:
+            raise ValueError("head_map needs one entry per q-head")
+        keep.append(hm)
+        hm_ptr = ctypes.cast(hm, ctypes.POINTER(ctypes.c_int32))
+    a = AttnArgs()
+    a.dtype = _DTYPES[q.dtype]
+    a.batch, a.q_len, a.num_q_heads, a.num_kv_heads, a.head_dim = B, q_len, hq, hkv, d
+    a.page_size, a.num_phys_pages, a.max_pages_per_seq = P, num_phys, page_table.shape[1]
+    a.split_tokens = int(split_tokens)
+    a.scale = float(scale)
+    a.head_map = hm_ptr
+    a.q, a.k_pages, a.v_pages = _ptr(q), _ptr(k_pages), _ptr(v_pages)
+    a.page_table, a.context_lens = _ptr(page_table), _ptr(context_lens)
+    a.window, a.sink_tokens, a.softcap = _ptr(window), _ptr(sink_tokens), _ptr(softcap)
+    a.out, a.lse = _ptr(out), _ptr(lse)
+    if workspace is not None:
+        _check(workspace, "workspace", None, dev)
+        a.workspace = _ptr(workspace)
+        a.workspace_bytes = workspace.numel() * workspace.element_size()
+    return a, keep
+
+
+def atlas_decode_workspace_bytes(args: AttnArgs) -> int:
+    n = lib.atlas_decode_workspace_bytes(ctypes.byref(args))
+    if n == ctypes.c_size_t(-1).value:
+        raise AtlasError(lib_status_from_error(), "atlas_decode_workspace_bytes")
+    return int(n)
+
+
+def atlas_prefill_workspace_bytes(args: AttnArgs) -> int:
+    n = lib.atlas_prefill_workspace_bytes(ctypes.byref(args))
+    if n == ctypes.c_size_t(-1).value:
+        raise AtlasError(lib_status_from_error(), "atlas_prefill_workspace_bytes")
+    return int(n)
+
+
+def lib_status_from_error() -> int:
+    """Sizing calls report invalid arguments through SIZE_MAX; the status code
+    itself is not returned, so report it as a shape/range problem."""
+    return ATLAS_ERR_SHAPE
+
+
+def _attend(entry, ws_fn, q, k_pages, v_pages, page_table, context_lens, scale, out, lse,
+            workspace, stream, **kw):
+    B, q_len, hq, d = q.shape
+    if out is None:
+        out = torch.empty((B, q_len, hq, d), dtype=torch.float32, device=q.device)
+    if lse is None and kw.pop("want_lse", True):
+        lse = torch.empty((B, q_len, hq), dtype=torch.float32, device=q.device)
+    args, keep = make_attn_args(q, k_pages, v_pages, page_table, context_lens, scale, out=out,
+                                lse=lse, **kw)
+    if workspace is None:
+        need = ws_fn(args)
+        workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=q.device)
+        args.workspace = _ptr(workspace)
+        args.workspace_bytes = workspace.numel()
+    else:
+        _check(workspace, "workspace", None, q.device)
+        args.workspace = _ptr(workspace)
+        args.workspace_bytes = workspace.numel() * workspace.element_size()
+    st = getattr(lib, entry)(ctypes.byref(args), _stream(stream))
+    if st != ATLAS_OK:
+        raise AtlasError(st, entry)
+    return out, lse
+
+
+def atlas_attend_decode(q, k_pages, v_pages, page_table, context_lens, scale, *, head_map=None,
+                        window=None, sink_tokens=None, softcap=None, out=None, lse=None,
+                        workspace=None, split_tokens=0, stream=None, want_lse=True):
+    """Decode attention (q_len == 1).  Returns (out [B][1][Hq][D] f32, lse [B][1][Hq] f32)."""
+    return _attend("atlas_attend_decode", atlas_decode_workspace_bytes, q, k_pages, v_pages,
+                   page_table, context_lens, scale, out, lse, workspace, stream,
+                   head_map=head_map, window=window, sink_tokens=sink_tokens, softcap=softcap,
+                   split_tokens=split_tokens, want_lse=want_lse)
+
+
+def atlas_attend_prefill(q, k_pages, v_pages, page_table, context_lens, scale, *, head_map=None,
+                         window=None, sink_tokens=None, softcap=None, out=None, lse=None,
+                         workspace=None, split_tokens=0, stream=None, want_lse=True):
+    """Suffix-query attention (q_len >= 1).  Returns (out [B][q_len][Hq][D] f32, lse [B][q_len][Hq] f32)."""
+    return _attend("atlas_attend_prefill", atlas_prefill_workspace_bytes, q, k_pages, v_pages,
+                   page_table, context_lens, scale, out, lse, workspace, stream,
+                   head_map=head_map, window=window, sink_tokens=sink_tokens, softcap=softcap,
+                   split_tokens=split_tokens, want_lse=want_lse)
+
+
+def atlas_regenerate_pages(k_pages, v_pages, jobs, seed: int, layer: int = 0, stream=None):
+    """Regenerate whole pages into the arenas.  jobs: int32 [n][3] device tensor of
+    (seq, logical_page, phys_page)."""
+    if k_pages.dtype not in _DTYPES:
+        raise ValueError("arena dtype must be float32 or bfloat16")
+    _check(k_pages, "k_pages", None, None, 4)
+    _check(v_pages, "v_pages", k_pages.dtype, k_pages.device, 4)
+    if v_pages.shape != k_pages.shape:
+        raise ValueError("k_pages and v_pages must have the same shape")
+    n_jobs = 0
+    if jobs is not None and jobs.numel() > 0:
+        _check(jobs, "jobs", torch.int32, k_pages.device, 2)
+        if jobs.shape[1] != 3:
+            raise ValueError("jobs must be [n][3] int32")
+        n_jobs = jobs.shape[0]
+    num_phys, hkv, P, d = k_pages.shape
+    a = RegenArgs()
+    a.seed = int(seed) & 0xFFFFFFFFFFFFFFFF
+    a.layer = int(layer)
+    a.dtype = _DTYPES[k_pages.dtype]
+    a.num_kv_heads, a.head_dim, a.page_size, a.num_phys_pages = hkv, d, P, num_phys
+    a.num_jobs = n_jobs
+    a.jobs = _ptr(jobs) if n_jobs else None
+    a.k_pages, a.v_pages = _ptr(k_pages), _ptr(v_pages)
+    st = lib.atlas_regenerate_pages(ctypes.byref(a), _stream(stream))
+    if st != ATLAS_OK:
+        raise AtlasError(st, "atlas_regenerate_pages")

@@ -1,0 +1,465 @@
+// atlas_api.cpp -- the C ABI declared in include/atlas.h.
+//
+// Validates every host-visible argument before anything is launched (on an
+// error nothing is launched and no output is touched: the CFR-Atlas README,
+// "Validation and hardening", asks for checked layout arithmetic and
+// rejection of invalid configuration), builds the q-head <-> K/V-head groups,
+// plans the split-KV grid and dispatches to the kernels.  A shape with no
+// kernel returns ATLAS_ERR_UNSUPPORTED; there is no fallback path (ferrox-core
+// "kernel_registry": a missing kernel is loud, not silently slow).
+#include <hip/hip_runtime.h>
+
+#include <cmath>
+#include <cstdarg>
+#include <cstdio>
+#include <cstdlib>
+#include <cstring>
+#include <vector>
+
+#include "../../include/atlas.h"
+#include "kernels.h"
+#include "plan.h"
+
+namespace {
+
+thread_local char g_last_error[512] = "";
+
+int32_t fail(int32_t status, const char *fmt, ...)
+{
+    va_list ap;
+    va_start(ap, fmt);
+    std::vsnprintf(g_last_error, sizeof g_last_error, fmt, ap);
+    va_end(ap);
+    return status;
+}
+
+int32_t ok()
+{
+    g_last_error[0] = '\0';
+    return ATLAS_OK;
+}
+
+bool validate_mode()
+{
+    const char *v = std::getenv("ATLAS_VALIDATE");
+    return v && v[0] && std::strcmp(v, "0") != 0;
+}
+
+bool is_pow2(int64_t x) { return x > 0 && (x & (x - 1)) == 0; }
+
+int log2i(int64_t x)
+{
+    int s = 0;
+    while ((int64_t(1) << s) < x)
+        ++s;
+    return s;
+}
+
+// Checked a*b for non-negative operands; false on int64 overflow.
+bool mul_ok(int64_t a, int64_t b, int64_t *out)
+{
+    if (a < 0 || b < 0)
+        return false;
+    if (a != 0 && b > INT64_MAX / a)
+        return false;
+    *out = a * b;
+    return true;
+}
+
+enum class Path { SplitValu, SplitMfma, TiledPrefill };
+
+// Everything derived from the arguments before launching.
+struct Plan {
+    atlas::HeadGroups groups;
+    int page_shift = 0;
+    int max_context = 0;
+    int rows_per_item = 1;
+    int n_chunks = 1;
+    int split_tokens = 0;
+    int max_splits = 0;
+    int64_t rows_total = 0;
+    size_t workspace = 0;
+    Path path = Path::SplitValu;
+};
+
+constexpr size_t kWorkspaceHeader = 256;  // validation-mode flags live here
+constexpr int kTargetItems = 8192;        // split work items to aim for (~32 per CU)
+
+int32_t check_shapes(const atlas_attn_args *a, bool decode, Plan *p)
+{
+    if (!a)
+        return fail(ATLAS_ERR_NULL, "args is NULL");
+    if (a->dtype != ATLAS_DTYPE_F32 && a->dtype != ATLAS_DTYPE_BF16)
+        return fail(ATLAS_ERR_UNSUPPORTED, "dtype %d has no kernel (f32=0, bf16=1)", a->dtype);
+    if (a->batch < 1 || a->q_len < 1 || a->num_q_heads < 1 || a->num_kv_heads < 1)
+        return fail(ATLAS_ERR_SHAPE, "batch, q_len, num_q_heads, num_kv_heads must be >= 1");
+    if (decode && a->q_len != 1)
+        return fail(ATLAS_ERR_SHAPE, "atlas_attend_decode takes q_len == 1 (got %d)", a->q_len);
+    if (a->num_q_heads > atlas::kMaxHeads || a->num_kv_heads > atlas::kMaxHeads)
+        return fail(ATLAS_ERR_UNSUPPORTED, "at most %d q-heads and K/V heads", atlas::kMaxHeads);
+    if (a->head_dim != 64 && a->head_dim != 128)
+        return fail(ATLAS_ERR_UNSUPPORTED, "head_dim %d has no kernel (64 or 128)", a->head_dim);
+    if (a->page_size < 1)
+        return fail(ATLAS_ERR_SHAPE, "page_size must be >= 1");
+    if (!is_pow2(a->page_size) || a->page_size > 4096)
+        return fail(ATLAS_ERR_UNSUPPORTED, "page_size %d: powers of two up to 4096 only", a->page_size);
+    if (a->num_phys_pages < 1 || a->max_pages_per_seq < 1)
+        return fail(ATLAS_ERR_SHAPE, "num_phys_pages and max_pages_per_seq must be >= 1");
+    if (!std::isfinite(a->scale))
+        return fail(ATLAS_ERR_RANGE, "scale must be finite");
+
+    int64_t max_ctx = 0;
+    if (!mul_ok(a->max_pages_per_seq, a->page_size, &max_ctx) || max_ctx > INT32_MAX / 2)
+        return fail(ATLAS_ERR_RANGE, "max_pages_per_seq * page_size overflows");
+    if (a->q_len > max_ctx)
+        return fail(ATLAS_ERR_RANGE, "q_len %d exceeds the largest context %lld", a->q_len,
+                    (long long)max_ctx);
+    int64_t arena_elems = 0, t = 0;
+    if (!mul_ok(a->num_phys_pages, a->num_kv_heads, &t) || !mul_ok(t, a->page_size, &t) ||
+        !mul_ok(t, a->head_dim, &arena_elems))
+        return fail(ATLAS_ERR_RANGE, "arena size overflows");
+    int64_t rows = 0;
+    if (!mul_ok(a->batch, a->q_len, &t) || !mul_ok(t, a->num_q_heads, &rows) || rows > INT32_MAX)
+        return fail(ATLAS_ERR_RANGE, "batch * q_len * num_q_heads must stay below 2^31");
+    if ((int64_t)a->batch * a->max_pages_per_seq > INT32_MAX)
+        return fail(ATLAS_ERR_RANGE, "page table larger than 2^31 entries");
+    if (a->batch > 65535 || a->max_pages_per_seq > 65535 * 16)
+        return fail(ATLAS_ERR_RANGE, "batch must be <= 65535 and max_pages_per_seq <= 1048560");
+
+    // Head groups.
+    const int hq = a->num_q_heads, hkv = a->num_kv_heads;
+    std::vector<int> map(hq);
+    if (a->head_map) {
+        for (int h = 0; h < hq; ++h) {
+            if (a->head_map[h] < 0 || a->head_map[h] >= hkv)
+                return fail(ATLAS_ERR_SHAPE, "head_map[%d] = %d outside [0, %d)", h, a->head_map[h], hkv);
+            map[h] = a->head_map[h];
+        }
+    } else {
+        if (hq % hkv != 0)
+            return fail(ATLAS_ERR_SHAPE, "num_q_heads %d not a multiple of num_kv_heads %d (pass head_map)",
+                        hq, hkv);
+        for (int h = 0; h < hq; ++h)
+            map[h] = h / (hq / hkv);
+    }
+    std::memset(&p->groups, 0, sizeof p->groups);
+    int pos = 0, gmax = 0;
+    for (int g = 0; g < hkv; ++g) {
+        p->groups.start[g] = (int16_t)pos;
+        int n = 0;
+        for (int h = 0; h < hq; ++h)
+            if (map[h] == g) {
+                p->groups.list[pos++] = (int16_t)h;
+                p->groups.group_of[h] = (int16_t)g;
+                p->groups.slot_of[h] = (int16_t)n++;
+            }
+        gmax = n > gmax ? n : gmax;
+    }
+    p->groups.start[hkv] = (int16_t)pos;
+    p->groups.max_group = gmax;
+
+    p->page_shift = log2i(a->page_size);
+    p->max_context = (int)max_ctx;
+    p->rows_total = rows;
+
+    // Path.
+    const bool variants = a->window || a->sink_tokens || a->softcap;
+    if (!decode && a->dtype == ATLAS_DTYPE_BF16 && a->q_len >= 64 && !variants)
+        p->path = Path::TiledPrefill;
+    else
+        p->path = Path::SplitValu;
+
+    if (p->path == Path::TiledPrefill) {
+        p->workspace = kWorkspaceHeader;
+        return ok();
+    }
+
+    // Split-KV plan: rows of a K/V head per work item, then keys per split.
+    const int64_t rows_per_head = (int64_t)a->q_len * gmax;
+    int rpi = 1;
+    while (rpi < rows_per_head && rpi < 8)
+        rpi <<= 1;
+    p->rows_per_item = rpi;
+    p->n_chunks = (int)((rows_per_head + rpi - 1) / rpi);
+    const int64_t items_per_split = (int64_t)a->batch * hkv * p->n_chunks;
+    const int64_t max_t_by_lds = (int64_t)(atlas::kMaxSplitPages - 2) << p->page_shift;
+    int64_t T;
+    if (a->split_tokens != 0) {
+        if (a->split_tokens < 1)
+            return fail(ATLAS_ERR_RANGE, "split_tokens must be >= 0");
+        T = a->split_tokens;
+        if (T > max_t_by_lds)
+            return fail(ATLAS_ERR_RANGE, "split_tokens %d spans more than %d pages", a->split_tokens,
+                        atlas::kMaxSplitPages - 2);
+    } else {
+        T = (items_per_split * max_ctx + kTargetItems - 1) / kTargetItems;
+        T = ((T + 63) / 64) * 64;
+        if (T < 64)
+            T = 64;
+        if (T > 16384)
+            T = 16384;
+        if (T > max_t_by_lds)
+            T = max_t_by_lds;
+    }
+    p->split_tokens = (int)T;
+    p->max_splits = atlas::max_splits_bound((int)max_ctx, (int)T, a->sink_tokens != nullptr);
+    if ((int64_t)p->max_splits > 65535 || items_per_split / a->batch > 65535)
+        return fail(ATLAS_ERR_RANGE, "split grid too large (raise split_tokens)");
+    int64_t slots = 0, ws = 0;
+    if (!mul_ok(rows, p->max_splits, &slots) || !mul_ok(slots, (int64_t)(a->head_dim + 2) * 4, &ws))
+        return fail(ATLAS_ERR_RANGE, "workspace size overflows");
+    p->workspace = kWorkspaceHeader + (size_t)ws;
+    return ok();
+}
+
+int32_t check_pointers(const atlas_attn_args *a, const Plan &p)
+{
+    if (!a->q || !a->k_pages || !a->v_pages || !a->page_table || !a->context_lens || !a->out)
+        return fail(ATLAS_ERR_NULL, "q, k_pages, v_pages, page_table, context_lens and out are required");
+    if (p.workspace > 0) {
+        if (!a->workspace)
+            return fail(ATLAS_ERR_NULL, "workspace is required (%zu bytes)", p.workspace);
+        if (a->workspace_bytes < p.workspace)
+            return fail(ATLAS_ERR_WORKSPACE, "workspace of %zu bytes, %zu needed", a->workspace_bytes,
+                        p.workspace);
+    }
+    return ok();
+}
+
+// Validation mode: copy the device-resident lengths and page table to the
+// host, check them, and scan the visible inputs for NaN/Inf.
+int32_t validate_device(const atlas_attn_args *a, const Plan &p, hipStream_t stream)
+{
+    const int B = a->batch;
+    std::vector<int32_t> ctx(B), pt((size_t)B * a->max_pages_per_seq), win(B, 0), snk(B, 0);
+    hipError_t e = hipMemcpyAsync(ctx.data(), a->context_lens, sizeof(int32_t) * B, hipMemcpyDeviceToHost, stream);
+    if (e == hipSuccess)
+        e = hipMemcpyAsync(pt.data(), a->page_table, sizeof(int32_t) * pt.size(), hipMemcpyDeviceToHost, stream);
+    if (e == hipSuccess && a->window)
+        e = hipMemcpyAsync(win.data(), a->window, sizeof(int32_t) * B, hipMemcpyDeviceToHost, stream);
+    if (e == hipSuccess && a->sink_tokens)
+        e = hipMemcpyAsync(snk.data(), a->sink_tokens, sizeof(int32_t) * B, hipMemcpyDeviceToHost, stream);
+    if (e == hipSuccess)
+        e = hipStreamSynchronize(stream);
+    if (e != hipSuccess)
+        return fail(ATLAS_ERR_DEVICE, "validation copy failed: %s", hipGetErrorString(e));
+    for (int b = 0; b < B; ++b) {
+        if (ctx[b] < a->q_len || ctx[b] > p.max_context)
+            return fail(ATLAS_ERR_RANGE, "context_lens[%d] = %d outside [q_len=%d, %d]", b, ctx[b], a->q_len,
+                        p.max_context);
+        if (win[b] < 0 || snk[b] < 0)
+            return fail(ATLAS_ERR_RANGE, "window/sink_tokens[%d] negative", b);
+        const int np = (ctx[b] + a->page_size - 1) / a->page_size;
+        for (int lp = 0; lp < np; ++lp) {
+            const int32_t id = pt[(size_t)b * a->max_pages_per_seq + lp];
+            if (id < 0 || id >= a->num_phys_pages)
+                return fail(ATLAS_ERR_POOL, "page_table[%d][%d] = %d outside the pool of %d pages", b, lp, id,
+                            a->num_phys_pages);
+        }
+    }
+    // NaN/Inf scan of what the call will read; the flag word sits in the
+    // workspace header.
+    atlas::ScanArgs s{};
+    s.q = a->q;
+    s.k_pages = a->k_pages;
+    s.v_pages = a->v_pages;
+    s.page_table = a->page_table;
+    s.context_lens = a->context_lens;
+    s.flag = static_cast<int *>(a->workspace);
+    s.batch = a->batch;
+    s.q_len = a->q_len;
+    s.hq = a->num_q_heads;
+    s.hkv = a->num_kv_heads;
+    s.head_dim = a->head_dim;
+    s.page_shift = p.page_shift;
+    s.num_phys = a->num_phys_pages;
+    s.max_pages = a->max_pages_per_seq;
+    s.max_context = p.max_context;
+    int flag = 0;
+    e = hipMemsetAsync(s.flag, 0, sizeof(int), stream);
+    if (e == hipSuccess)
+        e = atlas::launch_scan(s, a->dtype, stream);
+    if (e == hipSuccess)
+        e = hipMemcpyAsync(&flag, s.flag, sizeof(int), hipMemcpyDeviceToHost, stream);
+    if (e == hipSuccess)
+        e = hipStreamSynchronize(stream);
+    if (e != hipSuccess)
+        return fail(ATLAS_ERR_DEVICE, "validation scan failed: %s", hipGetErrorString(e));
+    if (flag)
+        return fail(ATLAS_ERR_NONFINITE, "NaN or Inf in q or in the K/V rows the contexts cover");
+    return ok();
+}
+
+int32_t attend(const atlas_attn_args *a, void *stream_ptr, bool decode)
+{
+    Plan p;
+    int32_t st = check_shapes(a, decode, &p);
+    if (st != ATLAS_OK)
+        return st;
+    st = check_pointers(a, p);
+    if (st != ATLAS_OK)
+        return st;
+    hipStream_t stream = reinterpret_cast<hipStream_t>(stream_ptr);
+    if (validate_mode()) {
+        st = validate_device(a, p, stream);
+        if (st != ATLAS_OK)
+            return st;
+    }
+
+    if (p.path == Path::TiledPrefill) {
+        atlas::PrefillArgs k{};
+        k.q = a->q;
+        k.k_pages = a->k_pages;
+        k.v_pages = a->v_pages;
+        k.page_table = a->page_table;
+        k.context_lens = a->context_lens;
+        k.out = a->out;
+        k.lse = a->lse;
+        k.batch = a->batch;
+        k.q_len = a->q_len;
+        k.hq = a->num_q_heads;
+        k.hkv = a->num_kv_heads;
+        k.head_dim = a->head_dim;
+        k.page_shift = p.page_shift;
+        k.num_phys = a->num_phys_pages;
+        k.max_pages = a->max_pages_per_seq;
+        k.max_context = p.max_context;
+        k.scale = a->scale;
+        k.groups = p.groups;
+        hipError_t e = atlas::launch_prefill_mfma(k, stream);
+        if (e == hipErrorNotSupported)
+            return fail(ATLAS_ERR_UNSUPPORTED, "no tiled prefill kernel for this shape");
+        if (e != hipSuccess)
+            return fail(ATLAS_ERR_DEVICE, "prefill launch: %s", hipGetErrorString(e));
+        return ok();
+    }
+
+    atlas::SplitArgs k{};
+    k.q = a->q;
+    k.k_pages = a->k_pages;
+    k.v_pages = a->v_pages;
+    k.page_table = a->page_table;
+    k.context_lens = a->context_lens;
+    k.window = a->window;
+    k.sinks = a->sink_tokens;
+    k.softcap = a->softcap;
+    char *ws = static_cast<char *>(a->workspace) + kWorkspaceHeader;
+    const size_t acc_bytes = (size_t)p.rows_total * p.max_splits * a->head_dim * sizeof(float);
+    k.ws_acc = reinterpret_cast<float *>(ws);
+    k.ws_ml = reinterpret_cast<float *>(ws + acc_bytes);
+    k.out = a->out;
+    k.lse = a->lse;
+    k.batch = a->batch;
+    k.q_len = a->q_len;
+    k.hq = a->num_q_heads;
+    k.hkv = a->num_kv_heads;
+    k.head_dim = a->head_dim;
+    k.page_shift = p.page_shift;
+    k.num_phys = a->num_phys_pages;
+    k.max_pages = a->max_pages_per_seq;
+    k.max_context = p.max_context;
+    k.split_tokens = p.split_tokens;
+    k.max_splits = p.max_splits;
+    k.rows_per_item = p.rows_per_item;
+    k.n_chunks = p.n_chunks;
+    k.scale = a->scale;
+    k.groups = p.groups;
+
+    if (std::getenv("ATLAS_DEBUG"))
+        std::fprintf(stderr,
+                     "atlas: split-KV %s dtype=%d rows/item=%d chunks=%d split_tokens=%d max_splits=%d "
+                     "workspace=%zu\n",
+                     decode ? "decode" : "prefill", a->dtype, p.rows_per_item, p.n_chunks, p.split_tokens,
+                     p.max_splits, p.workspace);
+
+    hipError_t e = atlas::launch_split_valu(k, a->dtype, stream);
+    if (e != hipSuccess)
+        return fail(ATLAS_ERR_DEVICE, "split launch: %s", hipGetErrorString(e));
+    e = atlas::launch_merge(k, stream);
+    if (e != hipSuccess)
+        return fail(ATLAS_ERR_DEVICE, "merge launch: %s", hipGetErrorString(e));
+    return ok();
+}
+
+size_t workspace_bytes(const atlas_attn_args *a, bool decode)
+{
+    Plan p;
+    if (check_shapes(a, decode, &p) != ATLAS_OK)
+        return SIZE_MAX;
+    return p.workspace;
+}
+
+}  // namespace
+
+extern "C" {
+
+int32_t atlas_abi_version(void) { return ATLAS_ABI_VERSION; }
+
+const char *atlas_status_str(int32_t status)
+{
+    switch (status) {
+    case ATLAS_OK: return "ok";
+    case ATLAS_ERR_NULL: return "null pointer";
+    case ATLAS_ERR_SHAPE: return "invalid shape";
+    case ATLAS_ERR_RANGE: return "value out of range";
+    case ATLAS_ERR_UNSUPPORTED: return "unsupported (no kernel for this configuration)";
+    case ATLAS_ERR_WORKSPACE: return "workspace too small";
+    case ATLAS_ERR_POOL: return "page id outside the physical pool";
+    case ATLAS_ERR_NONFINITE: return "non-finite input";
+    case ATLAS_ERR_DEVICE: return "HIP runtime error";
+    default: return "unknown status";
+    }
+}
+
+const char *atlas_last_error(void) { return g_last_error; }
+
+size_t atlas_decode_workspace_bytes(const atlas_attn_args *args) { return workspace_bytes(args, true); }
+
+size_t atlas_prefill_workspace_bytes(const atlas_attn_args *args) { return workspace_bytes(args, false); }
+
+int32_t atlas_attend_decode(const atlas_attn_args *args, void *stream) { return attend(args, stream, true); }
+
+int32_t atlas_attend_prefill(const atlas_attn_args *args, void *stream) { return attend(args, stream, false); }
+
+int32_t atlas_regenerate_pages(const atlas_regen_args *a, void *stream)
+{
+    if (!a)
+        return fail(ATLAS_ERR_NULL, "args is NULL");
+    if (a->dtype != ATLAS_DTYPE_F32 && a->dtype != ATLAS_DTYPE_BF16)
+        return fail(ATLAS_ERR_UNSUPPORTED, "dtype %d has no kernel", a->dtype);
+    if (a->head_dim != 64 && a->head_dim != 128)
+        return fail(ATLAS_ERR_UNSUPPORTED, "head_dim %d has no kernel (64 or 128)", a->head_dim);
+    if (a->page_size < 1 || a->num_kv_heads < 1 || a->num_phys_pages < 1 || a->num_jobs < 0)
+        return fail(ATLAS_ERR_SHAPE, "page_size, num_kv_heads, num_phys_pages >= 1 and num_jobs >= 0 required");
+    if (!is_pow2(a->page_size) || a->page_size > 4096)
+        return fail(ATLAS_ERR_UNSUPPORTED, "page_size %d: powers of two up to 4096 only", a->page_size);
+    if (a->layer < 0 || a->layer >= (1 << 16))
+        return fail(ATLAS_ERR_RANGE, "layer must be in [0, 65536)");
+    if (a->num_kv_heads >= (1 << 30))
+        return fail(ATLAS_ERR_RANGE, "num_kv_heads must be below 2^30");
+    int64_t t = 0;
+    if (!mul_ok(a->num_phys_pages, a->num_kv_heads, &t) || !mul_ok(t, a->page_size, &t) ||
+        !mul_ok(t, a->head_dim, &t))
+        return fail(ATLAS_ERR_RANGE, "arena size overflows");
+    if (a->num_jobs == 0)
+        return ok();
+    if (!a->jobs || !a->k_pages || !a->v_pages)
+        return fail(ATLAS_ERR_NULL, "jobs, k_pages and v_pages are required");
+    atlas::RegenArgs k{};
+    k.seed = a->seed;
+    k.jobs = reinterpret_cast<const int32_t *>(a->jobs);
+    k.k_pages = a->k_pages;
+    k.v_pages = a->v_pages;
+    k.layer = a->layer;
+    k.hkv = a->num_kv_heads;
+    k.head_dim = a->head_dim;
+    k.page_shift = log2i(a->page_size);
+    k.num_phys = a->num_phys_pages;
+    k.n_jobs = a->num_jobs;
+    hipError_t e = atlas::launch_regen(k, a->dtype, reinterpret_cast<hipStream_t>(stream));
+    if (e != hipSuccess)
+        return fail(ATLAS_ERR_DEVICE, "regen launch: %s", hipGetErrorString(e));
+    return ok();
+}
+
+}  // extern "C"

@@ -1,0 +1,64 @@
+// device.h -- small gfx950 device helpers shared by the kernels.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace atlas {
+
+constexpr float kLog2e = 1.4426950408889634f;
+constexpr float kLn2 = 0.6931471805599453f;
+
+// DPP controls (GFX9 data-parallel primitives; operate inside 16-lane rows).
+constexpr int kDppQuadSwap1 = 0xB1;     // quad_perm [1,0,3,2]
+constexpr int kDppQuadSwap2 = 0x4E;     // quad_perm [2,3,0,1]
+constexpr int kDppRowHalfMirror = 0x141;
+constexpr int kDppRowMirror = 0x140;
+
+template <int Ctrl>
+__device__ __forceinline__ float dpp(float x)
+{
+    return __builtin_bit_cast(
+        float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, x), Ctrl, 0xF, 0xF, false));
+}
+
+// Sum over aligned groups of Lanes (4, 8 or 16) lanes; every lane gets the total.
+template <int Lanes>
+__device__ __forceinline__ float group_sum(float x)
+{
+    x += dpp<kDppQuadSwap1>(x);
+    x += dpp<kDppQuadSwap2>(x);
+    if constexpr (Lanes >= 8)
+        x += dpp<kDppRowHalfMirror>(x);
+    if constexpr (Lanes >= 16)
+        x += dpp<kDppRowMirror>(x);
+    return x;
+}
+
+template <int Lanes>
+__device__ __forceinline__ float group_max(float x)
+{
+    x = fmaxf(x, dpp<kDppQuadSwap1>(x));
+    x = fmaxf(x, dpp<kDppQuadSwap2>(x));
+    if constexpr (Lanes >= 8)
+        x = fmaxf(x, dpp<kDppRowHalfMirror>(x));
+    if constexpr (Lanes >= 16)
+        x = fmaxf(x, dpp<kDppRowMirror>(x));
+    return x;
+}
+
+// Hardware 2^x (v_exp_f32): exact 0 for -inf.
+__device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
+
+__device__ __forceinline__ float bf16_lo(uint32_t pair) { return __uint_as_float(pair << 16); }
+__device__ __forceinline__ float bf16_hi(uint32_t pair) { return __uint_as_float(pair & 0xFFFF0000u); }
+
+// fp32 -> bf16 bits, round to nearest even (finite inputs).
+__device__ __forceinline__ uint32_t f32_to_bf16_bits(float f)
+{
+    uint32_t u = __float_as_uint(f);
+    u += 0x7FFFu + ((u >> 16) & 1u);
+    return u >> 16;
+}
+
+}  // namespace atlas

@@ -1,0 +1,93 @@
+// kernels.h -- internal interface between the C ABI layer and the HIP kernels.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "plan.h"
+
+namespace atlas {
+
+constexpr int kMaxHeads = 256;
+
+// q-head <-> K/V-head grouping, built on the host from head_map and passed by
+// value in the kernel arguments (constant for the whole launch).
+struct HeadGroups {
+    int16_t start[kMaxHeads + 1];  // q-heads of K/V head g: list[start[g] .. start[g+1])
+    int16_t list[kMaxHeads];
+    int16_t group_of[kMaxHeads];   // q-head -> K/V head
+    int16_t slot_of[kMaxHeads];    // q-head -> its index inside the group
+    int32_t max_group;             // largest group size
+    int32_t pad;
+};
+
+// Everything a split-KV work item and the merge pass need.
+struct SplitArgs {
+    const void *q;
+    const void *k_pages;
+    const void *v_pages;
+    const int32_t *page_table;
+    const int32_t *context_lens;
+    const int32_t *window;      // may be null
+    const int32_t *sinks;       // may be null
+    const float *softcap;       // may be null
+    float *ws_acc;              // [rows][max_splits][D]  unnormalised accumulators
+    float *ws_ml;               // [rows][max_splits][2]  (running max in log2 units, sum)
+    float *out;                 // [B][q_len][Hq][D]
+    float *lse;                 // [B][q_len][Hq] or null
+    int32_t batch, q_len, hq, hkv, head_dim;
+    int32_t page_shift;         // log2(page_size)
+    int32_t num_phys, max_pages, max_context;
+    int32_t split_tokens, max_splits;
+    int32_t rows_per_item;      // rows of one work item (a chunk of a K/V head's rows)
+    int32_t n_chunks;           // chunks per K/V head
+    float scale;
+    HeadGroups groups;
+};
+
+struct RegenArgs {
+    uint64_t seed;
+    const int32_t *jobs;        // [n_jobs][3] (seq, logical page, physical page)
+    void *k_pages;
+    void *v_pages;
+    int32_t layer, hkv, head_dim, page_shift, num_phys, n_jobs;
+};
+
+// Largest page-id list one split work item stages in LDS.
+constexpr int kMaxSplitPages = 2048;
+
+hipError_t launch_split_valu(const SplitArgs &a, int dtype, hipStream_t stream);
+hipError_t launch_split_mfma(const SplitArgs &a, hipStream_t stream);
+hipError_t launch_merge(const SplitArgs &a, hipStream_t stream);
+hipError_t launch_regen(const RegenArgs &a, int dtype, hipStream_t stream);
+
+struct PrefillArgs {
+    const void *q;
+    const void *k_pages;
+    const void *v_pages;
+    const int32_t *page_table;
+    const int32_t *context_lens;
+    float *out;
+    float *lse;
+    int32_t batch, q_len, hq, hkv, head_dim, page_shift, num_phys, max_pages, max_context;
+    int32_t n_qblocks;          // query blocks per (sequence, K/V head)
+    float scale;
+    HeadGroups groups;
+};
+
+hipError_t launch_prefill_mfma(const PrefillArgs &a, hipStream_t stream);
+
+// Validation-mode NaN/Inf scan of q and the K/V rows each context covers.
+struct ScanArgs {
+    const void *q;
+    const void *k_pages;
+    const void *v_pages;
+    const int32_t *page_table;
+    const int32_t *context_lens;
+    int *flag;                  // set to nonzero on a hit (cleared by the caller)
+    int32_t batch, q_len, hq, hkv, head_dim, page_shift, num_phys, max_pages, max_context;
+};
+
+hipError_t launch_scan(const ScanArgs &a, int dtype, hipStream_t stream);
+
+}  // namespace atlas

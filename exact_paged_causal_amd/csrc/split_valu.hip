@@ -1,0 +1,313 @@
+// split_valu.hip -- split-KV fold on the vector ALUs (fp32 K/V).
+//
+// One workgroup (4 waves) = one work item (sequence b, K/V head g, chunk of
+// rows, split s).  Its keys are the span plan.h assigns to split s; every
+// visible key is folded, for every row of the chunk, into an online-softmax
+// state (running max m, sum l, accumulator acc) -- CFR-Atlas README: each
+// page is folded into online softmax; CPUAttn README "Operator model": a
+// split is allowed because a structured merge (merge.hip) recombines it.
+//
+// Lane layout.  A K or V row of D elements is read by a group of R lanes
+// (R = 16 for 256-byte rows, 8 for 128-byte rows), each lane loading NL
+// 16-byte pieces; one load instruction of a wave therefore covers 64/R whole
+// rows (1 KiB contiguous when they sit in one page).  Each lane keeps its
+// slice of q and acc for every row of the chunk in registers.  Dot products
+// are reduced across the R lanes with DPP row operations; exp2 runs on the
+// hardware v_exp_f32 with the scale folded by log2(e).  Page ids of the
+// split are staged once in LDS, so the per-key address math is scalar-free
+// shifts and masks (page sizes are powers of two).
+#include "device.h"
+#include "kernels.h"
+
+namespace atlas {
+namespace {
+
+template <typename E>
+struct Elem;
+
+template <>
+struct Elem<float> {
+    static constexpr int kPer16 = 4;
+    __device__ static void unpack(const uint4 &c, float *out)
+    {
+        out[0] = __uint_as_float(c.x);
+        out[1] = __uint_as_float(c.y);
+        out[2] = __uint_as_float(c.z);
+        out[3] = __uint_as_float(c.w);
+    }
+};
+
+template <>
+struct Elem<uint16_t> {  // bf16 bit patterns
+    static constexpr int kPer16 = 8;
+    __device__ static void unpack(const uint4 &c, float *out)
+    {
+        out[0] = bf16_lo(c.x);
+        out[1] = bf16_hi(c.x);
+        out[2] = bf16_lo(c.y);
+        out[3] = bf16_hi(c.y);
+        out[4] = bf16_lo(c.z);
+        out[5] = bf16_hi(c.z);
+        out[6] = bf16_lo(c.w);
+        out[7] = bf16_hi(c.w);
+    }
+};
+
+template <typename E, int D, int MC, int KU>
+__global__ __launch_bounds__(256) void split_valu_kernel(SplitArgs a)
+{
+    constexpr int EPC = Elem<E>::kPer16;                 // elements per 16-byte piece
+    constexpr int ROWB = D * (int)sizeof(E);             // bytes per K/V row
+    constexpr int R = ROWB / 16 >= 16 ? 16 : ROWB / 16;  // lanes per row
+    constexpr int NL = ROWB / (R * 16);                  // pieces per lane per row
+    constexpr int DPL = NL * EPC;                        // dims per lane
+    constexpr int GPW = 64 / R;                          // row groups per wave
+    constexpr int KPI = 4 * GPW * KU;                    // keys per iteration per workgroup
+    static_assert(R == 8 || R == 16, "row group");
+
+    __shared__ int32_t s_pid[kMaxSplitPages];
+    __shared__ float s_m[4][MC];
+    __shared__ float s_l[4][MC];
+    __shared__ float s_acc[4][MC][D];
+
+    const int tid = threadIdx.x;
+    const int wave = tid >> 6;
+    const int lane = tid & 63;
+    const int grp = lane / R;
+    const int li = lane % R;
+
+    const int split = blockIdx.x;
+    const int g = blockIdx.y / a.n_chunks;
+    const int chunk = blockIdx.y - g * a.n_chunks;
+    const int b = blockIdx.z;
+    const int gstart = a.groups.start[g];
+    const int gsize = a.groups.start[g + 1] - gstart;
+
+    int ctx = a.context_lens[b];
+    ctx = ctx < 0 ? 0 : (ctx > a.max_context ? a.max_context : ctx);
+    const ChunkRows cr = chunk_rows(chunk, MC, gsize, a.q_len, ctx);
+    if (cr.r0 >= cr.r1)
+        return;
+    const int W = a.window ? a.window[b] : 0;
+    const int S = a.sinks ? a.sinks[b] : 0;
+    const float cap = a.softcap ? a.softcap[b] : 0.0f;
+    const SplitPlan plan = plan_splits(cr.pos_min, cr.pos_max, W, S, a.split_tokens);
+    if (split >= plan.n_splits)
+        return;
+    int ka, kb;
+    split_range(plan, split, a.split_tokens, &ka, &kb);
+
+    // Stage the split's physical page ids (clamped into the arena).
+    const int ps = a.page_shift;
+    const int pmask = (1 << ps) - 1;
+    const int p0 = ka >> ps;
+    const int np = ((kb - 1) >> ps) - p0 + 1;
+    for (int t = tid; t < np; t += 256) {
+        int pid = a.page_table[(int64_t)b * a.max_pages + p0 + t];
+        s_pid[t] = ((unsigned)pid < (unsigned)a.num_phys) ? pid : 0;
+    }
+
+    // Query slices and positions of the chunk's rows.
+    float q[MC][DPL];
+    int pos[MC];
+#pragma unroll
+    for (int r = 0; r < MC; ++r) {
+        const int rr = cr.r0 + r;
+        if (rr < cr.r1) {
+            const int i = rr / gsize;
+            const int h = a.groups.list[gstart + rr % gsize];
+            pos[r] = ctx - a.q_len + i;
+            const E *qrow = reinterpret_cast<const E *>(a.q) +
+                            (((int64_t)b * a.q_len + i) * a.hq + h) * D;
+#pragma unroll
+            for (int n = 0; n < NL; ++n) {
+                uint4 c = *reinterpret_cast<const uint4 *>(qrow + n * R * EPC + li * EPC);
+                Elem<E>::unpack(c, &q[r][n * EPC]);
+            }
+        } else {
+            pos[r] = -1;
+#pragma unroll
+            for (int e = 0; e < DPL; ++e)
+                q[r][e] = 0.0f;
+        }
+    }
+    __syncthreads();
+
+    float m[MC], l[MC], acc[MC][DPL];
+#pragma unroll
+    for (int r = 0; r < MC; ++r) {
+        m[r] = -INFINITY;
+        l[r] = 0.0f;
+#pragma unroll
+        for (int e = 0; e < DPL; ++e)
+            acc[r][e] = 0.0f;
+    }
+
+    const float qk_scale = a.scale;
+    const E *kbase = reinterpret_cast<const E *>(a.k_pages);
+    const E *vbase = reinterpret_cast<const E *>(a.v_pages);
+    const int64_t head_off = (int64_t)g << ps;  // rows before head g inside a page
+
+    for (int base = ka; base < kb; base += KPI) {
+        float kv[KU][DPL], vv[KU][DPL];
+        int key[KU];
+#pragma unroll
+        for (int u = 0; u < KU; ++u) {
+            key[u] = base + u * (4 * GPW) + wave * GPW + grp;
+            const int jj = key[u] < kb ? key[u] : kb - 1;
+            const int pid = s_pid[(jj >> ps) - p0];
+            const int64_t row = ((int64_t)pid * a.hkv << ps) + head_off + (jj & pmask);
+            const E *kr = kbase + row * D;
+            const E *vr = vbase + row * D;
+#pragma unroll
+            for (int n = 0; n < NL; ++n) {
+                uint4 ck = *reinterpret_cast<const uint4 *>(kr + n * R * EPC + li * EPC);
+                uint4 cv = *reinterpret_cast<const uint4 *>(vr + n * R * EPC + li * EPC);
+                Elem<E>::unpack(ck, &kv[u][n * EPC]);
+                Elem<E>::unpack(cv, &vv[u][n * EPC]);
+            }
+        }
+
+#pragma unroll
+        for (int r = 0; r < MC; ++r) {
+            float s2[KU];
+#pragma unroll
+            for (int u = 0; u < KU; ++u) {
+                float part = 0.0f;
+#pragma unroll
+                for (int e = 0; e < DPL; ++e)
+                    part = fmaf(q[r][e], kv[u][e], part);
+                float s = group_sum<R>(part) * qk_scale;
+                if (cap > 0.0f)
+                    s = cap * tanhf(s / cap);
+                const int j = key[u];
+                const bool vis = j < kb && j <= pos[r] && (W <= 0 || j > pos[r] - W || j < S);
+                s2[u] = vis ? s * kLog2e : -INFINITY;
+            }
+            float mx = s2[0];
+#pragma unroll
+            for (int u = 1; u < KU; ++u)
+                mx = fmaxf(mx, s2[u]);
+            const float mnew = fmaxf(m[r], mx);
+            const float msafe = mnew == -INFINITY ? 0.0f : mnew;
+            const float alpha = fast_exp2(m[r] - msafe);
+            float p[KU];
+            float psum = 0.0f;
+#pragma unroll
+            for (int u = 0; u < KU; ++u) {
+                p[u] = fast_exp2(s2[u] - msafe);
+                psum += p[u];
+            }
+            l[r] = fmaf(l[r], alpha, psum);
+#pragma unroll
+            for (int e = 0; e < DPL; ++e) {
+                float x = acc[r][e] * alpha;
+#pragma unroll
+                for (int u = 0; u < KU; ++u)
+                    x = fmaf(p[u], vv[u][e], x);
+                acc[r][e] = x;
+            }
+            m[r] = mnew;
+        }
+    }
+
+    // Combine the row groups of each wave (butterfly over lane offsets R..32).
+#pragma unroll
+    for (int off = R; off < 64; off <<= 1) {
+#pragma unroll
+        for (int r = 0; r < MC; ++r) {
+            const float mo = __shfl_xor(m[r], off);
+            const float lo = __shfl_xor(l[r], off);
+            const float mnew = fmaxf(m[r], mo);
+            const float msafe = mnew == -INFINITY ? 0.0f : mnew;
+            const float a1 = fast_exp2(m[r] - msafe);
+            const float a2 = fast_exp2(mo - msafe);
+            l[r] = l[r] * a1 + lo * a2;
+#pragma unroll
+            for (int e = 0; e < DPL; ++e) {
+                const float ao = __shfl_xor(acc[r][e], off);
+                acc[r][e] = acc[r][e] * a1 + ao * a2;
+            }
+            m[r] = mnew;
+        }
+    }
+    if (lane < R) {
+#pragma unroll
+        for (int r = 0; r < MC; ++r) {
+            if (lane == 0) {
+                s_m[wave][r] = m[r];
+                s_l[wave][r] = l[r];
+            }
+#pragma unroll
+            for (int n = 0; n < NL; ++n)
+#pragma unroll
+                for (int e = 0; e < EPC; ++e)
+                    s_acc[wave][r][n * R * EPC + li * EPC + e] = acc[r][n * EPC + e];
+        }
+    }
+    __syncthreads();
+
+    // Combine the 4 waves and write this split's partial state per row.
+    for (int idx = tid; idx < MC * D; idx += 256) {
+        const int r = idx / D;
+        const int d = idx - r * D;
+        const int rr = cr.r0 + r;
+        if (rr >= cr.r1)
+            continue;
+        float mm = s_m[0][r];
+#pragma unroll
+        for (int w = 1; w < 4; ++w)
+            mm = fmaxf(mm, s_m[w][r]);
+        const float msafe = mm == -INFINITY ? 0.0f : mm;
+        float ls = 0.0f, as = 0.0f;
+#pragma unroll
+        for (int w = 0; w < 4; ++w) {
+            const float f = fast_exp2(s_m[w][r] - msafe);
+            ls = fmaf(s_l[w][r], f, ls);
+            as = fmaf(s_acc[w][r][d], f, as);
+        }
+        const int i = rr / gsize;
+        const int h = a.groups.list[gstart + rr % gsize];
+        const int64_t row_id = ((int64_t)b * a.q_len + i) * a.hq + h;
+        const int64_t slot = row_id * a.max_splits + split;
+        a.ws_acc[slot * D + d] = as;
+        if (d == 0) {
+            a.ws_ml[slot * 2 + 0] = mm;
+            a.ws_ml[slot * 2 + 1] = ls;
+        }
+    }
+}
+
+template <typename E, int D, int MC>
+hipError_t launch_one(const SplitArgs &a, hipStream_t stream)
+{
+    constexpr int KU = (MC <= 2) ? 8 : 4;
+    dim3 grid(a.max_splits, a.hkv * a.n_chunks, a.batch);
+    hipLaunchKernelGGL((split_valu_kernel<E, D, MC, KU>), grid, dim3(256), 0, stream, a);
+    return hipGetLastError();
+}
+
+template <typename E, int D>
+hipError_t launch_rows(const SplitArgs &a, hipStream_t stream)
+{
+    switch (a.rows_per_item) {
+    case 1: return launch_one<E, D, 1>(a, stream);
+    case 2: return launch_one<E, D, 2>(a, stream);
+    case 4: return launch_one<E, D, 4>(a, stream);
+    case 8: return launch_one<E, D, 8>(a, stream);
+    default: return hipErrorInvalidValue;
+    }
+}
+
+}  // namespace
+
+hipError_t launch_split_valu(const SplitArgs &a, int dtype, hipStream_t stream)
+{
+    if (dtype == 0)
+        return a.head_dim == 64 ? launch_rows<float, 64>(a, stream)
+                                : launch_rows<float, 128>(a, stream);
+    return a.head_dim == 64 ? launch_rows<uint16_t, 64>(a, stream)
+                            : launch_rows<uint16_t, 128>(a, stream);
+}
+
+}  // namespace atlas

@@ -1,0 +1,200 @@
+/*
+ * atlas.h -- C ABI of libatlas: exact causal grouped-query attention over a
+ * paged K/V cache on AMD Instinct MI355X (gfx950).
+ *
+ * What the library computes.  For sequence b with context length L_b (keys at
+ * positions 0..L_b-1) and q_len queries that are the suffix of that history
+ * (query i sits at position pos = L_b - q_len + i; CPUAttn README, "Parallel
+ * example", cache-backed semantics), and q-head h reading K/V head g =
+ * head_map[h] (CPUAttn "Operator model": standard, GQA, MQA):
+ *
+ *     visible(j) = j <= pos  and  (W_b == 0  or  j > pos - W_b  or  j < S_b)
+ *     s_j        = scale * <q, K_g[j]>
+ *     s_j        = c_b * tanh(s_j / c_b)                 if softcap c_b > 0
+ *     out        = sum_j softmax_j(s) * V_g[j]  over visible j
+ *     lse        = log sum_j exp(s_j)           over visible j
+ *
+ * The window / sink / softcap variants are named by the ferrox-core crate
+ * index (causal_gqa_attention_windowed, _sinks, _softcap, _paged_sinks,
+ * _windowed_softcap); the pages give no formulas, and the readings above are
+ * the ones this library implements.  The K/V history is paged: the CFR-Atlas
+ * README ("Core contract") requires the page-by-page folded result to equal
+ * full-K/V attention, which is what these entry points return: every visible
+ * key is read, nothing is pruned or approximated; the pages are folded into
+ * online-softmax states (max, sum, accumulator) and the partial states are
+ * merged exactly (log-sum-exp merge; CPUAttn "Operator model", split-K only
+ * with a structured merge).
+ *
+ * Memory layout (all row-major, all caller-owned; the library never
+ * allocates device memory):
+ *   q           [B][q_len][Hq][D]                 (dtype)
+ *   k_pages     [num_phys_pages][Hkv][P][D]       (dtype) one (page, head)
+ *   v_pages     [num_phys_pages][Hkv][P][D]       slab is K[token][dim],
+ *                                                 CFR-Atlas "Minimal integration"
+ *   page_table  [B][max_pages_per_seq] int32      logical page -> physical id
+ *   context_lens[B] int32                         L_b
+ *   window, sink_tokens [B] int32, softcap [B] f32  optional (NULL = off)
+ *   out         [B][q_len][Hq][D] f32
+ *   lse         [B][q_len][Hq] f32                optional (NULL = not written)
+ * Rows of a sequence's last page past L_b, and physical pages no page table
+ * references, are never read, whatever they hold.
+ *
+ * Calls are asynchronous on the caller's HIP stream (a hipStream_t passed as
+ * void*, NULL = the null stream) and never synchronise the host, except in
+ * validation mode (environment ATLAS_VALIDATE=1), which copies the device
+ * page table and lengths to the host and checks them before launching.
+ *
+ * Errors.  Every check of host-visible arguments runs before any launch: on
+ * an error nothing is launched and no output is written.  The detail of the
+ * last error on the calling thread is returned by atlas_last_error().
+ * Device-resident values (page ids, lengths, window/sink counts) are trusted
+ * outside validation mode; kernels clamp them so that no access leaves the
+ * caller's buffers, and a query row with no visible key (possible only when
+ * q_len > L_b) yields NaN outputs and lse = -inf.
+ *
+ * Thread safety: the functions keep no state between calls (only a
+ * thread-local error string), so concurrent calls on different streams with
+ * disjoint outputs and workspaces are safe.
+ */
+#ifndef ATLAS_H
+#define ATLAS_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define ATLAS_ABI_VERSION 1
+
+/* Status codes returned by every entry point. */
+enum {
+    ATLAS_OK = 0,
+    ATLAS_ERR_NULL = 1,        /* a required pointer is NULL */
+    ATLAS_ERR_SHAPE = 2,       /* bad sizes, Hq % Hkv != 0 without head_map, bad head_map entry */
+    ATLAS_ERR_RANGE = 3,       /* a size or count out of range (e.g. q_len > max context) */
+    ATLAS_ERR_UNSUPPORTED = 4, /* no kernel for this dtype / head_dim / page size: never a silent fallback */
+    ATLAS_ERR_WORKSPACE = 5,   /* workspace smaller than the matching *_workspace_bytes() */
+    ATLAS_ERR_POOL = 6,        /* validation mode: a page id outside [0, num_phys_pages) */
+    ATLAS_ERR_NONFINITE = 7,   /* validation mode: a NaN or Inf in the visible inputs */
+    ATLAS_ERR_DEVICE = 8       /* a HIP runtime error */
+};
+
+/* Element types of q, k_pages and v_pages (all three share one type). */
+enum {
+    ATLAS_DTYPE_F32 = 0,
+    ATLAS_DTYPE_BF16 = 1
+};
+
+/*
+ * Arguments of one attention call.  Supported: head_dim 64 or 128; page_size
+ * a power of two in [1, 4096]; Hq, Hkv <= 256; dtype f32 or bf16.
+ */
+typedef struct atlas_attn_args {
+    int32_t dtype;              /* ATLAS_DTYPE_* of q, k_pages, v_pages */
+    int32_t batch;              /* B >= 1 */
+    int32_t q_len;              /* queries per sequence (1 for decode) */
+    int32_t num_q_heads;        /* Hq */
+    int32_t num_kv_heads;       /* Hkv */
+    int32_t head_dim;           /* D */
+    int32_t page_size;          /* P, tokens per page */
+    int32_t num_phys_pages;     /* pages in each arena */
+    int32_t max_pages_per_seq;  /* columns of page_table; every L_b <= max_pages_per_seq * P */
+    int32_t split_tokens;       /* keys per split-KV work item; 0 = library's choice
+                                   (results depend on it only through rounding order) */
+    float scale;                /* score scale, e.g. 1/sqrt(D) */
+    int32_t reserved0;
+    const int32_t *head_map;    /* HOST [Hq] -> K/V head, or NULL for h / (Hq / Hkv) */
+    const void *q;              /* device, see layout above */
+    const void *k_pages;        /* device */
+    const void *v_pages;        /* device */
+    const int32_t *page_table;  /* device */
+    const int32_t *context_lens;/* device */
+    const int32_t *window;      /* device [B] or NULL; 0 = no window for that sequence */
+    const int32_t *sink_tokens; /* device [B] or NULL; only used where window > 0 */
+    const float *softcap;       /* device [B] or NULL; 0 = no softcap for that sequence */
+    float *out;                 /* device */
+    float *lse;                 /* device or NULL */
+    void *workspace;            /* device scratch, >= the matching *_workspace_bytes() */
+    size_t workspace_bytes;
+} atlas_attn_args;
+
+/* One page to regenerate: page `logical_page` of sequence `seq` is written
+ * into physical page `phys_page` of both arenas (all Hkv heads). */
+typedef struct atlas_regen_job {
+    int32_t seq;
+    int32_t logical_page;
+    int32_t phys_page;
+} atlas_regen_job;
+
+/*
+ * Arguments of one regeneration call.  The CFR-Atlas README ("Minimal
+ * integration") has the backend replay exact row-major K[token][dim] and
+ * V[token][dim] rows of one (layer, K/V head, token range) on demand; this
+ * library's replay is a seeded counter-based generator: value (tensor t in
+ * {1 = K, 2 = V}, head h, token j, dim d) is the Box-Muller normal built from
+ * Philox4x32-10 (Salmon et al., SC'11) with key = seed and counter
+ * (j, d / 4, h | t << 30, layer | seq << 16): words 0,1 give dims 4k, 4k+1
+ * as r cos(2 pi u1), r sin(2 pi u1) with r = sqrt(-2 ln u0), words 2,3 give
+ * dims 4k+2, 4k+3, and word x maps to u = (floor(x / 512) + 1/2) * 2^-23.
+ * Computed in fp32; bf16 arenas store it rounded to nearest-even.
+ * Requires layer < 2^16, seq < 2^16, Hkv < 2^30.
+ */
+typedef struct atlas_regen_args {
+    uint64_t seed;
+    int32_t layer;
+    int32_t dtype;              /* ATLAS_DTYPE_* of the arenas */
+    int32_t num_kv_heads;
+    int32_t head_dim;           /* 64 or 128 */
+    int32_t page_size;          /* power of two in [1, 4096] */
+    int32_t num_phys_pages;
+    int32_t num_jobs;           /* >= 0 */
+    int32_t reserved0;
+    const atlas_regen_job *jobs;/* device [num_jobs]; jobs with phys_page outside
+                                   [0, num_phys_pages) or seq/logical_page < 0 are skipped */
+    void *k_pages;              /* device arena */
+    void *v_pages;              /* device arena */
+} atlas_regen_args;
+
+/* ABI version of the loaded library (ATLAS_ABI_VERSION at build time). */
+int32_t atlas_abi_version(void);
+
+/* Static description of a status code. */
+const char *atlas_status_str(int32_t status);
+
+/* Detail of the last non-OK status returned on this thread ("" if none). */
+const char *atlas_last_error(void);
+
+/* Workspace bytes atlas_attend_decode / atlas_attend_prefill need for these
+ * arguments (pointers are not inspected).  Returns SIZE_MAX when the sizes
+ * are invalid (the reason is in atlas_last_error()). */
+size_t atlas_decode_workspace_bytes(const atlas_attn_args *args);
+size_t atlas_prefill_workspace_bytes(const atlas_attn_args *args);
+
+/*
+ * Decode: one query per sequence (q_len must be 1) at position L_b - 1.
+ * Split-KV: each (sequence, K/V head, span of keys) work item folds its keys
+ * into an online-softmax state for all q-heads of that K/V head, then a merge
+ * pass combines the states of each (sequence, q-head) by log-sum-exp.
+ */
+int32_t atlas_attend_decode(const atlas_attn_args *args, void *stream);
+
+/*
+ * Prefill / cache-backed short queries: q_len >= 1 queries per sequence, the
+ * suffix of the history (requires q_len <= L_b).  bf16 with q_len >= 64 and
+ * no window / sink / softcap arrays runs the tiled matrix-core kernel
+ * (query x key tiles with causal block-stop: each query tile stops at the
+ * last key tile its last row can see).  Every other case runs the split-KV
+ * kernels of atlas_attend_decode with each (query, q-head) pair as a row.
+ */
+int32_t atlas_attend_prefill(const atlas_attn_args *args, void *stream);
+
+/* Regenerate whole pages (all heads, all P tokens) into the arenas. */
+int32_t atlas_regenerate_pages(const atlas_regen_args *args, void *stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* ATLAS_H */

@@ -1,0 +1,191 @@
+"""Shared helpers for the GPU parity tests: device inputs from the seeded
+workloads, the oracle's answer for the same inputs, and the tolerance check.
+
+Tolerances (stated for this method): fp32 inputs |gpu - ref| <= 2e-5 +
+1e-4 |ref| element-wise; bf16 inputs |gpu - ref| <= 2e-3 with fp32
+accumulation.  Integer and index results are compared bit-exactly.
+"""
+from __future__ import annotations
+
+import math
+from dataclasses import dataclass
+
+import numpy as np
+import torch
+
+import oracle
+import workloads
+
+F32_ATOL, F32_RTOL = 2e-5, 1e-4
+BF16_ATOL = 2e-3
+
+
+def tdtype(w):
+    return torch.float32 if w.dtype == "f32" else torch.bfloat16
+
+
+def assert_close(got, want, dtype: str, what: str = ""):
+    got = np.asarray(got, np.float64)
+    want = np.asarray(want, np.float64)
+    assert got.shape == want.shape, f"{what}: shape {got.shape} != {want.shape}"
+    err = np.abs(got - want)
+    bound = (F32_ATOL + F32_RTOL * np.abs(want)) if dtype == "f32" else np.full(want.shape, BF16_ATOL)
+    bad = ~(err <= bound)
+    if bad.any():
+        idx = np.argwhere(bad)[:5].tolist()
+        raise AssertionError(f"{what}: {int(bad.sum())}/{bad.size} out of tolerance, "
+                             f"max err {np.nanmax(err):.3e}, first at {idx}: "
+                             f"got {got[tuple(idx[0])]!r} want {want[tuple(idx[0])]!r}")
+
+
+@dataclass
+class DeviceInputs:
+    w: workloads.Workload
+    layout: workloads.PageLayout
+    q: torch.Tensor
+    k: torch.Tensor
+    v: torch.Tensor
+    page_table: torch.Tensor
+    context_lens: torch.Tensor
+    window: torch.Tensor | None
+    sinks: torch.Tensor | None
+    softcap: torch.Tensor | None
+    cold_jobs: torch.Tensor | None
+    hot_jobs: torch.Tensor | None
+
+
+def logical_kv(w, device, seed_offset=0):
+    """Seeded K/V in logical page order: [total_pages][Hkv][P][D] (pages of
+    sequence 0 first), independent of any physical placement."""
+    n_pages = [int(math.ceil(int(L) / w.page_size)) for L in w.context_lens]
+    shape = (sum(n_pages), w.hkv, w.page_size, w.head_dim)
+    k = workloads.randn(shape, seed=w.seed * 100 + 2 + seed_offset, dtype=w.dtype, device=device)
+    v = workloads.randn(shape, seed=w.seed * 100 + 3 + seed_offset, dtype=w.dtype, device=device)
+    return k, v, n_pages
+
+
+def build(w, device="cuda", hot_fraction=None, layout_seed=0, extra_phys=0, poison=False,
+          regen_hot=True) -> DeviceInputs:
+    """Device-resident inputs.  Regenerated workloads: resident pages are
+    regenerated once here, cold pages are left for each call.  Others: seeded
+    logical K/V scattered into a shuffled arena.  poison=True fills every
+    arena row that no context covers (page tails, spare pages) with NaN."""
+    import exact_paged_causal_amd as atlas
+    lay = workloads.page_layout(w, hot_fraction, layout_seed, extra_phys)
+    dt = tdtype(w)
+    q = workloads.randn(workloads.query_shape(w), seed=w.seed * 100 + 1, dtype=w.dtype, device=device)
+    shape = workloads.arena_shape(w, lay.num_phys)
+    fill = float("nan") if poison else 0.0
+    pt = torch.from_numpy(lay.page_table).to(device)
+    ctx = torch.from_numpy(w.context_lens.astype(np.int32)).to(device)
+    if w.regenerated:
+        k = torch.full(shape, fill, dtype=dt, device=device)
+        v = torch.full(shape, fill, dtype=dt, device=device)
+        hot = torch.from_numpy(lay.hot_jobs).to(device) if len(lay.hot_jobs) else None
+        cold = torch.from_numpy(lay.cold_jobs).to(device) if len(lay.cold_jobs) else None
+        if regen_hot and hot is not None:
+            atlas.atlas_regenerate_pages(k, v, hot, seed=w.seed, layer=w.layer)
+    else:
+        kl, vl, n_pages = logical_kv(w, device)
+        k = torch.full(shape, fill, dtype=dt, device=device)
+        v = torch.full(shape, fill, dtype=dt, device=device)
+        ids = torch.from_numpy(np.concatenate([lay.page_table[b, :n_pages[b]]
+                                               for b in range(w.batch)]).astype(np.int64)).to(device)
+        k.index_copy_(0, ids, kl)
+        v.index_copy_(0, ids, vl)
+        del kl, vl
+        if poison:
+            # NaN in the rows past each context inside its last page
+            for b in range(w.batch):
+                L = int(w.context_lens[b])
+                tail = L % w.page_size
+                if tail:
+                    pid = int(lay.page_table[b, (L - 1) // w.page_size])
+                    k[pid, :, tail:, :] = float("nan")
+                    v[pid, :, tail:, :] = float("nan")
+        hot = cold = None
+    opt = lambda a, t: None if a is None else torch.from_numpy(a.astype(t)).to(device)
+    return DeviceInputs(w, lay, q, k, v, pt, ctx, opt(w.window, np.int32), opt(w.sinks, np.int32),
+                        opt(w.softcap, np.float32), cold, hot)
+
+
+def run(inp: DeviceInputs, entry: str | None = None, split_tokens: int = 0, workspace=None,
+        head_map=None):
+    """One call of the path: regenerate cold pages (if any), then attend."""
+    import exact_paged_causal_amd as atlas
+    w = inp.w
+    if inp.cold_jobs is not None:
+        atlas.atlas_regenerate_pages(inp.k, inp.v, inp.cold_jobs, seed=w.seed, layer=w.layer)
+    if entry is None:
+        entry = "decode" if w.q_len == 1 else "prefill"
+    fn = atlas.atlas_attend_decode if entry == "decode" else atlas.atlas_attend_prefill
+    return fn(inp.q, inp.k, inp.v, inp.page_table, inp.context_lens, w.scale,
+              head_map=head_map, window=inp.window, sink_tokens=inp.sinks, softcap=inp.softcap,
+              split_tokens=split_tokens, workspace=workspace)
+
+
+def to_f32_numpy(t: torch.Tensor) -> np.ndarray:
+    return t.detach().float().cpu().numpy()
+
+
+class OracleSource:
+    """Per-sequence unpaged K/V for the oracle: regenerated by the oracle's own
+    generator, or gathered from a host copy of the arena through the page
+    table."""
+
+    def __init__(self, inp: DeviceInputs):
+        self.inp = inp
+        w = inp.w
+        self.k_host = self.v_host = None
+        if not w.regenerated:
+            self.k_host = to_f32_numpy(inp.k)
+            self.v_host = to_f32_numpy(inp.v)
+
+    def kv(self, b: int):
+        w = self.inp.w
+        L = int(w.context_lens[b])
+        if w.regenerated:
+            kind = "f32" if w.dtype == "f32" else "bf16"
+            ks, vs = [], []
+            for h in range(w.hkv):
+                kr = oracle.regen_rows(w.seed, w.layer, b, oracle.TENSOR_K, h, 0, L, w.head_dim, kind)
+                vr = oracle.regen_rows(w.seed, w.layer, b, oracle.TENSOR_V, h, 0, L, w.head_dim, kind)
+                if kind == "bf16":
+                    kr, vr = oracle.bf16_bits_to_f32(kr), oracle.bf16_bits_to_f32(vr)
+                ks.append(kr)
+                vs.append(vr)
+            return np.stack(ks), np.stack(vs)
+        pt = self.inp.layout.page_table[b]
+        return (oracle.gather_pages(self.k_host, pt, L, w.page_size),
+                oracle.gather_pages(self.v_host, pt, L, w.page_size))
+
+
+def oracle_answer(inp: DeviceInputs, b: int, rows=None, head_map=None, src: OracleSource | None = None):
+    """Oracle output for sequence b (all query rows, or the listed ones)."""
+    w = inp.w
+    src = src or OracleSource(inp)
+    k, v = src.kv(b)
+    q = to_f32_numpy(inp.q[b])                       # [q_len][Hq][D]
+    L = int(w.context_lens[b])
+    pos = np.arange(L - w.q_len, L, dtype=np.int32)
+    if rows is not None:
+        q, pos = q[rows], pos[rows]
+    hm = oracle.default_head_map(w.hq, w.hkv) if head_map is None else np.asarray(head_map, np.int32)
+    win = int(w.window[b]) if w.window is not None else 0
+    snk = int(w.sinks[b]) if (w.sinks is not None and win > 0) else 0
+    cap = float(w.softcap[b]) if w.softcap is not None else 0.0
+    return oracle.attend(q, k, v, pos, hm, w.scale, win, snk, cap)
+
+
+def check_against_oracle(inp, out, lse, seqs=None, rows=None, head_map=None, what=""):
+    w = inp.w
+    src = OracleSource(inp)
+    out_h = to_f32_numpy(out)
+    lse_h = to_f32_numpy(lse) if lse is not None else None
+    for b in (range(w.batch) if seqs is None else seqs):
+        ref_o, ref_l = oracle_answer(inp, b, rows, head_map, src)
+        got_o = out_h[b] if rows is None else out_h[b][rows]
+        assert_close(got_o, ref_o, w.dtype, f"{what} out[b={b}]")
+        if lse_h is not None:
+            got_l = lse_h[b] if rows is None else lse_h[b][rows]
+            assert_close(got_l, ref_l, w.dtype, f"{what} lse[b={b}]")

@@ -1,0 +1,212 @@
+"""CPU tests of the boundary: the library loads and exports every entry point
+include/atlas.h declares, host-visible argument errors are reported before any
+launch, and the split planner is checked against brute-force enumeration.
+No test here launches a kernel."""
+import ctypes
+import os
+import re
+import subprocess
+
+import numpy as np
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "atlas.h")
+
+
+def _declared_functions():
+    text = open(HEADER).read()
+    return sorted(set(re.findall(r"^\s*(?:const\s+)?\w+\s*\**\s*(atlas_\w+)\s*\(", text, re.M)))
+
+
+def test_header_declares_the_boundary():
+    names = _declared_functions()
+    assert names == sorted(["atlas_abi_version", "atlas_status_str", "atlas_last_error",
+                            "atlas_decode_workspace_bytes", "atlas_prefill_workspace_bytes",
+                            "atlas_attend_decode", "atlas_attend_prefill",
+                            "atlas_regenerate_pages"])
+
+
+def test_library_exports_every_declared_symbol():
+    from exact_paged_causal_amd import atlas as A
+    lib = ctypes.CDLL(A.LIB_PATH)
+    for name in _declared_functions():
+        assert hasattr(lib, name), name
+    nm = subprocess.run(["nm", "-D", "--defined-only", A.LIB_PATH], capture_output=True, text=True,
+                        check=True).stdout
+    exported = set(re.findall(r" T (atlas_\w+)", nm))
+    assert exported == set(_declared_functions())
+    assert A.atlas_abi_version() == 1
+    assert A.atlas_status_str(A.ATLAS_ERR_POOL) == "page id outside the physical pool"
+
+
+def _struct_offsets_from_header(struct):
+    """Field order of a struct in atlas.h (names only)."""
+    text = open(HEADER).read()
+    body = re.search(r"typedef struct %s \{(.*?)\} %s;" % (struct, struct), text, re.S).group(1)
+    body = re.sub(r"/\*.*?\*/", "", body, flags=re.S)
+    return re.findall(r"(\w+)\s*;", body)
+
+
+def test_binding_structs_mirror_the_header():
+    from exact_paged_causal_amd import atlas as A
+    assert [f[0] for f in A.AttnArgs._fields_] == _struct_offsets_from_header("atlas_attn_args")
+    assert [f[0] for f in A.RegenArgs._fields_] == _struct_offsets_from_header("atlas_regen_args")
+    assert [f[0] for f in A.RegenJob._fields_] == _struct_offsets_from_header("atlas_regen_job")
+    assert ctypes.sizeof(A.AttnArgs) == 4 * 12 + 8 * 13
+    assert ctypes.sizeof(A.RegenArgs) == 8 + 4 * 8 + 8 * 3
+
+
+FAKE = 0x10000  # never dereferenced: every case below fails host validation first
+
+
+def _valid_args(**over):
+    from exact_paged_causal_amd import atlas as A
+    a = A.AttnArgs()
+    a.dtype, a.batch, a.q_len, a.num_q_heads, a.num_kv_heads, a.head_dim = 0, 2, 1, 8, 2, 64
+    a.page_size, a.num_phys_pages, a.max_pages_per_seq, a.split_tokens, a.scale = 16, 10, 4, 0, 0.125
+    for f in ("q", "k_pages", "v_pages", "page_table", "context_lens", "out", "workspace"):
+        setattr(a, f, FAKE)
+    a.workspace_bytes = 1 << 40
+    for k, v in over.items():
+        setattr(a, k, v)
+    return a
+
+
+@pytest.mark.parametrize("field,value,status", [
+    ("dtype", 5, 4), ("batch", 0, 2), ("q_len", 0, 2), ("q_len", 2, 2),      # decode needs q_len 1
+    ("num_q_heads", 7, 2), ("num_kv_heads", 0, 2), ("num_q_heads", 512, 4),
+    ("head_dim", 96, 4), ("page_size", 0, 2), ("page_size", 24, 4), ("page_size", 8192, 4),
+    ("num_phys_pages", 0, 2), ("max_pages_per_seq", 0, 2), ("split_tokens", -1, 3),
+    ("max_pages_per_seq", 1 << 30, 3), ("q", None, 1), ("page_table", None, 1),
+    ("out", None, 1), ("workspace_bytes", 16, 5), ("scale", float("inf"), 3),
+])
+def test_decode_rejects_bad_arguments_before_launch(field, value, status):
+    from exact_paged_causal_amd import atlas as A
+    a = _valid_args(**{field: value})
+    st = A.lib.atlas_attend_decode(ctypes.byref(a), None)
+    assert st == status, (st, A.atlas_last_error())
+    assert A.atlas_last_error() != ""
+
+
+def test_prefill_limits_and_head_map():
+    from exact_paged_causal_amd import atlas as A
+    a = _valid_args(q_len=65, max_pages_per_seq=4, page_size=16)   # 65 > 64-token context
+    assert A.lib.atlas_attend_prefill(ctypes.byref(a), None) == A.ATLAS_ERR_RANGE
+    bad_map = (ctypes.c_int32 * 8)(0, 1, 2, 0, 1, 0, 1, 0)
+    a = _valid_args(head_map=ctypes.cast(bad_map, ctypes.POINTER(ctypes.c_int32)))
+    assert A.lib.atlas_attend_decode(ctypes.byref(a), None) == A.ATLAS_ERR_SHAPE
+    assert "head_map[2]" in A.atlas_last_error()
+    # an explicit map lifts the Hq % Hkv requirement
+    ok_map = (ctypes.c_int32 * 7)(0, 1, 0, 1, 0, 1, 0)
+    a = _valid_args(num_q_heads=7, head_map=ctypes.cast(ok_map, ctypes.POINTER(ctypes.c_int32)))
+    assert A.lib.atlas_decode_workspace_bytes(ctypes.byref(a)) not in (0, ctypes.c_size_t(-1).value)
+
+
+def test_workspace_sizing():
+    from exact_paged_causal_amd import atlas as A
+    a = _valid_args()
+    n = A.lib.atlas_decode_workspace_bytes(ctypes.byref(a))
+    # rows (B*Hq) x splits x (D + 2) floats + a 256-byte header
+    rows, d = 2 * 8, 64
+    assert (n - 256) % (rows * (d + 2) * 4) == 0 and n > 256
+    bad = _valid_args(head_dim=80)
+    assert A.lib.atlas_decode_workspace_bytes(ctypes.byref(bad)) == ctypes.c_size_t(-1).value
+
+
+def test_regenerate_rejects_bad_arguments():
+    from exact_paged_causal_amd import atlas as A
+    r = A.RegenArgs()
+    r.dtype, r.num_kv_heads, r.head_dim, r.page_size, r.num_phys_pages, r.num_jobs = 0, 2, 64, 16, 4, 1
+    r.jobs = r.k_pages = r.v_pages = FAKE
+    for field, value, status in [("head_dim", 32, 4), ("page_size", 3, 4), ("layer", 1 << 16, 3),
+                                 ("num_jobs", -1, 2), ("dtype", 9, 4)]:
+        saved = getattr(r, field)
+        setattr(r, field, value)
+        assert A.lib.atlas_regenerate_pages(ctypes.byref(r), None) == status, field
+        setattr(r, field, saved)
+    r.jobs = None
+    assert A.lib.atlas_regenerate_pages(ctypes.byref(r), None) == A.ATLAS_ERR_NULL
+    r.num_jobs = 0   # nothing to do is not an error
+    assert A.lib.atlas_regenerate_pages(ctypes.byref(r), None) == A.ATLAS_OK
+
+
+# ---------------------------------------------------------------- planner
+
+@pytest.fixture(scope="module")
+def planner(tmp_path_factory):
+    so = str(tmp_path_factory.mktemp("plan") / "plan_probe.so")
+    subprocess.run(["g++", "-O1", "-std=c++17", "-fPIC", "-shared",
+                    "-I", os.path.join(ROOT, "exact_paged_causal_amd", "csrc"),
+                    os.path.join(ROOT, "tests", "plan_probe.cpp"), "-o", so], check=True)
+    lib = ctypes.CDLL(so)
+    ip = ctypes.POINTER(ctypes.c_int)
+    lib.probe_plan.argtypes = [ctypes.c_int] * 5 + [ip]
+    lib.probe_ranges.argtypes = [ctypes.c_int] * 5 + [ip, ctypes.c_int, ip]
+    lib.probe_bound.argtypes = [ctypes.c_int] * 3
+    lib.probe_chunk.argtypes = [ctypes.c_int] * 5 + [ip]
+    return lib
+
+
+def _ranges(lib, pmin, pmax, w, s, t):
+    buf = (ctypes.c_int * 4096)()
+    n = ctypes.c_int()
+    lib.probe_ranges(pmin, pmax, w, s, t, buf, 2048, ctypes.byref(n))
+    return [(buf[2 * i], buf[2 * i + 1]) for i in range(n.value)]
+
+
+def _union_visible(pmin, pmax, w, s):
+    keys = set()
+    for pos in range(max(pmin, 0), pmax + 1):
+        if w <= 0:
+            keys |= set(range(pos + 1))
+        else:
+            keys |= set(range(max(0, pos - w + 1), pos + 1)) | set(range(min(s, pos + 1)))
+    return keys
+
+
+def test_split_ranges_cover_exactly_the_visible_keys(planner):
+    """Splits are disjoint, ordered, at most T keys each, cut at multiples of
+    T, cover exactly the union of the rows' visible keys, and never exceed
+    the host's bound."""
+    rng = np.random.default_rng(0)
+    for _ in range(1500):
+        ctx = int(rng.integers(1, 400))
+        q_len = int(rng.integers(1, min(ctx, 40) + 1))
+        pmin = ctx - q_len + int(rng.integers(0, q_len))
+        pmax = int(rng.integers(pmin, ctx))
+        w = int(rng.choice([0, 1, 2, 5, 17, 64, 1000]))
+        s = int(rng.choice([0, 1, 4, 30, 500]))
+        t = int(rng.choice([1, 3, 16, 64, 128]))
+        rs = _ranges(planner, pmin, pmax, w, s, t)
+        keys = []
+        for a, b in rs:
+            assert 0 <= a < b <= pmax + 1 and b - a <= t
+            assert a // t == (b - 1) // t, "split crosses a T boundary"
+            keys.extend(range(a, b))
+        assert keys == sorted(keys) and len(keys) == len(set(keys))
+        assert set(keys) == _union_visible(pmin, pmax, w, s), (pmin, pmax, w, s, t)
+        max_ctx = ctx + int(rng.integers(0, 50))
+        assert len(rs) <= planner.probe_bound(max_ctx, t, 1 if (w > 0 and s > 0) else 0)
+
+
+def test_split_plan_edge_cases(planner):
+    out = (ctypes.c_int * 6)()
+    planner.probe_plan(-1, -1, 0, 0, 64, out)          # no valid row
+    assert out[0] == 0
+    assert _ranges(planner, 0, 0, 0, 0, 64) == [(0, 1)]          # one-token history
+    assert _ranges(planner, 99, 99, 1, 0, 64) == [(99, 100)]     # window of one
+    assert _ranges(planner, 99, 99, 1, 4, 64) == [(0, 4), (99, 100)]
+    assert _ranges(planner, 99, 99, 10, 200, 64) == [(0, 64), (64, 90), (90, 100)]  # sinks reach the window
+    assert _ranges(planner, 4095, 4095, 0, 0, 1024) == [(0, 1024), (1024, 2048), (2048, 3072), (3072, 4096)]
+
+
+def test_chunk_rows(planner):
+    out = (ctypes.c_int * 4)()
+    # 16 queries x group 4 = 64 rows, 8 per chunk; chunk 3 = rows 24..31 = queries 6, 7
+    planner.probe_chunk(3, 8, 4, 16, 256, out)
+    assert list(out) == [24, 32, 256 - 16 + 6, 256 - 16 + 7]
+    planner.probe_chunk(8, 8, 4, 16, 256, out)   # past the end
+    assert out[0] >= out[1]
+    planner.probe_chunk(0, 4, 3, 1, 10, out)     # decode, group of 3 in a chunk of 4
+    assert list(out) == [0, 3, 9, 9]
