@@ -1,0 +1,272 @@
+"""Benchmark of the paged-attention hot path on one MI355X.
+
+One step = one pass of the whole hot path over the synthetic inputs:
+  * long-context paged decode (B=8 x 65536 tokens, Hq=32, Hkv=8, D=64,
+    pages of 512, fp32, 25 % of pages resident): the cold 75 % of pages are
+    regenerated into scratch on the device, then the split-KV fold and the
+    log-sum-exp merge run over resident + scratch pages;
+  * causal GQA prefill (S=8192, Hq=32, Hkv=8, D=128, bf16, pages of 128 in a
+    random physical order) on the tiled matrix-core kernel.
+Inputs are resident in HBM before timing starts.  `value` is the decode
+attention pass's K/V-read throughput (algorithmic bytes / time of the
+attention call, split + merge); the prefill throughput and the regenerator
+are reported beside it.  Per-kernel times come from HIP events recorded on
+the stream the kernels run on.
+
+Prints one JSON line.  `--gpus N` with N > 1 exits: this path runs on one GPU.
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import math
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, GB/s
+BF16_PEAK_TFLOPS = 2500.0      # MI355X dense bf16 matrix peak, TFLOP/s
+METRIC = "decode attn KV-read GB/s (% HBM peak); prefill TFLOP/s (% MFMA peak)"
+
+
+def parse():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--split-tokens", type=int, default=0)
+    ap.add_argument("--no-prefill", action="store_true")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-sample-seqs", type=int, default=2)
+    ap.add_argument("--copy-calibration", action="store_true",
+                    help="also run a plain device copy of known size (HBM counter calibration)")
+    return ap.parse_args()
+
+
+class Timer:
+    """HIP-event timing of one launch sequence on the current stream."""
+
+    def __init__(self, torch):
+        self.torch = torch
+        self.pairs = []
+
+    def __call__(self, fn):
+        t = self.torch
+        s, e = t.cuda.Event(enable_timing=True), t.cuda.Event(enable_timing=True)
+        s.record()
+        r = fn()
+        e.record()
+        self.pairs.append((s, e))
+        return r
+
+    def ms(self):
+        return [s.elapsed_time(e) for s, e in self.pairs]
+
+
+def decode_setup(torch, workloads, atlas):
+    w = workloads.make("long_context_decode")
+    lay = workloads.page_layout(w)
+    shape = workloads.arena_shape(w, lay.num_phys)
+    k = torch.zeros(shape, dtype=torch.float32, device="cuda")
+    v = torch.zeros_like(k)
+    hot = torch.from_numpy(lay.hot_jobs).cuda()
+    cold = torch.from_numpy(lay.cold_jobs).cuda()
+    atlas.atlas_regenerate_pages(k, v, hot, seed=w.seed, layer=w.layer)
+    q = workloads.randn(workloads.query_shape(w), seed=w.seed * 100 + 1, device="cuda")
+    pt = torch.from_numpy(lay.page_table).cuda()
+    ctx = torch.from_numpy(w.context_lens).cuda()
+    return dict(w=w, lay=lay, k=k, v=v, hot=hot, cold=cold, q=q, pt=pt, ctx=ctx)
+
+
+def prefill_setup(torch, workloads, np):
+    w = workloads.make("causal_prefill")
+    lay = workloads.page_layout(w)
+    shape = workloads.arena_shape(w, lay.num_phys)
+    n = lay.num_phys
+    kl = workloads.randn(shape, seed=w.seed * 100 + 2, dtype="bf16", device="cuda")
+    vl = workloads.randn(shape, seed=w.seed * 100 + 3, dtype="bf16", device="cuda")
+    ids = torch.from_numpy(lay.page_table[0, :n].astype(np.int64)).cuda()
+    k = torch.empty_like(kl)
+    v = torch.empty_like(vl)
+    k.index_copy_(0, ids, kl)
+    v.index_copy_(0, ids, vl)
+    q = workloads.randn(workloads.query_shape(w), seed=w.seed * 100 + 1, dtype="bf16", device="cuda")
+    pt = torch.from_numpy(lay.page_table).cuda()
+    ctx = torch.from_numpy(w.context_lens).cuda()
+    return dict(w=w, lay=lay, k=k, v=v, q=q, pt=pt, ctx=ctx, kl=kl, vl=vl)
+
+
+def cpu_baseline(d, out, n_seqs, np, oracle):
+    """Time the oracle's attention (fp64, OpenMP) on a bounded sample of the
+    decode workload: the first n_seqs sequences, all q-heads, full 65536-token
+    histories.  K/V generation by the oracle's own generator is not timed.
+    The GPU outputs of the same rows are checked against it on the way."""
+    w = d["w"]
+    q = d["q"].cpu().numpy()
+    hm = oracle.default_head_map(w.hq, w.hkv)
+    total_bytes = 0
+    secs = 0.0
+    max_err = 0.0
+    for b in range(n_seqs):
+        L = int(w.context_lens[b])
+        kk = np.stack([oracle.regen_rows(w.seed, w.layer, b, oracle.TENSOR_K, h, 0, L, w.head_dim)
+                       for h in range(w.hkv)])
+        vv = np.stack([oracle.regen_rows(w.seed, w.layer, b, oracle.TENSOR_V, h, 0, L, w.head_dim)
+                       for h in range(w.hkv)])
+        t0 = time.perf_counter()
+        ro, _ = oracle.attend(q[b], kk, vv, np.array([L - 1], np.int32), hm, w.scale)
+        secs += time.perf_counter() - t0
+        total_bytes += kk.nbytes + vv.nbytes
+        err = np.abs(out[b].astype(np.float64) - ro)
+        bound = 2e-5 + 1e-4 * np.abs(ro)
+        if not np.all(err <= bound):
+            raise SystemExit(f"bench: GPU decode output disagrees with the oracle (seq {b}, max err {err.max():.3e})")
+        max_err = max(max_err, float(err.max()))
+    return {"value": total_bytes / secs / 1e9, "unit": "GB/s", "cores": oracle.num_threads(),
+            "kind": "oracle",
+            "sample": f"{n_seqs} of 8 sequences x 32 q-heads x 65536 keys, fp64 two-pass attention "
+                      f"({total_bytes / 1e9:.2f} GB of fp32 K/V, {secs:.1f} s); outputs agreed with the GPU "
+                      f"(max abs err {max_err:.2e})"}
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(json.dumps({"error": "this build runs on one GPU; --gpus must be 1 (no multi-GPU path)"}))
+        sys.exit(2)
+    import numpy as np
+    import torch
+
+    import exact_paged_causal_amd as atlas
+    import workloads
+
+    torch.cuda.set_device(0)
+    d = decode_setup(torch, workloads, atlas)
+    w = d["w"]
+    dec_out = torch.empty(workloads.query_shape(w), dtype=torch.float32, device="cuda")
+    dec_lse = torch.empty(w.batch, 1, w.hq, dtype=torch.float32, device="cuda")
+    args_tmp, _ = atlas.make_attn_args(d["q"], d["k"], d["v"], d["pt"], d["ctx"], w.scale,
+                                       split_tokens=args.split_tokens)
+    ws = torch.empty(atlas.atlas_decode_workspace_bytes(args_tmp), dtype=torch.uint8, device="cuda")
+
+    p = None
+    if not args.no_prefill:
+        p = prefill_setup(torch, workloads, np)
+        pw = p["w"]
+        pre_out = torch.empty(workloads.query_shape(pw), dtype=torch.float32, device="cuda")
+        pre_lse = torch.empty(pw.batch, pw.q_len, pw.hq, dtype=torch.float32, device="cuda")
+        pargs, _ = atlas.make_attn_args(p["q"], p["k"], p["v"], p["pt"], p["ctx"], pw.scale)
+        pws = torch.empty(atlas.atlas_prefill_workspace_bytes(pargs), dtype=torch.uint8, device="cuda")
+
+    def regen():
+        atlas.atlas_regenerate_pages(d["k"], d["v"], d["cold"], seed=w.seed, layer=w.layer)
+
+    def decode():
+        atlas.atlas_attend_decode(d["q"], d["k"], d["v"], d["pt"], d["ctx"], w.scale, out=dec_out,
+                                  lse=dec_lse, workspace=ws, split_tokens=args.split_tokens)
+
+    def prefill():
+        atlas.atlas_attend_prefill(p["q"], p["k"], p["v"], p["pt"], p["ctx"], pw.scale, out=pre_out,
+                                   lse=pre_lse, workspace=pws)
+
+    def step(t_regen=None, t_dec=None, t_pre=None):
+        (t_regen or (lambda f: f()))(regen)
+        (t_dec or (lambda f: f()))(decode)
+        if p is not None:
+            (t_pre or (lambda f: f()))(prefill)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    print(f"bench: warmup done ({args.warmup} steps)", file=sys.stderr, flush=True)
+
+    t_regen, t_dec, t_pre = Timer(torch), Timer(torch), Timer(torch)
+    s0, s1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    wall0 = time.perf_counter()
+    s0.record()
+    for _ in range(args.steps):
+        step(t_regen, t_dec, t_pre)
+    s1.record()
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - wall0
+    step_ms = s0.elapsed_time(s1) / args.steps
+    dec_ms = float(np.mean(t_dec.ms()))
+    regen_ms = float(np.mean(t_regen.ms()))
+    print(f"bench: timed {args.steps} steps in {wall:.2f} s", file=sys.stderr, flush=True)
+
+    kv_bytes = int(w.context_lens.astype(np.int64).sum()) * w.hkv * w.head_dim * 4 * 2
+    dec_gbs = kv_bytes / (dec_ms * 1e-3) / 1e9
+    n_cold = int(d["cold"].shape[0])
+    regen_bytes = n_cold * w.hkv * w.page_size * w.head_dim * 4 * 2
+    result = {
+        "metric": METRIC,
+        "value": round(dec_gbs, 1),
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(step_ms, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "f32",
+        "data": "synthetic",
+        "config": {
+            "workload": "long_context_decode: B=8 x 65536 tokens, Hq=32, Hkv=8, D=64, page 512, fp32, "
+                        "shuffled pool, 25% resident + 75% regenerated per step"
+                        + ("" if p is None else "; causal_prefill: S=8192, Hq=32, Hkv=8, D=128, page 128, bf16"),
+            "decode_attention_ms": round(dec_ms, 4),
+            "decode_kv_bytes": kv_bytes,
+            "regen_ms": round(regen_ms, 4),
+            "regen_pages": n_cold,
+            "regen_write_GBs": round(regen_bytes / (regen_ms * 1e-3) / 1e9, 1),
+            "decode_end_to_end_ms": round(dec_ms + regen_ms, 4),
+        },
+        "roofline": {
+            "bound": "hbm",
+            "kernel": "decode attention pass (split-KV fold + LSE merge)",
+            "achieved": round(dec_gbs, 1),
+            "peak": HBM_PEAK_GBS,
+            "unit": "GB/s",
+            "frac": round(dec_gbs / HBM_PEAK_GBS, 4),
+            "traffic": None,
+        },
+    }
+    if p is not None:
+        pre_ms = float(np.mean(t_pre.ms()))
+        S, hq, dd = pw.q_len, pw.hq, pw.head_dim
+        flops = 4.0 * dd * hq * S * (S + 1) / 2.0
+        tf = flops / (pre_ms * 1e-3) / 1e12
+        result["prefill"] = {
+            "value": round(tf, 1), "unit": "TFLOP/s", "ms": round(pre_ms, 4), "flop": flops,
+            "dtype": "bf16",
+            "roofline": {"bound": "mfma", "kernel": "tiled causal prefill", "achieved": round(tf, 1),
+                         "peak": BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
+                         "frac": round(tf / BF16_PEAK_TFLOPS, 4), "traffic": None},
+        }
+    if args.copy_calibration:
+        src = torch.empty(1 << 28, dtype=torch.uint8, device="cuda")   # 256 MiB
+        dst = torch.empty_like(src)
+        for _ in range(3):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        tc = Timer(torch)
+        for _ in range(10):
+            tc(lambda: dst.copy_(src))
+        torch.cuda.synchronize()
+        cms = float(np.mean(tc.ms()))
+        result["copy_calibration"] = {"bytes_read": src.numel(), "bytes_written": dst.numel(),
+                                      "ms": round(cms, 4),
+                                      "GBs": round(2 * src.numel() / (cms * 1e-3) / 1e9, 1)}
+    if not args.no_cpu_baseline:
+        import oracle
+        result["cpu_baseline"] = cpu_baseline(d, dec_out.cpu().numpy(), args.cpu_sample_seqs, np, oracle)
+    print(json.dumps(result), flush=True)
+
+
+if __name__ == "__main__":
+    main()

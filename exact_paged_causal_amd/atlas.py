@@ -247,9 +247,10 @@ def lib_status_from_error() -> int:
 def _attend(entry, ws_fn, q, k_pages, v_pages, page_table, context_lens, scale, out, lse,
             workspace, stream, **kw):
     B, q_len, hq, d = q.shape
+    want_lse = kw.pop("want_lse", True)
     if out is None:
         out = torch.empty((B, q_len, hq, d), dtype=torch.float32, device=q.device)
-    if lse is None and kw.pop("want_lse", True):
+    if lse is None and want_lse:
         lse = torch.empty((B, q_len, hq), dtype=torch.float32, device=q.device)
     args, keep = make_attn_args(q, k_pages, v_pages, page_table, context_lens, scale, out=out,
                                 lse=lse, **kw)

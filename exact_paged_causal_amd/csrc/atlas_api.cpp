@@ -83,7 +83,7 @@ struct Plan {
 };
 
 constexpr size_t kWorkspaceHeader = 256;  // validation-mode flags live here
-constexpr int kTargetItems = 8192;        // split work items to aim for (~32 per CU)
+constexpr int kTargetItems = 2048;        // split work items to aim for (~8 per CU)
 
 int32_t check_shapes(const atlas_attn_args *a, bool decode, Plan *p)
 {
@@ -105,8 +105,8 @@ int32_t check_shapes(const atlas_attn_args *a, bool decode, Plan *p)
         return fail(ATLAS_ERR_UNSUPPORTED, "page_size %d: powers of two up to 4096 only", a->page_size);
     if (a->num_phys_pages < 1 || a->max_pages_per_seq < 1)
         return fail(ATLAS_ERR_SHAPE, "num_phys_pages and max_pages_per_seq must be >= 1");
-    if (!std::isfinite(a->scale))
-        return fail(ATLAS_ERR_RANGE, "scale must be finite");
+    if (!std::isfinite(a->scale) || !(a->scale > 0.0f))
+        return fail(ATLAS_ERR_RANGE, "scale must be finite and > 0");
 
     int64_t max_ctx = 0;
     if (!mul_ok(a->max_pages_per_seq, a->page_size, &max_ctx) || max_ctx > INT32_MAX / 2)
@@ -203,7 +203,7 @@ int32_t check_shapes(const atlas_attn_args *a, bool decode, Plan *p)
     }
     p->split_tokens = (int)T;
     p->max_splits = atlas::max_splits_bound((int)max_ctx, (int)T, a->sink_tokens != nullptr);
-    if ((int64_t)p->max_splits > 65535 || items_per_split / a->batch > 65535)
+    if (p->max_splits > atlas::kMaxMergeSplits || items_per_split / a->batch > 65535)
         return fail(ATLAS_ERR_RANGE, "split grid too large (raise split_tokens)");
     int64_t slots = 0, ws = 0;
     if (!mul_ok(rows, p->max_splits, &slots) || !mul_ok(slots, (int64_t)(a->head_dim + 2) * 4, &ws))
@@ -275,6 +275,7 @@ int32_t validate_device(const atlas_attn_args *a, const Plan &p, hipStream_t str
     s.num_phys = a->num_phys_pages;
     s.max_pages = a->max_pages_per_seq;
     s.max_context = p.max_context;
+    s.check_v_f16 = p.path == Path::TiledPrefill ? 1 : 0;
     int flag = 0;
     e = hipMemsetAsync(s.flag, 0, sizeof(int), stream);
     if (e == hipSuccess)
@@ -285,8 +286,10 @@ int32_t validate_device(const atlas_attn_args *a, const Plan &p, hipStream_t str
         e = hipStreamSynchronize(stream);
     if (e != hipSuccess)
         return fail(ATLAS_ERR_DEVICE, "validation scan failed: %s", hipGetErrorString(e));
-    if (flag)
+    if (flag & 1)
         return fail(ATLAS_ERR_NONFINITE, "NaN or Inf in q or in the K/V rows the contexts cover");
+    if (flag & 2)
+        return fail(ATLAS_ERR_RANGE, "a V value exceeds 65504, the fp16 range of the tiled prefill's P.V product");
     return ok();
 }
 

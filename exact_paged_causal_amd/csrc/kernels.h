@@ -55,6 +55,8 @@ struct RegenArgs {
 
 // Largest page-id list one split work item stages in LDS.
 constexpr int kMaxSplitPages = 2048;
+// Most splits one output row may have (the merge keeps their weights in LDS).
+constexpr int kMaxMergeSplits = 8192;
 
 hipError_t launch_split_valu(const SplitArgs &a, int dtype, hipStream_t stream);
 hipError_t launch_split_mfma(const SplitArgs &a, hipStream_t stream);
@@ -84,8 +86,9 @@ struct ScanArgs {
     const void *v_pages;
     const int32_t *page_table;
     const int32_t *context_lens;
-    int *flag;                  // set to nonzero on a hit (cleared by the caller)
+    int *flag;                  // bit 0: NaN/Inf; bit 1: |V| beyond fp16 range (cleared by the caller)
     int32_t batch, q_len, hq, hkv, head_dim, page_shift, num_phys, max_pages, max_context;
+    int32_t check_v_f16;        // also flag |V| > 65504 (the tiled prefill's fp16 P.V product)
 };
 
 hipError_t launch_scan(const ScanArgs &a, int dtype, hipStream_t stream);

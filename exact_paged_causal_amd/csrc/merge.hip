@@ -20,7 +20,9 @@ namespace {
 template <int D>
 __global__ __launch_bounds__(64) void merge_kernel(SplitArgs a)
 {
-    constexpr int DPT = D / 64;  // dims per thread
+    constexpr int DPT = D / 64;  // dims per lane
+    extern __shared__ float s_f[];  // [max_splits] weights of the splits
+    const int lane = threadIdx.x;
     const int64_t row_id = blockIdx.x;
     const int h = (int)(row_id % a.hq);
     const int64_t bi = row_id / a.hq;
@@ -40,35 +42,49 @@ __global__ __launch_bounds__(64) void merge_kernel(SplitArgs a)
 
     const float *ml = a.ws_ml + row_id * a.max_splits * 2;
     const float *acc = a.ws_acc + row_id * a.max_splits * D;
+
+    // Pass 1 (lanes over splits): the maximum, then each split's weight.
     float mm = -INFINITY;
-    for (int s = 0; s < n; ++s)
+    for (int s = lane; s < n; s += 64)
         mm = fmaxf(mm, ml[2 * s]);
+    for (int off = 32; off > 0; off >>= 1)
+        mm = fmaxf(mm, __shfl_xor(mm, off));
     const float msafe = mm == -INFINITY ? 0.0f : mm;
     float L = 0.0f;
+    for (int s = lane; s < n; s += 64) {
+        const float f = fast_exp2(ml[2 * s] - msafe);
+        s_f[s] = f;
+        L = fmaf(ml[2 * s + 1], f, L);
+    }
+    for (int off = 32; off > 0; off >>= 1)
+        L += __shfl_xor(L, off);
+    __syncthreads();
+
+    // Pass 2 (lanes over dims): weighted sum of the accumulators, in split order.
     float o[DPT];
 #pragma unroll
     for (int e = 0; e < DPT; ++e)
         o[e] = 0.0f;
+#pragma unroll 8
     for (int s = 0; s < n; ++s) {
-        const float f = fast_exp2(ml[2 * s] - msafe);
-        L = fmaf(ml[2 * s + 1], f, L);
+        const float f = s_f[s];
 #pragma unroll
         for (int e = 0; e < DPT; ++e)
-            o[e] = fmaf(acc[(int64_t)s * D + e * 64 + threadIdx.x], f, o[e]);
+            o[e] = fmaf(acc[(int64_t)s * D + e * 64 + lane], f, o[e]);
     }
     float *orow = a.out + row_id * D;
     if (L > 0.0f) {
         const float inv = 1.0f / L;
 #pragma unroll
         for (int e = 0; e < DPT; ++e)
-            orow[e * 64 + threadIdx.x] = o[e] * inv;
-        if (a.lse && threadIdx.x == 0)
+            orow[e * 64 + lane] = o[e] * inv;
+        if (a.lse && lane == 0)
             a.lse[row_id] = (mm + log2f(L)) * kLn2;
     } else {
 #pragma unroll
         for (int e = 0; e < DPT; ++e)
-            orow[e * 64 + threadIdx.x] = __builtin_nanf("");
-        if (a.lse && threadIdx.x == 0)
+            orow[e * 64 + lane] = __builtin_nanf("");
+        if (a.lse && lane == 0)
             a.lse[row_id] = -INFINITY;
     }
 }
@@ -78,10 +94,11 @@ __global__ __launch_bounds__(64) void merge_kernel(SplitArgs a)
 hipError_t launch_merge(const SplitArgs &a, hipStream_t stream)
 {
     const int64_t rows = (int64_t)a.batch * a.q_len * a.hq;
+    const size_t lds = sizeof(float) * (size_t)a.max_splits;
     if (a.head_dim == 64)
-        hipLaunchKernelGGL(merge_kernel<64>, dim3((unsigned)rows), dim3(64), 0, stream, a);
+        hipLaunchKernelGGL(merge_kernel<64>, dim3((unsigned)rows), dim3(64), lds, stream, a);
     else
-        hipLaunchKernelGGL(merge_kernel<128>, dim3((unsigned)rows), dim3(64), 0, stream, a);
+        hipLaunchKernelGGL(merge_kernel<128>, dim3((unsigned)rows), dim3(64), lds, stream, a);
     return hipGetLastError();
 }
 

@@ -1,10 +1,324 @@
-// prefill_mfma.hip -- tiled causal prefill on the matrix cores (placeholder
-// until the tiled kernel lands: reports "not supported" so the C ABI returns
-// ATLAS_ERR_UNSUPPORTED instead of running anything else).
+// prefill_mfma.hip -- tiled causal prefill on the gfx950 matrix cores (bf16).
+//
+// CPUAttn README: the parallel lowering runs a fused QK -> Mod/RowNorm -> PV
+// tile pipeline, and an exact causal mask stops each query block at the last
+// key block it can reach.  This kernel is that pipeline for a paged bf16 K/V
+// history, with the cache-backed suffix positions of the same page (query i
+// of a sequence with L keys sits at position L - q_len + i):
+//
+//   workgroup  = 256 rows x one K/V head: the rows are (query position, q-head
+//                of the group) pairs, so a K/V tile staged in LDS serves all
+//                q-heads of the group (grouped-query attention);
+//   key blocks = 64 keys; block kb runs only while kb*64 <= the last row's
+//                position (causal block-stop); only blocks that reach past
+//                the first row's position apply the per-row causal mask;
+//   per wave   = 32 rows.  S^T = K Q^T on v_mfma_f32_32x32x16_bf16 (A = K
+//                from LDS, B = Q held in registers), so each lane owns one
+//                row's scores and the row max is lane-local plus one swap
+//                between the two lane halves; online softmax with exp2 and
+//                the scale folded by log2(e); rescaling of the accumulator is
+//                skipped while the running max grows by less than 2^8
+//                (results are the same up to rounding: every term uses the
+//                same reference max); P is rounded to fp16 (11-bit
+//                mantissa) and O^T += V^T P^T runs on
+//                v_mfma_f32_32x32x16_f16, with V converted bf16 -> fp16 while
+//                it is staged and read transposed by ds_read_b64_tr_b16.
+//                fp32 accumulation throughout, fp32 output.
+//   pipeline   = the next key block is fetched into registers while the
+//                current one is computed, then written to the other LDS
+//                buffer: one barrier per block.
+//   grid       = heavy-first: the query blocks with the most keys launch
+//                first; consecutive workgroups cycle over K/V heads, so all
+//                workgroups of one K/V head land on the same XCD (the
+//                hardware deals workgroups to the 8 XCDs round-robin) and
+//                share its L2.
+//
+// Precondition of the fp16 P.V product: |V| <= 65504 (validation mode
+// checks it).  Scores use bf16 K and Q exactly (products are exact in fp32).
+#include "device.h"
 #include "kernels.h"
 
 namespace atlas {
+namespace {
 
-hipError_t launch_prefill_mfma(const PrefillArgs &, hipStream_t) { return hipErrorNotSupported; }
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
+typedef _Float16 f16x2 __attribute__((ext_vector_type(2)));
+typedef float f32x2 __attribute__((ext_vector_type(2)));
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef short i16x4 __attribute__((ext_vector_type(4)));
+typedef short i16x8 __attribute__((ext_vector_type(8)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) i16x4 lds_i16x4;
+
+constexpr int kWaves = 8;
+constexpr int kRows = 32 * kWaves;   // rows per workgroup
+constexpr int kBN = 64;              // keys per block
+constexpr int kPad = 8;              // LDS row padding (elements)
+constexpr float kRescaleSlack = 8.0f;  // log2 units the running max may lag
+
+template <int D>
+struct Smem {
+    uint16_t k[2][kBN][D + kPad];  // bf16 bits
+    uint16_t v[2][kBN][D + kPad];  // fp16 bits
+};
+
+__device__ __forceinline__ uint32_t bf16pair_to_f16pair(uint32_t x)
+{
+    f32x2 f = {bf16_lo(x), bf16_hi(x)};
+    return __builtin_bit_cast(uint32_t, __builtin_convertvector(f, f16x2));
+}
+
+template <int D>
+__global__ __launch_bounds__(512) void prefill_kernel(PrefillArgs a)
+{
+    constexpr int KS = D / 16;            // k-steps of the QK product
+    constexpr int DT = D / 32;            // 32-dim tiles of the output
+    constexpr int CPR = D / 8;            // 16-byte chunks per K/V row
+    constexpr int CH = kBN * CPR / 512;   // chunks per thread per tile
+    __shared__ Smem<D> sm;
+
+    const int tid = threadIdx.x;
+    const int wave = tid >> 6;
+    const int lane = tid & 63;
+    const int half = lane >> 5;
+
+    // Heavy-first workgroup order; consecutive ids cycle over (b, K/V head).
+    const int per_q = a.batch * a.hkv;
+    const int qb_rev = blockIdx.x / per_q;
+    const int rem = blockIdx.x - qb_rev * per_q;
+    const int b = rem / a.hkv;
+    const int g = rem - b * a.hkv;
+    const int qblock = a.n_qblocks - 1 - qb_rev;
+    const int G = a.groups.max_group;
+    const int npos = kRows / G;
+    const int gstart = a.groups.start[g];
+    const int gsize = a.groups.start[g + 1] - gstart;
+
+    int ctx = a.context_lens[b];
+    ctx = ctx < 0 ? 0 : (ctx > a.max_context ? a.max_context : ctx);
+    const int i0 = qblock * npos;
+    const int i1 = i0 + npos < a.q_len ? i0 + npos : a.q_len;
+    const int pos_lo = ctx - a.q_len + i0;
+    const int pos_hi = ctx - a.q_len + i1 - 1;
+
+    // This lane's row.
+    const int r = wave * 32 + (lane & 31);
+    const int ri = r / G;
+    const int rj = r - ri * G;
+    const int qi = i0 + ri;
+    const bool row_ok = ri < npos && qi < i1 && rj < gsize;
+    const int pos = row_ok ? ctx - a.q_len + qi : -1;
+    const int h = row_ok ? a.groups.list[gstart + rj] : 0;
+
+    bf16x8 qf[KS];
+    {
+        const uint16_t *qrow = reinterpret_cast<const uint16_t *>(a.q) +
+                               (((int64_t)b * a.q_len + (row_ok ? qi : 0)) * a.hq + h) * D;
+#pragma unroll
+        for (int s = 0; s < KS; ++s) {
+            if (row_ok)
+                qf[s] = *reinterpret_cast<const bf16x8 *>(qrow + 16 * s + 8 * half);
+            else
+                qf[s] = bf16x8{};
+        }
+    }
+
+    const int ps = a.page_shift;
+    const int pmask = (1 << ps) - 1;
+    const uint16_t *kpages = reinterpret_cast<const uint16_t *>(a.k_pages);
+    const uint16_t *vpages = reinterpret_cast<const uint16_t *>(a.v_pages);
+    const int32_t *ptab = a.page_table + (int64_t)b * a.max_pages;
+
+    // Global -> registers for key block kb (zeros past the last visible key).
+    uint4 kreg[CH], vreg[CH];
+    auto fetch = [&](int kb) {
+#pragma unroll
+        for (int u = 0; u < CH; ++u) {
+            const int c = tid + 512 * u;
+            const int row = c / CPR;
+            const int col = c - row * CPR;
+            const int j = kb * kBN + row;
+            if (j <= pos_hi) {
+                int pid = ptab[j >> ps];
+                pid = ((unsigned)pid < (unsigned)a.num_phys) ? pid : 0;
+                const int64_t off = ((((int64_t)pid * a.hkv + g) << ps) + (j & pmask)) * D + col * 8;
+                kreg[u] = *reinterpret_cast<const uint4 *>(kpages + off);
+                vreg[u] = *reinterpret_cast<const uint4 *>(vpages + off);
+            } else {
+                kreg[u] = make_uint4(0, 0, 0, 0);
+                vreg[u] = make_uint4(0, 0, 0, 0);
+            }
+        }
+    };
+    // Registers -> LDS buffer (V converted to fp16).
+    auto stash = [&](int buf) {
+#pragma unroll
+        for (int u = 0; u < CH; ++u) {
+            const int c = tid + 512 * u;
+            const int row = c / CPR;
+            const int col = c - row * CPR;
+            *reinterpret_cast<uint4 *>(&sm.k[buf][row][col * 8]) = kreg[u];
+            uint4 v16;
+            v16.x = bf16pair_to_f16pair(vreg[u].x);
+            v16.y = bf16pair_to_f16pair(vreg[u].y);
+            v16.z = bf16pair_to_f16pair(vreg[u].z);
+            v16.w = bf16pair_to_f16pair(vreg[u].w);
+            *reinterpret_cast<uint4 *>(&sm.v[buf][row][col * 8]) = v16;
+        }
+    };
+
+    const float c_log2 = a.scale * kLog2e;
+    float m_ref = -INFINITY;  // reference max (log2 units) the accumulator is scaled to
+    float l_part = 0.0f;      // this lane-half's share of the softmax denominator
+    f32x16 acc[DT];
+#pragma unroll
+    for (int t = 0; t < DT; ++t)
+        acc[t] = f32x16{};
+
+    const int kb_last = pos_hi >= 0 ? pos_hi / kBN : -1;
+    if (kb_last >= 0) {
+        fetch(0);
+        stash(0);
+    }
+    __syncthreads();
+
+    for (int kb = 0; kb <= kb_last; ++kb) {
+        const int cur = kb & 1;
+        if (kb < kb_last)
+            fetch(kb + 1);
+
+        // S^T for the block: two 32-key tiles.
+        f32x16 st[2];
+#pragma unroll
+        for (int t = 0; t < 2; ++t) {
+            st[t] = f32x16{};
+#pragma unroll
+            for (int s = 0; s < KS; ++s) {
+                const bf16x8 kf =
+                    *reinterpret_cast<const bf16x8 *>(&sm.k[cur][32 * t + (lane & 31)][16 * s + 8 * half]);
+                st[t] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf, qf[s], st[t], 0, 0, 0);
+            }
+        }
+
+        // Causal mask where the block reaches past the first row.
+        if (kb * kBN + kBN - 1 > pos_lo) {
+#pragma unroll
+            for (int t = 0; t < 2; ++t)
+#pragma unroll
+                for (int e = 0; e < 16; ++e) {
+                    const int j = kb * kBN + 32 * t + 8 * (e >> 2) + 4 * half + (e & 3);
+                    if (j > pos)
+                        st[t][e] = -INFINITY;
+                }
+        }
+
+        // Online softmax (lane = one row, two lane halves share it).
+        float mx = st[0][0];
+#pragma unroll
+        for (int t = 0; t < 2; ++t)
+#pragma unroll
+            for (int e = 0; e < 16; ++e)
+                mx = fmaxf(mx, st[t][e]);
+        mx = fmaxf(mx, __shfl_xor(mx, 32));
+        const float m_blk = mx * c_log2;
+        if (m_blk > m_ref + kRescaleSlack) {
+            const float alpha = fast_exp2(m_ref - m_blk);
+            l_part *= alpha;
+#pragma unroll
+            for (int t = 0; t < DT; ++t)
+                acc[t] *= alpha;
+            m_ref = m_blk;
+        }
+        const float msafe = m_ref == -INFINITY ? 0.0f : m_ref;
+
+        // P^T as the B operand: tile t, k-step ks -> elements 8ks..8ks+7,
+        // packed two fp16 values per 32-bit word.
+        u32x4 pw[2][2];
+#pragma unroll
+        for (int t = 0; t < 2; ++t) {
+#pragma unroll
+            for (int e = 0; e < 16; e += 2) {
+                const float p0 = fast_exp2(fmaf(st[t][e], c_log2, -msafe));
+                const float p1 = fast_exp2(fmaf(st[t][e + 1], c_log2, -msafe));
+                l_part += p0 + p1;
+                pw[t][e >> 3][(e & 7) >> 1] =
+                    __builtin_bit_cast(uint32_t, __builtin_convertvector(f32x2{p0, p1}, f16x2));
+            }
+        }
+
+        // O^T += V^T P^T.  A operand via transposed LDS reads: lane 16q+j loads
+        // V[key0 + j/4][d0 + 4(j%4) .. +3] and receives V[key0 + k][d0 + j] (k=0..3).
+        const int q16 = lane >> 4;
+        const int j16 = lane & 15;
+#pragma unroll
+        for (int dt = 0; dt < DT; ++dt) {
+#pragma unroll
+            for (int t = 0; t < 2; ++t) {
+#pragma unroll
+                for (int ks = 0; ks < 2; ++ks) {
+                    const int key0 = 32 * t + 16 * ks + 4 * half + (j16 >> 2);
+                    const int dim0 = 32 * dt + 16 * (q16 & 1) + 4 * (j16 & 3);
+                    const i16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+                        (lds_i16x4 *)(&sm.v[cur][key0][dim0]));
+                    const i16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+                        (lds_i16x4 *)(&sm.v[cur][key0 + 8][dim0]));
+                    // Whole-vector concatenation: extracting the read's 16-bit
+                    // elements one by one is mis-compiled by this toolchain
+                    // (the operand gets splatted halves).
+                    const f16x8 va = __builtin_bit_cast(f16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
+                    const f16x8 pb = __builtin_bit_cast(f16x8, pw[t][ks]);
+                    acc[dt] = __builtin_amdgcn_mfma_f32_32x32x16_f16(va, pb, acc[dt], 0, 0, 0);
+                }
+            }
+        }
+
+        if (kb < kb_last)
+            stash(cur ^ 1);
+        __syncthreads();
+    }
+
+    // Epilogue: O = O^T / l, lse = (m + log2 l) ln 2.
+    const float l_row = l_part + __shfl_xor(l_part, 32);
+    if (!row_ok)
+        return;
+    float *orow = a.out + (((int64_t)b * a.q_len + qi) * a.hq + h) * D;
+    const bool any = l_row > 0.0f;
+    const float inv = any ? 1.0f / l_row : __builtin_nanf("");
+#pragma unroll
+    for (int dt = 0; dt < DT; ++dt)
+#pragma unroll
+        for (int e4 = 0; e4 < 4; ++e4) {
+            float4 o;
+            o.x = acc[dt][4 * e4 + 0] * inv;
+            o.y = acc[dt][4 * e4 + 1] * inv;
+            o.z = acc[dt][4 * e4 + 2] * inv;
+            o.w = acc[dt][4 * e4 + 3] * inv;
+            *reinterpret_cast<float4 *>(orow + 32 * dt + 8 * e4 + 4 * half) = o;
+        }
+    if (a.lse && half == 0)
+        a.lse[((int64_t)b * a.q_len + qi) * a.hq + h] = any ? (m_ref + log2f(l_row)) * kLn2 : -INFINITY;
+}
+
+}  // namespace
+
+hipError_t launch_prefill_mfma(const PrefillArgs &a, hipStream_t stream)
+{
+    if (a.head_dim != 64 && a.head_dim != 128)
+        return hipErrorNotSupported;
+    if (a.groups.max_group < 1 || a.groups.max_group > kRows)
+        return hipErrorNotSupported;
+    const int npos = kRows / a.groups.max_group;
+    PrefillArgs k = a;
+    k.n_qblocks = (a.q_len + npos - 1) / npos;
+    const int64_t blocks = (int64_t)k.n_qblocks * a.batch * a.hkv;
+    if (blocks > 0x7FFFFFFF)
+        return hipErrorInvalidValue;
+    if (a.head_dim == 64)
+        hipLaunchKernelGGL(prefill_kernel<64>, dim3((unsigned)blocks), dim3(512), 0, stream, k);
+    else
+        hipLaunchKernelGGL(prefill_kernel<128>, dim3((unsigned)blocks), dim3(512), 0, stream, k);
+    return hipGetLastError();
+}
 
 }  // namespace atlas

@@ -4,7 +4,9 @@
 // inputs before they reach the cache.  In validation mode the C ABI runs this
 // scan first: every query element, and every K/V element of the rows each
 // sequence's context covers (rows past the context are never read and are
-// not scanned).  A hit sets a flag word, which the host reads back.
+// not scanned).  For the tiled bf16 prefill it also flags V values outside
+// the fp16 range its P.V product uses.  Hits set bits of a flag word, which
+// the host reads back.
 #include "device.h"
 #include "kernels.h"
 
@@ -13,6 +15,21 @@ namespace {
 
 template <typename E>
 __device__ __forceinline__ bool finite_elem(E x);
+
+template <typename E>
+__device__ __forceinline__ bool beyond_f16(E x);
+
+template <>
+__device__ __forceinline__ bool beyond_f16<float>(float x)
+{
+    return fabsf(x) > 65504.0f;
+}
+
+template <>
+__device__ __forceinline__ bool beyond_f16<uint16_t>(uint16_t x)
+{
+    return fabsf(__uint_as_float((uint32_t)x << 16)) > 65504.0f;
+}
 
 template <>
 __device__ __forceinline__ bool finite_elem<float>(float x)
@@ -35,6 +52,7 @@ __global__ __launch_bounds__(256) void scan_kernel(ScanArgs a)
     int ctx = a.context_lens[b];
     ctx = ctx < 0 ? 0 : (ctx > a.max_context ? a.max_context : ctx);
     bool bad = false;
+    bool wide = false;
     if (lp == a.max_pages) {
         const int64_t n = (int64_t)a.q_len * a.hq * a.head_dim;
         const E *q = reinterpret_cast<const E *>(a.q) + (int64_t)b * n;
@@ -52,14 +70,18 @@ __global__ __launch_bounds__(256) void scan_kernel(ScanArgs a)
                     const int64_t h = i / ((int64_t)rows * a.head_dim);
                     const int64_t rest = i - h * rows * a.head_dim;
                     const int64_t off = ((int64_t)pid * a.hkv + h) * per_head + rest;
+                    const E vv = reinterpret_cast<const E *>(a.v_pages)[off];
                     bad |= !finite_elem<E>(reinterpret_cast<const E *>(a.k_pages)[off]);
-                    bad |= !finite_elem<E>(reinterpret_cast<const E *>(a.v_pages)[off]);
+                    bad |= !finite_elem<E>(vv);
+                    wide |= a.check_v_f16 && beyond_f16<E>(vv);
                 }
             }
         }
     }
     if (bad)
         atomicOr(a.flag, 1);
+    if (wide)
+        atomicOr(a.flag, 2);
 }
 
 }  // namespace

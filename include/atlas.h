@@ -103,7 +103,7 @@ typedef struct atlas_attn_args {
     int32_t max_pages_per_seq;  /* columns of page_table; every L_b <= max_pages_per_seq * P */
     int32_t split_tokens;       /* keys per split-KV work item; 0 = library's choice
                                    (results depend on it only through rounding order) */
-    float scale;                /* score scale, e.g. 1/sqrt(D) */
+    float scale;                /* score scale, finite and > 0, e.g. 1/sqrt(D) */
     int32_t reserved0;
     const int32_t *head_map;    /* HOST [Hq] -> K/V head, or NULL for h / (Hq / Hkv) */
     const void *q;              /* device, see layout above */
@@ -185,7 +185,9 @@ int32_t atlas_attend_decode(const atlas_attn_args *args, void *stream);
  * suffix of the history (requires q_len <= L_b).  bf16 with q_len >= 64 and
  * no window / sink / softcap arrays runs the tiled matrix-core kernel
  * (query x key tiles with causal block-stop: each query tile stops at the
- * last key tile its last row can see).  Every other case runs the split-KV
+ * last key tile its last row can see).  Its P.V product runs in fp16 with
+ * fp32 accumulation, so it requires |V| <= 65504 (validation mode checks
+ * this and returns ATLAS_ERR_RANGE).  Every other case runs the split-KV
  * kernels of atlas_attend_decode with each (query, q-head) pair as a row.
  */
 int32_t atlas_attend_prefill(const atlas_attn_args *args, void *stream);
