@@ -162,10 +162,13 @@ int32_t check_shapes(const atlas_attn_args *a, bool decode, Plan *p)
     p->max_context = (int)max_ctx;
     p->rows_total = rows;
 
-    // Path.
+    // Path: the tiled kernel for long bf16 prefills without variants; else the
+    // split-KV kernels (matrix cores for bf16, vector ALUs for fp32).
     const bool variants = a->window || a->sink_tokens || a->softcap;
     if (!decode && a->dtype == ATLAS_DTYPE_BF16 && a->q_len >= 64 && !variants)
         p->path = Path::TiledPrefill;
+    else if (a->dtype == ATLAS_DTYPE_BF16)
+        p->path = Path::SplitMfma;
     else
         p->path = Path::SplitValu;
 
@@ -177,8 +180,12 @@ int32_t check_shapes(const atlas_attn_args *a, bool decode, Plan *p)
     // Split-KV plan: rows of a K/V head per work item, then keys per split.
     const int64_t rows_per_head = (int64_t)a->q_len * gmax;
     int rpi = 1;
-    while (rpi < rows_per_head && rpi < 8)
-        rpi <<= 1;
+    if (p->path == Path::SplitMfma) {
+        rpi = 16;  // the matrix-core fold always takes 16 rows (MFMA width)
+    } else {
+        while (rpi < rows_per_head && rpi < 8)
+            rpi <<= 1;
+    }
     p->rows_per_item = rpi;
     p->n_chunks = (int)((rows_per_head + rpi - 1) / rpi);
     const int64_t items_per_split = (int64_t)a->batch * hkv * p->n_chunks;
@@ -370,12 +377,14 @@ int32_t attend(const atlas_attn_args *a, void *stream_ptr, bool decode)
 
     if (std::getenv("ATLAS_DEBUG"))
         std::fprintf(stderr,
-                     "atlas: split-KV %s dtype=%d rows/item=%d chunks=%d split_tokens=%d max_splits=%d "
+                     "atlas: split-KV %s (%s) rows/item=%d chunks=%d split_tokens=%d max_splits=%d "
                      "workspace=%zu\n",
-                     decode ? "decode" : "prefill", a->dtype, p.rows_per_item, p.n_chunks, p.split_tokens,
+                     decode ? "decode" : "prefill", p.path == Path::SplitMfma ? "mfma" : "valu",
+                     p.rows_per_item, p.n_chunks, p.split_tokens,
                      p.max_splits, p.workspace);
 
-    hipError_t e = atlas::launch_split_valu(k, a->dtype, stream);
+    hipError_t e = p.path == Path::SplitMfma ? atlas::launch_split_mfma(k, stream)
+                                             : atlas::launch_split_valu(k, stream);
     if (e != hipSuccess)
         return fail(ATLAS_ERR_DEVICE, "split launch: %s", hipGetErrorString(e));
     e = atlas::launch_merge(k, stream);

@@ -58,8 +58,8 @@ constexpr int kMaxSplitPages = 2048;
 // Most splits one output row may have (the merge keeps their weights in LDS).
 constexpr int kMaxMergeSplits = 8192;
 
-hipError_t launch_split_valu(const SplitArgs &a, int dtype, hipStream_t stream);
-hipError_t launch_split_mfma(const SplitArgs &a, hipStream_t stream);
+hipError_t launch_split_valu(const SplitArgs &a, hipStream_t stream);   // fp32 K/V
+hipError_t launch_split_mfma(const SplitArgs &a, hipStream_t stream);   // bf16 K/V
 hipError_t launch_merge(const SplitArgs &a, hipStream_t stream);
 hipError_t launch_regen(const RegenArgs &a, int dtype, hipStream_t stream);
 

@@ -1,0 +1,321 @@
+// split_mfma.hip -- split-KV fold on the matrix cores (bf16 K/V).
+//
+// Same work items and partial states as split_valu.hip (one workgroup per
+// (sequence, K/V head, chunk of rows, span of keys); plan.h fixes the spans),
+// for bf16 inputs, where the vector ALUs alone cannot keep up with HBM: a
+// group of 8 q-heads costs 4 flop per K/V byte.
+//
+// Per wave, 32 keys at a time (the 4 waves interleave 32-key chunks):
+//   S^T = K Q^T     v_mfma_f32_16x16x32_bf16, A = 16 keys x 32 dims loaded
+//                   straight from the page into the A-operand layout (each
+//                   lane 16 contiguous bytes of one key row), B = Q^T for the
+//                   item's <= 16 rows (q-heads of the group x queries) kept in
+//                   registers; each lane ends up with 8 scores of one row.
+//   softmax         row max over the 4 lanes that share a row (two xor
+//                   shuffles), exp2 with the scale folded by log2(e), and a
+//                   lazily rescaled accumulator (the reference max may lag the
+//                   running max by up to 2^8; every term uses the same
+//                   reference, so only rounding changes).
+//   O^T += V^T P^T  v_mfma_f32_16x16x32_bf16 twice: P is split into a bf16
+//                   high part and a bf16 remainder (together ~16 significant
+//                   bits), so V stays exact bf16 with no range restriction.
+//                   V is staged in the wave's own LDS tile and read transposed
+//                   with ds_read_b64_tr_b16 (4 consecutive keys of one dim per
+//                   read).
+// The next chunk's K and V are loaded into registers before the current one
+// is computed.  At the end the 4 waves' states are combined in LDS and one
+// (m, l, acc) partial per row is written; merge.hip finishes.
+#include "device.h"
+#include "kernels.h"
+
+namespace atlas {
+namespace {
+
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef float f32x2 __attribute__((ext_vector_type(2)));
+typedef short i16x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) i16x4 lds_i16x4;
+
+constexpr int kChunk = 32;            // keys per wave step
+constexpr int kRowsMax = 16;          // rows per work item (MFMA N)
+constexpr float kRescaleSlack = 8.0f;
+
+template <int D>
+struct SplitSmem {
+    static constexpr int RS = D + 8;  // padded LDS row (elements)
+    union {
+        uint16_t v[4][kChunk][RS];    // per-wave V tile (bf16 bits)
+        float acc[4][kRowsMax][D];    // end-of-span wave states
+    } u;
+    float m[4][kRowsMax];
+    float l[4][kRowsMax];
+    int32_t pid[kMaxSplitPages];
+};
+
+// bf16 pair (hi part, remainder) of two fp32 values, packed per part.
+__device__ __forceinline__ void split_hi_lo(float p0, float p1, uint32_t &hi, uint32_t &lo)
+{
+    const bf16x2 h = __builtin_convertvector(f32x2{p0, p1}, bf16x2);
+    hi = __builtin_bit_cast(uint32_t, h);
+    const float r0 = p0 - bf16_lo(hi);
+    const float r1 = p1 - bf16_hi(hi);
+    lo = __builtin_bit_cast(uint32_t, __builtin_convertvector(f32x2{r0, r1}, bf16x2));
+}
+
+template <int D>
+__global__ __launch_bounds__(256) void split_mfma_kernel(SplitArgs a)
+{
+    constexpr int KS = D / 32;                 // QK k-steps
+    constexpr int DT = D / 16;                 // output dim tiles
+    constexpr int CPR = D / 8;                 // 16-byte pieces per row
+    constexpr int VCH = kChunk * CPR / 64;     // V pieces per lane per chunk
+    __shared__ SplitSmem<D> sm;
+
+    const int tid = threadIdx.x;
+    const int wave = tid >> 6;
+    const int lane = tid & 63;
+    const int l16 = lane & 15;
+    const int g4 = lane >> 4;
+
+    const int split = blockIdx.x;
+    const int g = blockIdx.y / a.n_chunks;
+    const int chunk = blockIdx.y - g * a.n_chunks;
+    const int b = blockIdx.z;
+    const int gstart = a.groups.start[g];
+    const int gsize = a.groups.start[g + 1] - gstart;
+
+    int ctx = a.context_lens[b];
+    ctx = ctx < 0 ? 0 : (ctx > a.max_context ? a.max_context : ctx);
+    const ChunkRows cr = chunk_rows(chunk, kRowsMax, gsize, a.q_len, ctx);
+    if (cr.r0 >= cr.r1)
+        return;
+    const int W = a.window ? a.window[b] : 0;
+    const int S = a.sinks ? a.sinks[b] : 0;
+    const float cap = a.softcap ? a.softcap[b] : 0.0f;
+    const SplitPlan plan = plan_splits(cr.pos_min, cr.pos_max, W, S, a.split_tokens);
+    if (split >= plan.n_splits)
+        return;
+    int ka, kb;
+    split_range(plan, split, a.split_tokens, &ka, &kb);
+
+    const int ps = a.page_shift;
+    const int pmask = (1 << ps) - 1;
+    const int p0 = ka >> ps;
+    const int np = ((kb - 1) >> ps) - p0 + 1;
+    for (int t = tid; t < np; t += 256) {
+        int pid = a.page_table[(int64_t)b * a.max_pages + p0 + t];
+        sm.pid[t] = ((unsigned)pid < (unsigned)a.num_phys) ? pid : 0;
+    }
+
+    // This lane's row (column of the S^T / O^T tiles) and its query operand.
+    const int rr = cr.r0 + l16;
+    const bool row_ok = rr < cr.r1;
+    const int qi = row_ok ? rr / gsize : 0;
+    const int h = row_ok ? a.groups.list[gstart + rr % gsize] : 0;
+    const int pos = row_ok ? ctx - a.q_len + qi : -1;
+    bf16x8 qf[KS];
+    {
+        const uint16_t *qrow = reinterpret_cast<const uint16_t *>(a.q) +
+                               (((int64_t)b * a.q_len + qi) * a.hq + h) * D;
+#pragma unroll
+        for (int s = 0; s < KS; ++s)
+            qf[s] = row_ok ? *reinterpret_cast<const bf16x8 *>(qrow + 32 * s + 8 * g4) : bf16x8{};
+    }
+    __syncthreads();
+
+    const uint16_t *kpages = reinterpret_cast<const uint16_t *>(a.k_pages);
+    const uint16_t *vpages = reinterpret_cast<const uint16_t *>(a.v_pages);
+    const int64_t head_rows = (int64_t)g << ps;
+    auto row_ptr = [&](const uint16_t *base, int j) {
+        const int jj = j < kb ? j : kb - 1;
+        const int pid = sm.pid[(jj >> ps) - p0];
+        return base + ((((int64_t)pid * a.hkv) << ps) + head_rows + (jj & pmask)) * D;
+    };
+
+    // K operand registers (2 tiles x KS steps) and V staging registers.
+    bf16x8 kreg[2][KS];
+    uint4 vreg[VCH];
+    auto load_chunk = [&](int cb) {
+#pragma unroll
+        for (int t = 0; t < 2; ++t) {
+            const uint16_t *kr = row_ptr(kpages, cb + 16 * t + l16);
+#pragma unroll
+            for (int s = 0; s < KS; ++s)
+                kreg[t][s] = *reinterpret_cast<const bf16x8 *>(kr + 32 * s + 8 * g4);
+        }
+#pragma unroll
+        for (int u = 0; u < VCH; ++u) {
+            const int c = lane + 64 * u;
+            const int key = c / CPR;
+            const int col = c - key * CPR;
+            vreg[u] = *reinterpret_cast<const uint4 *>(row_ptr(vpages, cb + key) + col * 8);
+        }
+    };
+
+    const float qk_scale = a.scale;
+    float m_ref = -INFINITY;
+    float l_part = 0.0f;
+    f32x4 acc[DT];
+#pragma unroll
+    for (int t = 0; t < DT; ++t)
+        acc[t] = f32x4{};
+
+    int cb = ka + kChunk * wave;
+    if (cb < kb)
+        load_chunk(cb);
+    for (; cb < kb; cb += 4 * kChunk) {
+        // Stage this chunk's V, then prefetch the next chunk.
+#pragma unroll
+        for (int u = 0; u < VCH; ++u) {
+            const int c = lane + 64 * u;
+            const int key = c / CPR;
+            const int col = c - key * CPR;
+            *reinterpret_cast<uint4 *>(&sm.u.v[wave][key][col * 8]) = vreg[u];
+        }
+        bf16x8 kcur[2][KS];
+#pragma unroll
+        for (int t = 0; t < 2; ++t)
+#pragma unroll
+            for (int s = 0; s < KS; ++s)
+                kcur[t][s] = kreg[t][s];
+        if (cb + 4 * kChunk < kb)
+            load_chunk(cb + 4 * kChunk);
+
+        // S^T tiles: lane holds row l16, keys 16t + 4*g4 + j.
+        f32x4 st[2];
+#pragma unroll
+        for (int t = 0; t < 2; ++t) {
+            st[t] = f32x4{};
+#pragma unroll
+            for (int s = 0; s < KS; ++s)
+                st[t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kcur[t][s], qf[s], st[t], 0, 0, 0);
+        }
+
+        // Scale, softcap, mask (log2 units).
+        float x[8];
+#pragma unroll
+        for (int t = 0; t < 2; ++t)
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+                const int key = cb + 16 * t + 4 * g4 + j;
+                float s = st[t][j] * qk_scale;
+                if (cap > 0.0f)
+                    s = cap * tanhf(s / cap);
+                const bool vis = key < kb && key <= pos && (W <= 0 || key > pos - W || key < S);
+                x[4 * t + j] = vis ? s * kLog2e : -INFINITY;
+            }
+        float mx = x[0];
+#pragma unroll
+        for (int e = 1; e < 8; ++e)
+            mx = fmaxf(mx, x[e]);
+        mx = fmaxf(mx, __shfl_xor(mx, 16));
+        mx = fmaxf(mx, __shfl_xor(mx, 32));
+        if (mx > m_ref + kRescaleSlack) {
+            const float alpha = fast_exp2(m_ref - mx);
+            l_part *= alpha;
+#pragma unroll
+            for (int t = 0; t < DT; ++t)
+                acc[t] *= alpha;
+            m_ref = mx;
+        }
+        const float msafe = m_ref == -INFINITY ? 0.0f : m_ref;
+        u32x4 phi, plo;
+#pragma unroll
+        for (int e = 0; e < 8; e += 2) {
+            const float p0v = fast_exp2(x[e] - msafe);
+            const float p1v = fast_exp2(x[e + 1] - msafe);
+            l_part += p0v + p1v;
+            uint32_t hi, lo;
+            split_hi_lo(p0v, p1v, hi, lo);
+            phi[e >> 1] = hi;
+            plo[e >> 1] = lo;
+        }
+        const bf16x8 pbh = __builtin_bit_cast(bf16x8, phi);
+        const bf16x8 pbl = __builtin_bit_cast(bf16x8, plo);
+
+        // The tile's transposed reads must follow its writes in this wave.
+        __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+        __builtin_amdgcn_wave_barrier();
+        __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+
+        // O^T += V^T P^T: slots 0..3 = keys 4*g4 + k, slots 4..7 = 16 + 4*g4 + k.
+#pragma unroll
+        for (int dt = 0; dt < DT; ++dt) {
+            const int key0 = 4 * g4 + (l16 >> 2);
+            const int dim0 = 16 * dt + 4 * (l16 & 3);
+            const i16x4 r0 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4 *)(&sm.u.v[wave][key0][dim0]));
+            const i16x4 r1 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4 *)(&sm.u.v[wave][key0 + 16][dim0]));
+            // Whole-vector concatenation (element-wise extraction from these
+            // reads is mis-compiled by this toolchain).
+            const bf16x8 va = __builtin_bit_cast(bf16x8, __builtin_shufflevector(r0, r1, 0, 1, 2, 3, 4, 5, 6, 7));
+            acc[dt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(va, pbh, acc[dt], 0, 0, 0);
+            acc[dt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(va, pbl, acc[dt], 0, 0, 0);
+        }
+        // The next chunk's writes must not overtake these reads.
+        __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+        __builtin_amdgcn_wave_barrier();
+        __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+    }
+
+    // Per-row sum of the four lane groups.
+    l_part += __shfl_xor(l_part, 16);
+    l_part += __shfl_xor(l_part, 32);
+    __syncthreads();  // every wave is done with its V tile (the state area aliases it)
+#pragma unroll
+    for (int dt = 0; dt < DT; ++dt)
+#pragma unroll
+        for (int j = 0; j < 4; ++j)
+            sm.u.acc[wave][l16][16 * dt + 4 * g4 + j] = acc[dt][j];
+    if (g4 == 0) {
+        sm.m[wave][l16] = m_ref;
+        sm.l[wave][l16] = l_part;
+    }
+    __syncthreads();
+
+    for (int idx = tid; idx < kRowsMax * D; idx += 256) {
+        const int r = idx / D;
+        const int d = idx - r * D;
+        const int row = cr.r0 + r;
+        if (row >= cr.r1)
+            continue;
+        float mm = sm.m[0][r];
+#pragma unroll
+        for (int w = 1; w < 4; ++w)
+            mm = fmaxf(mm, sm.m[w][r]);
+        const float msafe = mm == -INFINITY ? 0.0f : mm;
+        float ls = 0.0f, as = 0.0f;
+#pragma unroll
+        for (int w = 0; w < 4; ++w) {
+            const float f = fast_exp2(sm.m[w][r] - msafe);
+            ls = fmaf(sm.l[w][r], f, ls);
+            as = fmaf(sm.u.acc[w][r][d], f, as);
+        }
+        const int i = row / gsize;
+        const int hh = a.groups.list[gstart + row % gsize];
+        const int64_t slot = (((int64_t)b * a.q_len + i) * a.hq + hh) * a.max_splits + split;
+        a.ws_acc[slot * D + d] = as;
+        if (d == 0) {
+            a.ws_ml[slot * 2 + 0] = mm;
+            a.ws_ml[slot * 2 + 1] = ls;
+        }
+    }
+}
+
+}  // namespace
+
+hipError_t launch_split_mfma(const SplitArgs &a, hipStream_t stream)
+{
+    if (a.rows_per_item != kRowsMax)
+        return hipErrorInvalidValue;
+    dim3 grid(a.max_splits, a.hkv * a.n_chunks, a.batch);
+    if (a.head_dim == 64)
+        hipLaunchKernelGGL(split_mfma_kernel<64>, grid, dim3(256), 0, stream, a);
+    else
+        hipLaunchKernelGGL(split_mfma_kernel<128>, grid, dim3(256), 0, stream, a);
+    return hipGetLastError();
+}
+
+}  // namespace atlas

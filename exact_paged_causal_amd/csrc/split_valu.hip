@@ -1,4 +1,5 @@
-// split_valu.hip -- split-KV fold on the vector ALUs (fp32 K/V).
+// split_valu.hip -- split-KV fold on the vector ALUs (fp32 K/V; bf16 runs on
+// the matrix cores, split_mfma.hip).
 //
 // One workgroup (4 waves) = one work item (sequence b, K/V head g, chunk of
 // rows, split s).  Its keys are the span plan.h assigns to split s; every
@@ -34,22 +35,6 @@ struct Elem<float> {
         out[1] = __uint_as_float(c.y);
         out[2] = __uint_as_float(c.z);
         out[3] = __uint_as_float(c.w);
-    }
-};
-
-template <>
-struct Elem<uint16_t> {  // bf16 bit patterns
-    static constexpr int kPer16 = 8;
-    __device__ static void unpack(const uint4 &c, float *out)
-    {
-        out[0] = bf16_lo(c.x);
-        out[1] = bf16_hi(c.x);
-        out[2] = bf16_lo(c.y);
-        out[3] = bf16_hi(c.y);
-        out[4] = bf16_lo(c.z);
-        out[5] = bf16_hi(c.z);
-        out[6] = bf16_lo(c.w);
-        out[7] = bf16_hi(c.w);
     }
 };
 
@@ -301,13 +286,9 @@ hipError_t launch_rows(const SplitArgs &a, hipStream_t stream)
 
 }  // namespace
 
-hipError_t launch_split_valu(const SplitArgs &a, int dtype, hipStream_t stream)
+hipError_t launch_split_valu(const SplitArgs &a, hipStream_t stream)
 {
-    if (dtype == 0)
-        return a.head_dim == 64 ? launch_rows<float, 64>(a, stream)
-                                : launch_rows<float, 128>(a, stream);
-    return a.head_dim == 64 ? launch_rows<uint16_t, 64>(a, stream)
-                            : launch_rows<uint16_t, 128>(a, stream);
+    return a.head_dim == 64 ? launch_rows<float, 64>(a, stream) : launch_rows<float, 128>(a, stream);
 }
 
 }  // namespace atlas

@@ -98,6 +98,9 @@ DECODE_CASES = [
     ("bf16", 8, 1, 128, 16, (1, 16, 33, 500), 0),
     ("bf16", 4, 2, 64, 64, (5, 64, 129), 64),
     ("bf16", 16, 8, 128, 128, (300, 1), 0),
+    ("bf16", 32, 1, 128, 16, (777, 33), 0),                    # group of 32: two 16-row items
+    ("bf16", 3, 1, 64, 8, (100, 40), 32),                      # group of 3
+    ("bf16", 8, 8, 64, 1, (70, 2), 16),                        # MHA, one-token pages
 ]
 
 
