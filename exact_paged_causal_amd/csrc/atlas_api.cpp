@@ -83,7 +83,8 @@ struct Plan {
 };
 
 constexpr size_t kWorkspaceHeader = 256;  // validation-mode flags live here
-constexpr int kTargetItems = 2048;        // split work items to aim for (~8 per CU)
+constexpr int kDefaultSplitTokens = 4096; // keys per split-KV work item by default
+constexpr int kMinItems = 1024;           // fewest work items (4 per CU) before spans shrink
 
 int32_t check_shapes(const atlas_attn_args *a, bool decode, Plan *p)
 {
@@ -199,12 +200,12 @@ int32_t check_shapes(const atlas_attn_args *a, bool decode, Plan *p)
             return fail(ATLAS_ERR_RANGE, "split_tokens %d spans more than %d pages", a->split_tokens,
                         atlas::kMaxSplitPages - 2);
     } else {
-        T = (items_per_split * max_ctx + kTargetItems - 1) / kTargetItems;
-        T = ((T + 63) / 64) * 64;
-        if (T < 64)
-            T = 64;
-        if (T > 16384)
-            T = 16384;
+        // Long spans amortise a work item's set-up (page ids, query, final
+        // combine); shorter ones only while the grid would be too small to
+        // fill the chip.
+        T = kDefaultSplitTokens;
+        while (T > 64 && items_per_split * ((max_ctx + T - 1) / T) < kMinItems)
+            T /= 2;
         if (T > max_t_by_lds)
             T = max_t_by_lds;
     }

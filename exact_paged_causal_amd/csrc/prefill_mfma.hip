@@ -20,7 +20,8 @@
 //                skipped while the running max grows by less than 2^8
 //                (results are the same up to rounding: every term uses the
 //                same reference max); P is rounded to fp16 (11-bit
-//                mantissa) and O^T += V^T P^T runs on
+//                mantissa), the row sum is taken over those fp16 values
+//                (v_dot2_f32_f16), and O^T += V^T P^T runs on
 //                v_mfma_f32_32x32x16_f16, with V converted bf16 -> fp16 while
 //                it is staged and read transposed by ds_read_b64_tr_b16.
 //                fp32 accumulation throughout, fp32 output.
@@ -54,13 +55,17 @@ typedef __attribute__((address_space(3))) i16x4 lds_i16x4;
 constexpr int kWaves = 8;
 constexpr int kRows = 32 * kWaves;   // rows per workgroup
 constexpr int kBN = 64;              // keys per block
-constexpr int kPad = 8;              // LDS row padding (elements)
+constexpr int kPad = 16;             // LDS row padding (elements); 32-byte row skew measured best
 constexpr float kRescaleSlack = 8.0f;  // log2 units the running max may lag
+constexpr int kPidWindow = 2048;       // page ids staged in LDS at a time
 
+// 16-byte alignment lets every K/V row piece move with one ds_read_b128 /
+// ds_write_b128 (without it the compiler splits them into 4-byte pairs).
 template <int D>
-struct Smem {
-    uint16_t k[2][kBN][D + kPad];  // bf16 bits
-    uint16_t v[2][kBN][D + kPad];  // fp16 bits
+struct alignas(16) Smem {
+    alignas(16) uint16_t k[2][kBN][D + kPad];  // bf16 bits
+    alignas(16) uint16_t v[2][kBN][D + kPad];  // fp16 bits
+    alignas(16) int32_t pid[kPidWindow];       // physical ids of pages [pid_base, pid_base + kPidWindow)
 };
 
 __device__ __forceinline__ uint32_t bf16pair_to_f16pair(uint32_t x)
@@ -130,22 +135,38 @@ __global__ __launch_bounds__(512) void prefill_kernel(PrefillArgs a)
     const uint16_t *vpages = reinterpret_cast<const uint16_t *>(a.v_pages);
     const int32_t *ptab = a.page_table + (int64_t)b * a.max_pages;
 
+    // Page ids come from LDS, so a block's K/V loads never wait on a
+    // page-table load.  Staged by windows of kPidWindow pages (one window
+    // covers every page of all but extremely long, finely paged histories).
+    int pid_base = 0;
+    auto stage_pids = [&](int first_page) {
+        pid_base = first_page;
+        const int last_page = pos_hi >= 0 ? pos_hi >> ps : -1;
+        for (int t = tid; t < kPidWindow && first_page + t <= last_page; t += 512) {
+            const int pid = ptab[first_page + t];
+            sm.pid[t] = ((unsigned)pid < (unsigned)a.num_phys) ? pid : 0;
+        }
+    };
+    stage_pids(0);
+
     // Global -> registers for key block kb (zeros past the last visible key).
+    // Thread t stages CH adjacent 16-byte pieces of one row: one page lookup.
+    const int srow = (tid * CH) / CPR;
+    const int scol = (tid * CH) - srow * CPR;
     uint4 kreg[CH], vreg[CH];
     auto fetch = [&](int kb) {
+        const int j = kb * kBN + srow;
+        if (j <= pos_hi) {
+            const int pid = sm.pid[(j >> ps) - pid_base];
+            const int64_t off = ((((int64_t)pid * a.hkv + g) << ps) + (j & pmask)) * D + scol * 8;
 #pragma unroll
-        for (int u = 0; u < CH; ++u) {
-            const int c = tid + 512 * u;
-            const int row = c / CPR;
-            const int col = c - row * CPR;
-            const int j = kb * kBN + row;
-            if (j <= pos_hi) {
-                int pid = ptab[j >> ps];
-                pid = ((unsigned)pid < (unsigned)a.num_phys) ? pid : 0;
-                const int64_t off = ((((int64_t)pid * a.hkv + g) << ps) + (j & pmask)) * D + col * 8;
-                kreg[u] = *reinterpret_cast<const uint4 *>(kpages + off);
-                vreg[u] = *reinterpret_cast<const uint4 *>(vpages + off);
-            } else {
+            for (int u = 0; u < CH; ++u) {
+                kreg[u] = *reinterpret_cast<const uint4 *>(kpages + off + 8 * u);
+                vreg[u] = *reinterpret_cast<const uint4 *>(vpages + off + 8 * u);
+            }
+        } else {
+#pragma unroll
+            for (int u = 0; u < CH; ++u) {
                 kreg[u] = make_uint4(0, 0, 0, 0);
                 vreg[u] = make_uint4(0, 0, 0, 0);
             }
@@ -155,9 +176,8 @@ __global__ __launch_bounds__(512) void prefill_kernel(PrefillArgs a)
     auto stash = [&](int buf) {
 #pragma unroll
         for (int u = 0; u < CH; ++u) {
-            const int c = tid + 512 * u;
-            const int row = c / CPR;
-            const int col = c - row * CPR;
+            const int row = srow;
+            const int col = scol + u;
             *reinterpret_cast<uint4 *>(&sm.k[buf][row][col * 8]) = kreg[u];
             uint4 v16;
             v16.x = bf16pair_to_f16pair(vreg[u].x);
@@ -176,7 +196,15 @@ __global__ __launch_bounds__(512) void prefill_kernel(PrefillArgs a)
     for (int t = 0; t < DT; ++t)
         acc[t] = f32x16{};
 
+    // Complete the query loads here, once: the asm "redefines" qf, so inside
+    // the loop the compiler knows no load into qf is pending and does not wait
+    // on the (prefetch) load counter before the first QK product.
+#pragma unroll
+    for (int s = 0; s < KS; ++s)
+        asm volatile("" : "+v"(qf[s]));
+
     const int kb_last = pos_hi >= 0 ? pos_hi / kBN : -1;
+    __syncthreads();  // page ids staged
     if (kb_last >= 0) {
         fetch(0);
         stash(0);
@@ -185,10 +213,17 @@ __global__ __launch_bounds__(512) void prefill_kernel(PrefillArgs a)
 
     for (int kb = 0; kb <= kb_last; ++kb) {
         const int cur = kb & 1;
+        if (kb < kb_last && ((((kb + 1) * kBN + kBN - 1) >> ps) - pid_base) >= kPidWindow) {
+            // Uniform across the workgroup: move the page-id window forward.
+            __syncthreads();
+            stage_pids(((kb + 1) * kBN) >> ps);
+            __syncthreads();
+        }
         if (kb < kb_last)
             fetch(kb + 1);
 
         // S^T for the block: two 32-key tiles.
+        __builtin_amdgcn_s_setprio(1);
         f32x16 st[2];
 #pragma unroll
         for (int t = 0; t < 2; ++t) {
@@ -200,6 +235,8 @@ __global__ __launch_bounds__(512) void prefill_kernel(PrefillArgs a)
                 st[t] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf, qf[s], st[t], 0, 0, 0);
             }
         }
+
+        __builtin_amdgcn_s_setprio(0);
 
         // Causal mask where the block reaches past the first row.
         if (kb * kBN + kBN - 1 > pos_lo) {
@@ -233,17 +270,19 @@ __global__ __launch_bounds__(512) void prefill_kernel(PrefillArgs a)
         const float msafe = m_ref == -INFINITY ? 0.0f : m_ref;
 
         // P^T as the B operand: tile t, k-step ks -> elements 8ks..8ks+7,
-        // packed two fp16 values per 32-bit word.
+        // packed two fp16 values per 32-bit word.  The row sum is taken over
+        // the same fp16 values the P.V product uses (one dot2 per pair).
         u32x4 pw[2][2];
+        const f16x2 ones = {(_Float16)1.0f, (_Float16)1.0f};
 #pragma unroll
         for (int t = 0; t < 2; ++t) {
 #pragma unroll
             for (int e = 0; e < 16; e += 2) {
                 const float p0 = fast_exp2(fmaf(st[t][e], c_log2, -msafe));
                 const float p1 = fast_exp2(fmaf(st[t][e + 1], c_log2, -msafe));
-                l_part += p0 + p1;
-                pw[t][e >> 3][(e & 7) >> 1] =
-                    __builtin_bit_cast(uint32_t, __builtin_convertvector(f32x2{p0, p1}, f16x2));
+                const f16x2 ph = __builtin_convertvector(f32x2{p0, p1}, f16x2);
+                l_part = __builtin_amdgcn_fdot2(ph, ones, l_part, false);
+                pw[t][e >> 3][(e & 7) >> 1] = __builtin_bit_cast(uint32_t, ph);
             }
         }
 
@@ -251,6 +290,7 @@ __global__ __launch_bounds__(512) void prefill_kernel(PrefillArgs a)
         // V[key0 + j/4][d0 + 4(j%4) .. +3] and receives V[key0 + k][d0 + j] (k=0..3).
         const int q16 = lane >> 4;
         const int j16 = lane & 15;
+        __builtin_amdgcn_s_setprio(1);
 #pragma unroll
         for (int dt = 0; dt < DT; ++dt) {
 #pragma unroll
@@ -272,6 +312,8 @@ __global__ __launch_bounds__(512) void prefill_kernel(PrefillArgs a)
                 }
             }
         }
+
+        __builtin_amdgcn_s_setprio(0);
 
         if (kb < kb_last)
             stash(cur ^ 1);

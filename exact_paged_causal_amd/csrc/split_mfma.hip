@@ -44,9 +44,9 @@ constexpr int kRowsMax = 16;          // rows per work item (MFMA N)
 constexpr float kRescaleSlack = 8.0f;
 
 template <int D>
-struct SplitSmem {
-    static constexpr int RS = D + 8;  // padded LDS row (elements)
-    union {
+struct alignas(16) SplitSmem {
+    static constexpr int RS = D + 16; // padded LDS row (elements): 32-byte skew between rows
+    union alignas(16) {
         uint16_t v[4][kChunk][RS];    // per-wave V tile (bf16 bits)
         float acc[4][kRowsMax][D];    // end-of-span wave states
     } u;
@@ -135,23 +135,27 @@ __global__ __launch_bounds__(256) void split_mfma_kernel(SplitArgs a)
         return base + ((((int64_t)pid * a.hkv) << ps) + head_rows + (jj & pmask)) * D;
     };
 
-    // K operand registers (2 tiles x KS steps) and V staging registers.
-    bf16x8 kreg[2][KS];
-    uint4 vreg[VCH];
-    auto load_chunk = [&](int cb) {
+    // Two register buffers for K (operand layout) and V (staging), used in
+    // ping-pong so the next chunk's loads are in flight while the current one
+    // is computed (a loop-carried copy would make the compiler wait for them).
+    struct Regs {
+        bf16x8 k[2][KS];
+        uint4 v[VCH];
+    };
+    auto load_chunk = [&](Regs &r, int cb) {
 #pragma unroll
         for (int t = 0; t < 2; ++t) {
             const uint16_t *kr = row_ptr(kpages, cb + 16 * t + l16);
 #pragma unroll
             for (int s = 0; s < KS; ++s)
-                kreg[t][s] = *reinterpret_cast<const bf16x8 *>(kr + 32 * s + 8 * g4);
+                r.k[t][s] = *reinterpret_cast<const bf16x8 *>(kr + 32 * s + 8 * g4);
         }
 #pragma unroll
         for (int u = 0; u < VCH; ++u) {
             const int c = lane + 64 * u;
             const int key = c / CPR;
             const int col = c - key * CPR;
-            vreg[u] = *reinterpret_cast<const uint4 *>(row_ptr(vpages, cb + key) + col * 8);
+            r.v[u] = *reinterpret_cast<const uint4 *>(row_ptr(vpages, cb + key) + col * 8);
         }
     };
 
@@ -163,26 +167,15 @@ __global__ __launch_bounds__(256) void split_mfma_kernel(SplitArgs a)
     for (int t = 0; t < DT; ++t)
         acc[t] = f32x4{};
 
-    int cb = ka + kChunk * wave;
-    if (cb < kb)
-        load_chunk(cb);
-    for (; cb < kb; cb += 4 * kChunk) {
-        // Stage this chunk's V, then prefetch the next chunk.
+    auto fold_chunk = [&](const Regs &r, int cb) {
+        // Stage this chunk's V in the wave's LDS tile.
 #pragma unroll
         for (int u = 0; u < VCH; ++u) {
             const int c = lane + 64 * u;
             const int key = c / CPR;
             const int col = c - key * CPR;
-            *reinterpret_cast<uint4 *>(&sm.u.v[wave][key][col * 8]) = vreg[u];
+            *reinterpret_cast<uint4 *>(&sm.u.v[wave][key][col * 8]) = r.v[u];
         }
-        bf16x8 kcur[2][KS];
-#pragma unroll
-        for (int t = 0; t < 2; ++t)
-#pragma unroll
-            for (int s = 0; s < KS; ++s)
-                kcur[t][s] = kreg[t][s];
-        if (cb + 4 * kChunk < kb)
-            load_chunk(cb + 4 * kChunk);
 
         // S^T tiles: lane holds row l16, keys 16t + 4*g4 + j.
         f32x4 st[2];
@@ -191,7 +184,7 @@ __global__ __launch_bounds__(256) void split_mfma_kernel(SplitArgs a)
             st[t] = f32x4{};
 #pragma unroll
             for (int s = 0; s < KS; ++s)
-                st[t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kcur[t][s], qf[s], st[t], 0, 0, 0);
+                st[t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(r.k[t][s], qf[s], st[t], 0, 0, 0);
         }
 
         // Scale, softcap, mask (log2 units).
@@ -201,11 +194,11 @@ __global__ __launch_bounds__(256) void split_mfma_kernel(SplitArgs a)
 #pragma unroll
             for (int j = 0; j < 4; ++j) {
                 const int key = cb + 16 * t + 4 * g4 + j;
-                float s = st[t][j] * qk_scale;
+                float sc = st[t][j] * qk_scale;
                 if (cap > 0.0f)
-                    s = cap * tanhf(s / cap);
+                    sc = cap * tanhf(sc / cap);
                 const bool vis = key < kb && key <= pos && (W <= 0 || key > pos - W || key < S);
-                x[4 * t + j] = vis ? s * kLog2e : -INFINITY;
+                x[4 * t + j] = vis ? sc * kLog2e : -INFINITY;
             }
         float mx = x[0];
 #pragma unroll
@@ -258,6 +251,25 @@ __global__ __launch_bounds__(256) void split_mfma_kernel(SplitArgs a)
         __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
         __builtin_amdgcn_wave_barrier();
         __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+    };
+
+    // The prefetch is unconditional: past the span every address is clamped
+    // to the span's last row (cache hits, no extra HBM traffic), and a
+    // conditional load would make the compiler wait for all loads at the join.
+    constexpr int kStride = 4 * kChunk;  // the 4 waves interleave chunks
+    Regs ra, rb;
+    int cb = ka + kChunk * wave;
+    if (cb < kb)
+        load_chunk(ra, cb);
+    while (cb < kb) {
+        load_chunk(rb, cb + kStride);
+        fold_chunk(ra, cb);
+        cb += kStride;
+        if (cb >= kb)
+            break;
+        load_chunk(ra, cb + kStride);
+        fold_chunk(rb, cb);
+        cb += kStride;
     }
 
     // Per-row sum of the four lane groups.
