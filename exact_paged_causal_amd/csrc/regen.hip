@@ -92,15 +92,19 @@ __global__ __launch_bounds__(256) void regen_kernel(RegenArgs a, int64_t items_p
         float z0, z1, z2, z3;
         box_muller(w.w0, w.w1, z0, z1);
         box_muller(w.w2, w.w3, z2, z3);
+        // Non-temporal stores: the pages go straight to HBM while this
+        // ALU-bound kernel runs, instead of sitting dirty in the last-level
+        // cache and being written back while the attention pass reads.
         void *arena = tensor == 1 ? a.k_pages : a.v_pages;
         if constexpr (BF16) {
-            uint2 packed;
-            packed.x = f32_to_bf16_bits(z0) | (f32_to_bf16_bits(z1) << 16);
-            packed.y = f32_to_bf16_bits(z2) | (f32_to_bf16_bits(z3) << 16);
-            *reinterpret_cast<uint2 *>(reinterpret_cast<uint16_t *>(arena) + elem) = packed;
+            typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+            const u32x2 packed = {f32_to_bf16_bits(z0) | (f32_to_bf16_bits(z1) << 16),
+                                  f32_to_bf16_bits(z2) | (f32_to_bf16_bits(z3) << 16)};
+            __builtin_nontemporal_store(packed, reinterpret_cast<u32x2 *>(reinterpret_cast<uint16_t *>(arena) + elem));
         } else {
-            *reinterpret_cast<float4 *>(reinterpret_cast<float *>(arena) + elem) =
-                make_float4(z0, z1, z2, z3);
+            typedef float f32x4 __attribute__((ext_vector_type(4)));
+            const f32x4 z = {z0, z1, z2, z3};
+            __builtin_nontemporal_store(z, reinterpret_cast<f32x4 *>(reinterpret_cast<float *>(arena) + elem));
         }
     }
 }

@@ -133,26 +133,43 @@ __global__ __launch_bounds__(256) void split_valu_kernel(SplitArgs a)
     const E *vbase = reinterpret_cast<const E *>(a.v_pages);
     const int64_t head_off = (int64_t)g << ps;  // rows before head g inside a page
 
-    for (int base = ka; base < kb; base += KPI) {
-        float kv[KU][DPL], vv[KU][DPL];
-        int key[KU];
+    // Two register buffers in ping-pong: the next keys' loads are in flight
+    // while the current ones are folded.  The prefetch is unconditional: past
+    // the span the key index is clamped to the span's last row (cache hits,
+    // no extra HBM traffic); a conditional load would make the compiler wait
+    // for all loads where the branches join.
+    struct Buf {
+        uint4 k[KU][NL];
+        uint4 v[KU][NL];
+    };
+    auto load = [&](Buf &bf, int base) {
 #pragma unroll
         for (int u = 0; u < KU; ++u) {
-            key[u] = base + u * (4 * GPW) + wave * GPW + grp;
-            const int jj = key[u] < kb ? key[u] : kb - 1;
+            const int key = base + u * (4 * GPW) + wave * GPW + grp;
+            const int jj = key < kb ? key : kb - 1;
             const int pid = s_pid[(jj >> ps) - p0];
             const int64_t row = ((int64_t)pid * a.hkv << ps) + head_off + (jj & pmask);
             const E *kr = kbase + row * D;
             const E *vr = vbase + row * D;
 #pragma unroll
             for (int n = 0; n < NL; ++n) {
-                uint4 ck = *reinterpret_cast<const uint4 *>(kr + n * R * EPC + li * EPC);
-                uint4 cv = *reinterpret_cast<const uint4 *>(vr + n * R * EPC + li * EPC);
-                Elem<E>::unpack(ck, &kv[u][n * EPC]);
-                Elem<E>::unpack(cv, &vv[u][n * EPC]);
+                bf.k[u][n] = *reinterpret_cast<const uint4 *>(kr + n * R * EPC + li * EPC);
+                bf.v[u][n] = *reinterpret_cast<const uint4 *>(vr + n * R * EPC + li * EPC);
             }
         }
-
+    };
+    auto fold = [&](const Buf &bf, int base) {
+        float kv[KU][DPL], vv[KU][DPL];
+        int key[KU];
+#pragma unroll
+        for (int u = 0; u < KU; ++u) {
+            key[u] = base + u * (4 * GPW) + wave * GPW + grp;
+#pragma unroll
+            for (int n = 0; n < NL; ++n) {
+                Elem<E>::unpack(bf.k[u][n], &kv[u][n * EPC]);
+                Elem<E>::unpack(bf.v[u][n], &vv[u][n * EPC]);
+            }
+        }
 #pragma unroll
         for (int r = 0; r < MC; ++r) {
             float s2[KU];
@@ -194,6 +211,20 @@ __global__ __launch_bounds__(256) void split_valu_kernel(SplitArgs a)
             }
             m[r] = mnew;
         }
+    };
+
+    Buf ba, bb;
+    int base = ka;
+    load(ba, base);
+    while (base < kb) {
+        load(bb, base + KPI);
+        fold(ba, base);
+        base += KPI;
+        if (base >= kb)
+            break;
+        load(ba, base + KPI);
+        fold(bb, base);
+        base += KPI;
     }
 
     // Combine the row groups of each wave (butterfly over lane offsets R..32).
@@ -266,7 +297,10 @@ __global__ __launch_bounds__(256) void split_valu_kernel(SplitArgs a)
 template <typename E, int D, int MC>
 hipError_t launch_one(const SplitArgs &a, hipStream_t stream)
 {
-    constexpr int KU = (MC <= 2) ? 8 : 4;
+    // Keys per row group per step, sized so that two register buffers, the
+    // query slices and the accumulators fit without spilling.
+    constexpr int DPL = D / 16;
+    constexpr int KU = (D == 64) ? ((MC <= 2) ? 8 : (MC * DPL <= 16 ? 4 : 2)) : ((MC <= 2) ? 4 : 2);
     dim3 grid(a.max_splits, a.hkv * a.n_chunks, a.batch);
     hipLaunchKernelGGL((split_valu_kernel<E, D, MC, KU>), grid, dim3(256), 0, stream, a);
     return hipGetLastError();
