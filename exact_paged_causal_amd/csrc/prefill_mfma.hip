@@ -55,7 +55,7 @@ typedef __attribute__((address_space(3))) i16x4 lds_i16x4;
 constexpr int kWaves = 8;
 constexpr int kRows = 32 * kWaves;   // rows per workgroup
 constexpr int kBN = 64;              // keys per block
-constexpr int kPad = 16;             // LDS row padding (elements); 32-byte row skew measured best
+constexpr int kPad = 24;             // LDS row padding (elements): conflict-free K rows, best transposed V reads
 constexpr float kRescaleSlack = 8.0f;  // log2 units the running max may lag
 constexpr int kPidWindow = 2048;       // page ids staged in LDS at a time
 
@@ -224,17 +224,26 @@ __global__ __launch_bounds__(512) void prefill_kernel(PrefillArgs a)
 
         // S^T for the block: two 32-key tiles.
         __builtin_amdgcn_s_setprio(1);
-        f32x16 st[2];
+        // The two tiles' accumulation chains alternate: back-to-back
+        // products into one accumulator would wait on each other.
+        f32x16 st[2] = {f32x16{}, f32x16{}};
 #pragma unroll
-        for (int t = 0; t < 2; ++t) {
-            st[t] = f32x16{};
+        for (int s = 0; s < KS; ++s) {
 #pragma unroll
-            for (int s = 0; s < KS; ++s) {
+            for (int t = 0; t < 2; ++t) {
                 const bf16x8 kf =
                     *reinterpret_cast<const bf16x8 *>(&sm.k[cur][32 * t + (lane & 31)][16 * s + 8 * half]);
                 st[t] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf, qf[s], st[t], 0, 0, 0);
             }
         }
+        // Keep the K operand reads a few products ahead of their use.
+        __builtin_amdgcn_sched_group_barrier(0x100, 4, 0);
+#pragma unroll
+        for (int i = 0; i < 2 * KS - 4; ++i) {
+            __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+            __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+        }
+        __builtin_amdgcn_sched_group_barrier(0x008, 4, 0);
 
         __builtin_amdgcn_s_setprio(0);
 
@@ -291,12 +300,14 @@ __global__ __launch_bounds__(512) void prefill_kernel(PrefillArgs a)
         const int q16 = lane >> 4;
         const int j16 = lane & 15;
         __builtin_amdgcn_s_setprio(1);
+        // Output tiles innermost: consecutive products go to different
+        // accumulators.
 #pragma unroll
-        for (int dt = 0; dt < DT; ++dt) {
+        for (int t = 0; t < 2; ++t) {
 #pragma unroll
-            for (int t = 0; t < 2; ++t) {
+            for (int ks = 0; ks < 2; ++ks) {
 #pragma unroll
-                for (int ks = 0; ks < 2; ++ks) {
+                for (int dt = 0; dt < DT; ++dt) {
                     const int key0 = 32 * t + 16 * ks + 4 * half + (j16 >> 2);
                     const int dim0 = 32 * dt + 16 * (q16 & 1) + 4 * (j16 & 3);
                     const i16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
@@ -312,6 +323,14 @@ __global__ __launch_bounds__(512) void prefill_kernel(PrefillArgs a)
                 }
             }
         }
+        // Transposed V reads run six ahead, then two per product.
+        __builtin_amdgcn_sched_group_barrier(0x100, 6, 0);
+#pragma unroll
+        for (int i = 0; i < (8 * DT - 6) / 2; ++i) {
+            __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+            __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
+        }
+        __builtin_amdgcn_sched_group_barrier(0x008, 4 * DT - (8 * DT - 6) / 2, 0);
 
         __builtin_amdgcn_s_setprio(0);
 
