@@ -84,7 +84,7 @@ struct Plan {
 
 constexpr size_t kWorkspaceHeader = 256;  // validation-mode flags live here
 constexpr int kDefaultSplitTokens = 4096; // keys per split-KV work item by default
-constexpr int kMinItems = 1024;           // fewest work items (4 per CU) before spans shrink
+constexpr int kMinItems = 2048;           // fewest work items (8 per CU) before spans shrink
 
 int32_t check_shapes(const atlas_attn_args *a, bool decode, Plan *p)
 {
