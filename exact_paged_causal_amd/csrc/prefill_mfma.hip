@@ -46,6 +46,7 @@ typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
 typedef _Float16 f16x2 __attribute__((ext_vector_type(2)));
 typedef float f32x2 __attribute__((ext_vector_type(2)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
 typedef short i16x4 __attribute__((ext_vector_type(4)));
 typedef short i16x8 __attribute__((ext_vector_type(8)));
@@ -350,15 +351,15 @@ __global__ __launch_bounds__(512) void prefill_kernel(PrefillArgs a)
     for (int dt = 0; dt < DT; ++dt)
 #pragma unroll
         for (int e4 = 0; e4 < 4; ++e4) {
-            float4 o;
-            o.x = acc[dt][4 * e4 + 0] * inv;
-            o.y = acc[dt][4 * e4 + 1] * inv;
-            o.z = acc[dt][4 * e4 + 2] * inv;
-            o.w = acc[dt][4 * e4 + 3] * inv;
-            *reinterpret_cast<float4 *>(orow + 32 * dt + 8 * e4 + 4 * half) = o;
+            // Non-temporal: the output goes to HBM while this compute-bound
+            // kernel runs instead of lingering dirty in the last-level cache.
+            const f32x4 o = {acc[dt][4 * e4 + 0] * inv, acc[dt][4 * e4 + 1] * inv,
+                             acc[dt][4 * e4 + 2] * inv, acc[dt][4 * e4 + 3] * inv};
+            __builtin_nontemporal_store(o, reinterpret_cast<f32x4 *>(orow + 32 * dt + 8 * e4 + 4 * half));
         }
     if (a.lse && half == 0)
-        a.lse[((int64_t)b * a.q_len + qi) * a.hq + h] = any ? (m_ref + log2f(l_row)) * kLn2 : -INFINITY;
+        __builtin_nontemporal_store(any ? (m_ref + log2f(l_row)) * kLn2 : -INFINITY,
+                                    a.lse + ((int64_t)b * a.q_len + qi) * a.hq + h);
 }
 
 }  // namespace
