@@ -11,7 +11,10 @@ Inputs are resident in HBM before timing starts.  `value` is the decode
 attention pass's K/V-read throughput (algorithmic bytes / time of the
 attention call, split + merge); the prefill throughput and the regenerator
 are reported beside it.  Per-kernel times come from HIP events recorded on
-the stream the kernels run on.
+the stream the kernels run on.  After the timed steps, the three smaller
+synthetic workloads (single-head decode, GQA short-query suffix attention,
+mixed-length decode with window / sinks / softcap) are timed per call and
+reported under "workloads" with the two step workloads.
 
 Prints one JSON line.  `--gpus N` with N > 1 exits: this path runs on one GPU.
 """
@@ -49,6 +52,8 @@ def parse():
     ap.add_argument("--split-tokens", type=int, default=0)
     ap.add_argument("--no-prefill", action="store_true")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-workloads", action="store_true",
+                    help="skip the per-call timing of the three smaller workloads")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="also run a plain device copy of known size (HBM counter calibration)")
     return ap.parse_args()
@@ -121,6 +126,101 @@ def prefill_setup(torch, workloads, np):
     pt = torch.from_numpy(lay.page_table).cuda()
     ctx = torch.from_numpy(w.context_lens).cuda()
     return dict(w=w, lay=lay, k=k, v=v, q=q, pt=pt, ctx=ctx, kl=kl, vl=vl)
+
+
+def _median_call_us(torch, np, fn, calls=30, warm=5):
+    for _ in range(warm):
+        fn()
+    torch.cuda.synchronize()
+    t = Timer(torch)
+    for _ in range(calls):
+        t(fn)
+    torch.cuda.synchronize()
+    return float(np.median(t.ms())) * 1000.0
+
+
+def _arena(torch, workloads, np, w, lay):
+    """Device K/V arenas of a non-regenerated workload: seeded logical pages
+    scattered to their physical ids."""
+    kl, vl, n_pages = workloads.logical_kv(w, "cuda")
+    shape = workloads.arena_shape(w, lay.num_phys)
+    k = torch.zeros(shape, dtype=kl.dtype, device="cuda")
+    v = torch.zeros_like(k)
+    ids = torch.from_numpy(np.concatenate([lay.page_table[b, :n_pages[b]]
+                                           for b in range(w.batch)]).astype(np.int64)).cuda()
+    k.index_copy_(0, ids, kl)
+    v.index_copy_(0, ids, vl)
+    return k, v
+
+
+def workload_report(torch, np, workloads, atlas):
+    """The three smaller synthetic workloads, each timed per call (median of
+    30 after 5 warm-up calls): single-head decode (all pages resident, and
+    all 8 pages regenerated inside the call), the GQA short-query suffix
+    attention, and the mixed-length decode with window / sinks / softcap on
+    even sequences."""
+    rep = {}
+    # Single-head decode: 2 MiB of K/V, launch-latency bound.
+    w = workloads.make("single_head_decode")
+    for mode, hf in (("resident", 1.0), ("cold", 0.0)):
+        lay = workloads.page_layout(w, hot_fraction=hf)
+        shape = workloads.arena_shape(w, lay.num_phys)
+        k = torch.zeros(shape, dtype=torch.float32, device="cuda")
+        v = torch.zeros_like(k)
+        if len(lay.hot_jobs):
+            atlas.atlas_regenerate_pages(k, v, torch.from_numpy(lay.hot_jobs).cuda(), seed=w.seed, layer=w.layer)
+        cold = torch.from_numpy(lay.cold_jobs).cuda() if len(lay.cold_jobs) else None
+        q = workloads.randn(workloads.query_shape(w), seed=w.seed * 100 + 1, device="cuda")
+        pt = torch.from_numpy(lay.page_table).cuda()
+        ctx = torch.from_numpy(w.context_lens).cuda()
+
+        def call():
+            if cold is not None:
+                atlas.atlas_regenerate_pages(k, v, cold, seed=w.seed, layer=w.layer)
+            atlas.atlas_attend_decode(q, k, v, pt, ctx, w.scale)
+        rep.setdefault("single_head_decode", {})[f"{mode}_us"] = round(_median_call_us(torch, np, call), 2)
+    kvb = int(w.context_lens.sum()) * w.hkv * w.head_dim * 4 * 2
+    us = rep["single_head_decode"]["resident_us"]
+    rep["single_head_decode"].update({"kv_bytes": kvb, "GBs": round(kvb / us / 1e3, 1),
+                                      "frac_hbm": round(kvb / us / 1e3 / HBM_PEAK_GBS, 4),
+                                      "note": "launch-latency bound (2 MiB of K/V); cold_us regenerates all 8 pages in the call"})
+    # GQA short-query suffix attention (16 queries at positions 240..255).
+    w = workloads.make("gqa_short_query")
+    lay = workloads.page_layout(w)
+    k, v = _arena(torch, workloads, np, w, lay)
+    q = workloads.randn(workloads.query_shape(w), seed=w.seed * 100 + 1, device="cuda")
+    pt = torch.from_numpy(lay.page_table).cuda()
+    ctx = torch.from_numpy(w.context_lens).cuda()
+    us = _median_call_us(torch, np, lambda: atlas.atlas_attend_prefill(q, k, v, pt, ctx, w.scale))
+    L = int(w.context_lens[0])
+    pairs = w.hq * sum(L - w.q_len + i + 1 for i in range(w.q_len))
+    rep["gqa_short_query"] = {"us": round(us, 2), "kv_bytes": L * w.hkv * w.head_dim * 4 * 2,
+                              "flop": 4 * w.head_dim * pairs,
+                              "note": "latency bound (256 KiB of K/V)"}
+    del k, v
+    # Mixed-length decode with window / sinks / softcap on even sequences.
+    w = workloads.make("mixed_decode")
+    lay = workloads.page_layout(w)
+    k, v = _arena(torch, workloads, np, w, lay)
+    q = workloads.randn(workloads.query_shape(w), seed=w.seed * 100 + 1, dtype=w.dtype, device="cuda")
+    pt = torch.from_numpy(lay.page_table).cuda()
+    ctx = torch.from_numpy(w.context_lens).cuda()
+    opt = lambda a, t: torch.from_numpy(a.astype(t)).cuda()
+    win, snk, cap = opt(w.window, np.int32), opt(w.sinks, np.int32), opt(w.softcap, np.float32)
+    out = torch.empty(workloads.query_shape(w), dtype=torch.float32, device="cuda")
+    us = _median_call_us(torch, np, lambda: atlas.atlas_attend_decode(
+        q, k, v, pt, ctx, w.scale, window=win, sink_tokens=snk, softcap=cap, out=out))
+    Ls = w.context_lens.astype(np.int64)
+    Ws = w.window.astype(np.int64)
+    Ss = w.sinks.astype(np.int64)
+    vis = np.where(Ws > 0, np.minimum(Ws, Ls) + np.minimum(Ss, np.maximum(Ls - Ws, 0)), Ls)
+    kvb = int(vis.sum()) * w.hkv * w.head_dim * 2 * 2
+    rep["mixed_decode"] = {"us": round(us, 1), "kv_bytes": kvb, "GBs": round(kvb / us / 1e3, 1),
+                           "frac_hbm": round(kvb / us / 1e3 / HBM_PEAK_GBS, 4),
+                           "note": "visible-key bytes (window + sinks on even sequences)"}
+    del k, v
+    torch.cuda.empty_cache()
+    return rep
 
 
 def cpu_baseline(d, out, np, oracle, min_seconds=3.0):
@@ -289,6 +389,19 @@ def main():
                          "traffic": measured_traffic("prefill_tiled_causal_8192"),
                          "traffic_unit": "HBM bytes per call (rocprofv3 FETCH_SIZE + WRITE_SIZE, copy-calibrated)"},
         }
+    if not args.no_workloads:
+        # Every synthetic workload's throughput (the long-context decode and
+        # the prefill are the step's own figures above).
+        wl = workload_report(torch, np, workloads, atlas)
+        wl["long_context_decode"] = {"us": round(dec_ms * 1000.0, 1), "kv_bytes": kv_bytes,
+                                     "GBs": round(dec_gbs, 1), "frac_hbm": round(dec_gbs / HBM_PEAK_GBS, 4),
+                                     "regen_us": round(regen_ms * 1000.0, 1)}
+        if p is not None:
+            wl["causal_prefill"] = {"us": round(pre_ms * 1000.0, 1), "flop": flops, "TFLOPs": round(tf, 1),
+                                    "frac_mfma": round(tf / BF16_PEAK_TFLOPS, 4)}
+        result["workloads"] = {k: wl[k] for k in ("single_head_decode", "gqa_short_query", "long_context_decode",
+                                                  "causal_prefill", "mixed_decode") if k in wl}
+        print("bench: workloads timed", file=sys.stderr, flush=True)
     if args.copy_calibration:
         src = torch.empty(1 << 28, dtype=torch.uint8, device="cuda")   # 256 MiB
         dst = torch.empty_like(src)

@@ -55,13 +55,8 @@ class DeviceInputs:
 
 
 def logical_kv(w, device, seed_offset=0):
-    """Seeded K/V in logical page order: [total_pages][Hkv][P][D] (pages of
-    sequence 0 first), independent of any physical placement."""
-    n_pages = [int(math.ceil(int(L) / w.page_size)) for L in w.context_lens]
-    shape = (sum(n_pages), w.hkv, w.page_size, w.head_dim)
-    k = workloads.randn(shape, seed=w.seed * 100 + 2 + seed_offset, dtype=w.dtype, device=device)
-    v = workloads.randn(shape, seed=w.seed * 100 + 3 + seed_offset, dtype=w.dtype, device=device)
-    return k, v, n_pages
+    """Seeded K/V in logical page order (see workloads.logical_kv)."""
+    return workloads.logical_kv(w, device, seed_offset)
 
 
 def build(w, device="cuda", hot_fraction=None, layout_seed=0, extra_phys=0, poison=False,

@@ -184,6 +184,17 @@ def randn(shape, seed: int, dtype: str = "f32", device: str = "cpu"):
     return t
 
 
+def logical_kv(w: Workload, device: str = "cpu", seed_offset: int = 0):
+    """Seeded K/V in logical page order: [total_pages][Hkv][P][D] (pages of
+    sequence 0 first), independent of any physical placement.  Used by the
+    workloads whose K/V are not regenerated."""
+    n_pages = [int(math.ceil(int(L) / w.page_size)) for L in w.context_lens]
+    shape = (sum(n_pages), w.hkv, w.page_size, w.head_dim)
+    k = randn(shape, seed=w.seed * 100 + 2 + seed_offset, dtype=w.dtype, device=device)
+    v = randn(shape, seed=w.seed * 100 + 3 + seed_offset, dtype=w.dtype, device=device)
+    return k, v, n_pages
+
+
 def query_shape(w: Workload):
     return (w.batch, w.q_len, w.hq, w.head_dim)
 
