@@ -54,6 +54,8 @@ def parse():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-workloads", action="store_true",
                     help="skip the per-call timing of the three smaller workloads")
+    ap.add_argument("--workloads-only", action="store_true",
+                    help="diagnostic: time only the three smaller workloads (for a kernel trace of them)")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="also run a plain device copy of known size (HBM counter calibration)")
     return ap.parse_args()
@@ -177,13 +179,16 @@ def workload_report(torch, np, workloads, atlas):
         def call():
             if cold is not None:
                 atlas.atlas_regenerate_pages(k, v, cold, seed=w.seed, layer=w.layer)
-            atlas.atlas_attend_decode(q, k, v, pt, ctx, w.scale)
-        rep.setdefault("single_head_decode", {})[f"{mode}_us"] = round(_median_call_us(torch, np, call), 2)
+            return atlas.atlas_attend_decode(q, k, v, pt, ctx, w.scale)[0]
+        r = rep.setdefault("single_head_decode", {})
+        r[f"{mode}_us"] = round(_median_call_us(torch, np, call), 2)
     kvb = int(w.context_lens.sum()) * w.hkv * w.head_dim * 4 * 2
     us = rep["single_head_decode"]["resident_us"]
     rep["single_head_decode"].update({"kv_bytes": kvb, "GBs": round(kvb / us / 1e3, 1),
                                       "frac_hbm": round(kvb / us / 1e3 / HBM_PEAK_GBS, 4),
-                                      "note": "launch-latency bound (2 MiB of K/V); cold_us regenerates all 8 pages in the call"})
+                                      "note": "launch-latency bound (2 MiB of K/V); times are per Python "
+                                              "call, host overhead included; cold regenerates all 8 pages "
+                                              "in the call"})
     # GQA short-query suffix attention (16 queries at positions 240..255).
     w = workloads.make("gqa_short_query")
     lay = workloads.page_layout(w)
@@ -191,12 +196,13 @@ def workload_report(torch, np, workloads, atlas):
     q = workloads.randn(workloads.query_shape(w), seed=w.seed * 100 + 1, device="cuda")
     pt = torch.from_numpy(lay.page_table).cuda()
     ctx = torch.from_numpy(w.context_lens).cuda()
-    us = _median_call_us(torch, np, lambda: atlas.atlas_attend_prefill(q, k, v, pt, ctx, w.scale))
+    call = lambda: atlas.atlas_attend_prefill(q, k, v, pt, ctx, w.scale)[0]
+    us = _median_call_us(torch, np, call)
     L = int(w.context_lens[0])
     pairs = w.hq * sum(L - w.q_len + i + 1 for i in range(w.q_len))
     rep["gqa_short_query"] = {"us": round(us, 2), "kv_bytes": L * w.hkv * w.head_dim * 4 * 2,
                               "flop": 4 * w.head_dim * pairs,
-                              "note": "latency bound (256 KiB of K/V)"}
+                              "note": "latency bound (256 KiB of K/V); per Python call, host overhead included"}
     del k, v
     # Mixed-length decode with window / sinks / softcap on even sequences.
     w = workloads.make("mixed_decode")
@@ -275,6 +281,9 @@ def main():
     import workloads
 
     torch.cuda.set_device(0)
+    if args.workloads_only:
+        print(json.dumps({"workloads": workload_report(torch, np, workloads, atlas), "n_gpus": 1}))
+        return
     d = decode_setup(torch, workloads, atlas)
     w = d["w"]
     dec_out = torch.empty(workloads.query_shape(w), dtype=torch.float32, device="cuda")
