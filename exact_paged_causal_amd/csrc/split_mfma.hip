@@ -22,8 +22,9 @@
 //                   V is staged in the wave's own LDS tile and read transposed
 //                   with ds_read_b64_tr_b16 (4 consecutive keys of one dim per
 //                   read).
-// The next chunk's K and V are loaded into registers before the current one
-// is computed.  At the end the 4 waves' states are combined in LDS and one
+// The next chunk's K and V are loaded into registers as soon as the current
+// chunk's have been consumed, so they are in flight during its softmax and
+// P.V products.  At the end the 4 waves' states are combined in LDS and one
 // (m, l, acc) partial per row is written; merge.hip finishes.
 #include "device.h"
 #include "kernels.h"
@@ -135,9 +136,7 @@ __global__ __launch_bounds__(256) void split_mfma_kernel(SplitArgs a)
         return base + ((((int64_t)pid * a.hkv) << ps) + head_rows + (jj & pmask)) * D;
     };
 
-    // Two register buffers for K (operand layout) and V (staging), used in
-    // ping-pong so the next chunk's loads are in flight while the current one
-    // is computed (a loop-carried copy would make the compiler wait for them).
+    // Register buffer for one chunk's K (operand layout) and V (staging).
     struct Regs {
         bf16x8 k[2][KS];
         uint4 v[VCH];
@@ -167,7 +166,10 @@ __global__ __launch_bounds__(256) void split_mfma_kernel(SplitArgs a)
     for (int t = 0; t < DT; ++t)
         acc[t] = f32x4{};
 
-    auto fold_chunk = [&](const Regs &r, int cb) {
+    // One chunk: V into the wave's LDS tile and S^T from the registers, then
+    // (once both are consumed) the next chunk's loads into the same
+    // registers, then softmax and O^T += V^T P^T from LDS.
+    auto fold_chunk = [&](Regs &r, int cb, int cb_next) {
         // Stage this chunk's V in the wave's LDS tile.
 #pragma unroll
         for (int u = 0; u < VCH; ++u) {
@@ -177,15 +179,15 @@ __global__ __launch_bounds__(256) void split_mfma_kernel(SplitArgs a)
             *reinterpret_cast<uint4 *>(&sm.u.v[wave][key][col * 8]) = r.v[u];
         }
 
-        // S^T tiles: lane holds row l16, keys 16t + 4*g4 + j.
-        f32x4 st[2];
+        // S^T tiles: lane holds row l16, keys 16t + 4*g4 + j.  The two tiles'
+        // chains alternate.
+        f32x4 st[2] = {f32x4{}, f32x4{}};
 #pragma unroll
-        for (int t = 0; t < 2; ++t) {
-            st[t] = f32x4{};
+        for (int s = 0; s < KS; ++s)
 #pragma unroll
-            for (int s = 0; s < KS; ++s)
+            for (int t = 0; t < 2; ++t)
                 st[t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(r.k[t][s], qf[s], st[t], 0, 0, 0);
-        }
+        load_chunk(r, cb_next);
 
         // Scale, softcap, mask (log2 units).
         float x[8];
@@ -256,21 +258,16 @@ __global__ __launch_bounds__(256) void split_mfma_kernel(SplitArgs a)
     // The prefetch is unconditional: past the span every address is clamped
     // to the span's last row (cache hits, no extra HBM traffic), and a
     // conditional load would make the compiler wait for all loads at the join.
+    // One register buffer: its next contents are loaded as soon as the
+    // current ones are consumed, so the loads are in flight during the
+    // softmax and the P.V products (and two waves fit per SIMD).
     constexpr int kStride = 4 * kChunk;  // the 4 waves interleave chunks
-    Regs ra, rb;
+    Regs rg;
     int cb = ka + kChunk * wave;
     if (cb < kb)
-        load_chunk(ra, cb);
-    while (cb < kb) {
-        load_chunk(rb, cb + kStride);
-        fold_chunk(ra, cb);
-        cb += kStride;
-        if (cb >= kb)
-            break;
-        load_chunk(ra, cb + kStride);
-        fold_chunk(rb, cb);
-        cb += kStride;
-    }
+        load_chunk(rg, cb);
+    for (; cb < kb; cb += kStride)
+        fold_chunk(rg, cb, cb + kStride);
 
     // Per-row sum of the four lane groups.
     l_part += __shfl_xor(l_part, 16);
