@@ -29,6 +29,8 @@ ATLAS_ERR_DEVICE = 8
 ATLAS_DTYPE_F32 = 0
 ATLAS_DTYPE_BF16 = 1
 
+ATLAS_PAGE_REGENERATE = -1   # page-table value of a page regenerated inside atlas_attend_decode_regen
+
 ABI_VERSION = 1
 
 _DTYPES = {torch.float32: ATLAS_DTYPE_F32, torch.bfloat16: ATLAS_DTYPE_BF16}
@@ -88,7 +90,8 @@ class RegenArgs(ctypes.Structure):
 
 EXPORTS = ("atlas_abi_version", "atlas_status_str", "atlas_last_error",
            "atlas_decode_workspace_bytes", "atlas_prefill_workspace_bytes",
-           "atlas_attend_decode", "atlas_attend_prefill", "atlas_regenerate_pages")
+           "atlas_attend_decode", "atlas_attend_prefill", "atlas_regenerate_pages",
+           "atlas_attend_decode_regen")
 
 
 def _load():
@@ -112,6 +115,9 @@ def _load():
         fn.argtypes = [ctypes.POINTER(AttnArgs), ctypes.c_void_p]
     lib.atlas_regenerate_pages.restype = ctypes.c_int32
     lib.atlas_regenerate_pages.argtypes = [ctypes.POINTER(RegenArgs), ctypes.c_void_p]
+    lib.atlas_attend_decode_regen.restype = ctypes.c_int32
+    lib.atlas_attend_decode_regen.argtypes = [ctypes.POINTER(AttnArgs), ctypes.c_uint64, ctypes.c_int32,
+                                              ctypes.c_void_p]
     if lib.atlas_abi_version() != ABI_VERSION:
         raise ImportError(f"libatlas ABI {lib.atlas_abi_version()} != binding ABI {ABI_VERSION}")
     return lib
@@ -245,7 +251,7 @@ def lib_status_from_error() -> int:
 
 
 def _attend(entry, ws_fn, q, k_pages, v_pages, page_table, context_lens, scale, out, lse,
-            workspace, stream, **kw):
+            workspace, stream, extra=(), **kw):
     B, q_len, hq, d = q.shape
     want_lse = kw.pop("want_lse", True)
     if out is None:
@@ -263,7 +269,7 @@ def _attend(entry, ws_fn, q, k_pages, v_pages, page_table, context_lens, scale, 
         _check(workspace, "workspace", None, q.device)
         args.workspace = _ptr(workspace)
         args.workspace_bytes = workspace.numel() * workspace.element_size()
-    st = getattr(lib, entry)(ctypes.byref(args), _stream(stream))
+    st = getattr(lib, entry)(ctypes.byref(args), *extra, _stream(stream))
     if st != ATLAS_OK:
         raise AtlasError(st, entry)
     return out, lse
@@ -275,6 +281,20 @@ def atlas_attend_decode(q, k_pages, v_pages, page_table, context_lens, scale, *,
     """Decode attention (q_len == 1).  Returns (out [B][1][Hq][D] f32, lse [B][1][Hq] f32)."""
     return _attend("atlas_attend_decode", atlas_decode_workspace_bytes, q, k_pages, v_pages,
                    page_table, context_lens, scale, out, lse, workspace, stream,
+                   head_map=head_map, window=window, sink_tokens=sink_tokens, softcap=softcap,
+                   split_tokens=split_tokens, want_lse=want_lse)
+
+
+def atlas_attend_decode_regen(q, k_pages, v_pages, page_table, context_lens, scale, seed: int, layer: int = 0,
+                              *, head_map=None, window=None, sink_tokens=None, softcap=None, out=None,
+                              lse=None, workspace=None, split_tokens=0, stream=None, want_lse=True):
+    """Decode attention in which page_table entries equal to ATLAS_PAGE_REGENERATE (-1) are
+    regenerated inside the kernel from (seed, layer, sequence, logical page) -- the rows
+    atlas_regenerate_pages would write -- instead of read from the arenas.  fp32 only.
+    Returns (out [B][1][Hq][D] f32, lse [B][1][Hq] f32)."""
+    return _attend("atlas_attend_decode_regen", atlas_decode_workspace_bytes, q, k_pages, v_pages,
+                   page_table, context_lens, scale, out, lse, workspace, stream,
+                   extra=(ctypes.c_uint64(int(seed) & 0xFFFFFFFFFFFFFFFF), ctypes.c_int32(int(layer))),
                    head_map=head_map, window=window, sink_tokens=sink_tokens, softcap=softcap,
                    split_tokens=split_tokens, want_lse=want_lse)
 

@@ -236,7 +236,7 @@ int32_t check_pointers(const atlas_attn_args *a, const Plan &p)
 
 // Validation mode: copy the device-resident lengths and page table to the
 // host, check them, and scan the visible inputs for NaN/Inf.
-int32_t validate_device(const atlas_attn_args *a, const Plan &p, hipStream_t stream)
+int32_t validate_device(const atlas_attn_args *a, const Plan &p, hipStream_t stream, bool regen)
 {
     const int B = a->batch;
     std::vector<int32_t> ctx(B), pt((size_t)B * a->max_pages_per_seq), win(B, 0), snk(B, 0);
@@ -260,6 +260,8 @@ int32_t validate_device(const atlas_attn_args *a, const Plan &p, hipStream_t str
         const int np = (ctx[b] + a->page_size - 1) / a->page_size;
         for (int lp = 0; lp < np; ++lp) {
             const int32_t id = pt[(size_t)b * a->max_pages_per_seq + lp];
+            if (regen && id == ATLAS_PAGE_REGENERATE)
+                continue;
             if (id < 0 || id >= a->num_phys_pages)
                 return fail(ATLAS_ERR_POOL, "page_table[%d][%d] = %d outside the pool of %d pages", b, lp, id,
                             a->num_phys_pages);
@@ -301,18 +303,32 @@ int32_t validate_device(const atlas_attn_args *a, const Plan &p, hipStream_t str
     return ok();
 }
 
-int32_t attend(const atlas_attn_args *a, void *stream_ptr, bool decode)
+// In-kernel regeneration request of atlas_attend_decode_regen.
+struct RegenSpec {
+    uint64_t seed;
+    int32_t layer;
+};
+
+int32_t attend(const atlas_attn_args *a, void *stream_ptr, bool decode, const RegenSpec *regen = nullptr)
 {
     Plan p;
     int32_t st = check_shapes(a, decode, &p);
     if (st != ATLAS_OK)
         return st;
+    if (regen) {
+        if (a->dtype != ATLAS_DTYPE_F32)
+            return fail(ATLAS_ERR_UNSUPPORTED, "in-kernel regeneration runs on fp32 K/V only");
+        if (regen->layer < 0 || regen->layer >= (1 << 16))
+            return fail(ATLAS_ERR_RANGE, "layer must be in [0, 65536)");
+        if (a->batch >= (1 << 16))
+            return fail(ATLAS_ERR_RANGE, "in-kernel regeneration takes fewer than 65536 sequences");
+    }
     st = check_pointers(a, p);
     if (st != ATLAS_OK)
         return st;
     hipStream_t stream = reinterpret_cast<hipStream_t>(stream_ptr);
     if (validate_mode()) {
-        st = validate_device(a, p, stream);
+        st = validate_device(a, p, stream, regen != nullptr);
         if (st != ATLAS_OK)
             return st;
     }
@@ -375,6 +391,11 @@ int32_t attend(const atlas_attn_args *a, void *stream_ptr, bool decode)
     k.n_chunks = p.n_chunks;
     k.scale = a->scale;
     k.groups = p.groups;
+    if (regen) {
+        k.regen_seed = regen->seed;
+        k.regen_layer = regen->layer;
+        k.regen = 1;
+    }
 
     if (std::getenv("ATLAS_DEBUG"))
         std::fprintf(stderr,
@@ -433,6 +454,12 @@ size_t atlas_prefill_workspace_bytes(const atlas_attn_args *args) { return works
 int32_t atlas_attend_decode(const atlas_attn_args *args, void *stream) { return attend(args, stream, true); }
 
 int32_t atlas_attend_prefill(const atlas_attn_args *args, void *stream) { return attend(args, stream, false); }
+
+int32_t atlas_attend_decode_regen(const atlas_attn_args *args, uint64_t seed, int32_t layer, void *stream)
+{
+    const RegenSpec r{seed, layer};
+    return attend(args, stream, true, &r);
+}
 
 int32_t atlas_regenerate_pages(const atlas_regen_args *a, void *stream)
 {

@@ -42,6 +42,11 @@ struct SplitArgs {
     int32_t rows_per_item;      // rows of one work item (a chunk of a K/V head's rows)
     int32_t n_chunks;           // chunks per K/V head
     float scale;
+    // In-kernel regeneration (fp32 fold only): page-table entries of -1 are
+    // regenerated from (regen_seed, regen_layer, sequence, logical page).
+    uint64_t regen_seed;
+    int32_t regen_layer;
+    int32_t regen;              // 0: every page is read from the arenas
     HeadGroups groups;
 };
 

@@ -17,8 +17,17 @@
 // hardware v_exp_f32 with the scale folded by log2(e).  Page ids of the
 // split are staged once in LDS, so the per-key address math is scalar-free
 // shifts and masks (page sizes are powers of two).
+//
+// In-kernel regeneration (REGEN instances): page-table entries of -1 mark
+// pages that are not stored; their keys' K and V values are produced at fold
+// time by the page regenerator's generator (philox.h) for exactly this
+// lane's dims -- a lane's 16-byte piece is one generator call of 4 dims --
+// so the fold sees the same bits a regenerated scratch page would hold.
+// Their loads still go out (to page 0, cached) so that the prefetch stays
+// unconditional.
 #include "device.h"
 #include "kernels.h"
+#include "philox.h"
 
 namespace atlas {
 namespace {
@@ -38,7 +47,7 @@ struct Elem<float> {
     }
 };
 
-template <typename E, int D, int MC, int KU>
+template <typename E, int D, int MC, int KU, bool REGEN>
 __global__ __launch_bounds__(256) void split_valu_kernel(SplitArgs a)
 {
     constexpr int EPC = Elem<E>::kPer16;                 // elements per 16-byte piece
@@ -89,7 +98,7 @@ __global__ __launch_bounds__(256) void split_valu_kernel(SplitArgs a)
     const int np = ((kb - 1) >> ps) - p0 + 1;
     for (int t = tid; t < np; t += 256) {
         int pid = a.page_table[(int64_t)b * a.max_pages + p0 + t];
-        s_pid[t] = ((unsigned)pid < (unsigned)a.num_phys) ? pid : 0;
+        s_pid[t] = (REGEN && pid == -1) ? -1 : (((unsigned)pid < (unsigned)a.num_phys) ? pid : 0);
     }
 
     // Query slices and positions of the chunk's rows.
@@ -141,13 +150,19 @@ __global__ __launch_bounds__(256) void split_valu_kernel(SplitArgs a)
     struct Buf {
         uint4 k[KU][NL];
         uint4 v[KU][NL];
+        uint32_t cold;  // REGEN: bit u set when key u's page is regenerated here
     };
     auto load = [&](Buf &bf, int base) {
+        bf.cold = 0;
 #pragma unroll
         for (int u = 0; u < KU; ++u) {
             const int key = base + u * (4 * GPW) + wave * GPW + grp;
             const int jj = key < kb ? key : kb - 1;
-            const int pid = s_pid[(jj >> ps) - p0];
+            int pid = s_pid[(jj >> ps) - p0];
+            if constexpr (REGEN) {
+                bf.cold |= (pid < 0 ? 1u : 0u) << u;
+                pid = pid < 0 ? 0 : pid;
+            }
             const int64_t row = ((int64_t)pid * a.hkv << ps) + head_off + (jj & pmask);
             const E *kr = kbase + row * D;
             const E *vr = vbase + row * D;
@@ -168,6 +183,25 @@ __global__ __launch_bounds__(256) void split_valu_kernel(SplitArgs a)
             for (int n = 0; n < NL; ++n) {
                 Elem<E>::unpack(bf.k[u][n], &kv[u][n * EPC]);
                 Elem<E>::unpack(bf.v[u][n], &vv[u][n * EPC]);
+            }
+        }
+        if constexpr (REGEN) {
+            static_assert(EPC == 4, "one generator call per 16-byte fp32 piece");
+            if (bf.cold) {
+#pragma unroll
+                for (int u = 0; u < KU; ++u) {
+                    if ((bf.cold >> u) & 1u) {
+                        const uint32_t tok = (uint32_t)(key[u] < kb ? key[u] : kb - 1);
+#pragma unroll
+                        for (int n = 0; n < NL; ++n) {
+                            const uint32_t quad = (uint32_t)(n * R + li);
+                            regen_quad(a.regen_seed, (uint32_t)a.regen_layer, (uint32_t)b, 1u, (uint32_t)g, tok,
+                                       quad, &kv[u][n * EPC]);
+                            regen_quad(a.regen_seed, (uint32_t)a.regen_layer, (uint32_t)b, 2u, (uint32_t)g, tok,
+                                       quad, &vv[u][n * EPC]);
+                        }
+                    }
+                }
             }
         }
 #pragma unroll
@@ -302,7 +336,10 @@ hipError_t launch_one(const SplitArgs &a, hipStream_t stream)
     constexpr int DPL = D / 16;
     constexpr int KU = (D == 64) ? ((MC <= 2) ? 8 : (MC * DPL <= 16 ? 4 : 2)) : ((MC <= 2) ? 4 : 2);
     dim3 grid(a.max_splits, a.hkv * a.n_chunks, a.batch);
-    hipLaunchKernelGGL((split_valu_kernel<E, D, MC, KU>), grid, dim3(256), 0, stream, a);
+    if (a.regen)
+        hipLaunchKernelGGL((split_valu_kernel<E, D, MC, KU, true>), grid, dim3(256), 0, stream, a);
+    else
+        hipLaunchKernelGGL((split_valu_kernel<E, D, MC, KU, false>), grid, dim3(256), 0, stream, a);
     return hipGetLastError();
 }
 

@@ -195,6 +195,27 @@ int32_t atlas_attend_prefill(const atlas_attn_args *args, void *stream);
 /* Regenerate whole pages (all heads, all P tokens) into the arenas. */
 int32_t atlas_regenerate_pages(const atlas_regen_args *args, void *stream);
 
+/* Page-table value of a page that is not stored (atlas_attend_decode_regen). */
+#define ATLAS_PAGE_REGENERATE (-1)
+
+/*
+ * Decode with cold pages regenerated inside the attention kernel.  The
+ * CFR-Atlas README ("Core contract") replays a cold page on demand and
+ * requires attention over replayed pages to equal attention over stored
+ * ones; here the replay happens in the kernel's registers instead of a
+ * scratch page, so a cold page costs generator arithmetic but no HBM
+ * traffic.  Same as atlas_attend_decode (same arguments, workspace and
+ * output), except that page_table entries equal to ATLAS_PAGE_REGENERATE
+ * stand for the rows atlas_regenerate_pages would write for
+ * (seed, layer, sequence b, that logical page): the result equals
+ * regenerating those pages into the pool and calling atlas_attend_decode, to
+ * the bit.  Nothing of such a page is read from the arenas.  fp32 only
+ * (ATLAS_ERR_UNSUPPORTED otherwise); requires layer in [0, 65536) and
+ * batch < 65536 (ATLAS_ERR_RANGE).  Validation mode accepts
+ * ATLAS_PAGE_REGENERATE entries.
+ */
+int32_t atlas_attend_decode_regen(const atlas_attn_args *args, uint64_t seed, int32_t layer, void *stream);
+
 #ifdef __cplusplus
 }
 #endif

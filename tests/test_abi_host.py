@@ -24,7 +24,7 @@ def test_header_declares_the_boundary():
     assert names == sorted(["atlas_abi_version", "atlas_status_str", "atlas_last_error",
                             "atlas_decode_workspace_bytes", "atlas_prefill_workspace_bytes",
                             "atlas_attend_decode", "atlas_attend_prefill",
-                            "atlas_regenerate_pages"])
+                            "atlas_regenerate_pages", "atlas_attend_decode_regen"])
 
 
 def test_library_exports_every_declared_symbol():
@@ -113,6 +113,20 @@ def test_workspace_sizing():
     assert (n - 256) % (rows * (d + 2) * 4) == 0 and n > 256
     bad = _valid_args(head_dim=80)
     assert A.lib.atlas_decode_workspace_bytes(ctypes.byref(bad)) == ctypes.c_size_t(-1).value
+
+
+def test_decode_regen_rejects_bad_arguments_before_launch():
+    from exact_paged_causal_amd import atlas as A
+    fn = A.lib.atlas_attend_decode_regen
+    a = _valid_args(dtype=1)                      # in-kernel regeneration is fp32 only
+    assert fn(ctypes.byref(a), 7, 0, None) == A.ATLAS_ERR_UNSUPPORTED
+    for layer in (-1, 1 << 16):
+        assert fn(ctypes.byref(_valid_args()), 7, layer, None) == A.ATLAS_ERR_RANGE, layer
+    assert fn(ctypes.byref(_valid_args(q_len=2)), 7, 0, None) == A.ATLAS_ERR_SHAPE   # decode only
+    assert fn(ctypes.byref(_valid_args(q=None)), 7, 0, None) == A.ATLAS_ERR_NULL
+    assert fn(ctypes.byref(_valid_args(workspace_bytes=16)), 7, 0, None) == A.ATLAS_ERR_WORKSPACE
+    assert A.ATLAS_PAGE_REGENERATE == -1
+    assert "#define ATLAS_PAGE_REGENERATE (-1)" in open(HEADER).read()
 
 
 def test_regenerate_rejects_bad_arguments():
