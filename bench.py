@@ -14,7 +14,11 @@ are reported beside it.  Per-kernel times come from HIP events recorded on
 the stream the kernels run on.  After the timed steps, the three smaller
 synthetic workloads (single-head decode, GQA short-query suffix attention,
 mixed-length decode with window / sinks / softcap) are timed per call and
-reported under "workloads" with the two step workloads.
+reported under "workloads" with the two step workloads, and the long-context
+decode is run once more with its cold pages generated inside the attention
+kernel (atlas_attend_decode_regen) instead of regenerated into scratch
+("next": "fused_regen_decode"; its output is compared bit for bit with the
+step's).
 
 Prints one JSON line.  `--gpus N` with N > 1 exits: this path runs on one GPU.
 """
@@ -36,7 +40,7 @@ sys.path.insert(0, ROOT)
 PROFILED_SOURCES = {
     "decode_split_long_context": ["split_valu.hip", "merge.hip", "plan.h", "device.h", "kernels.h"],
     "prefill_tiled_causal_8192": ["prefill_mfma.hip", "device.h", "kernels.h"],
-    "regen_long_context": ["regen.hip", "device.h", "kernels.h"],
+    "regen_long_context": ["regen.hip", "philox.h", "device.h", "kernels.h"],
 }
 
 HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, GB/s
@@ -153,6 +157,34 @@ def _arena(torch, workloads, np, w, lay):
     k.index_copy_(0, ids, kl)
     v.index_copy_(0, ids, vl)
     return k, v
+
+
+def fused_report(torch, np, d, atlas, dec_ms, regen_ms, calls=30):
+    """Long-context decode with the cold pages generated inside the fold
+    (atlas_attend_decode_regen) instead of regenerated into scratch: same
+    inputs and outputs as one regenerate + decode step, compared bit for bit
+    with the step's own output."""
+    w, lay = d["w"], d["lay"]
+    pt = lay.page_table.copy()
+    for seq, lp, _ in lay.cold_jobs:
+        pt[seq, lp] = -1
+    pt = torch.from_numpy(pt).cuda()
+    out = torch.empty(w.batch, 1, w.hq, w.head_dim, dtype=torch.float32, device="cuda")
+    ref = torch.empty_like(out)
+    atlas.atlas_regenerate_pages(d["k"], d["v"], d["cold"], seed=w.seed, layer=w.layer)
+    atlas.atlas_attend_decode(d["q"], d["k"], d["v"], d["pt"], d["ctx"], w.scale, out=ref)
+    call = lambda: atlas.atlas_attend_decode_regen(d["q"], d["k"], d["v"], pt, d["ctx"], w.scale,
+                                                   seed=w.seed, layer=w.layer, out=out)
+    us = _median_call_us(torch, np, call, calls=calls)
+    torch.cuda.synchronize()
+    n_cold, n_pages = int(lay.cold_jobs.shape[0]), int(lay.page_table.size)
+    per_page = w.hkv * w.page_size * w.head_dim * 4 * 2
+    unfused = (dec_ms + regen_ms) * 1000.0
+    return {"us": round(us, 1), "unfused_us": round(unfused, 1), "speedup": round(unfused / us, 3),
+            "hot_kv_bytes_read": (n_pages - n_cold) * per_page, "cold_kv_bytes_generated": n_cold * per_page,
+            "generated_values": n_cold * per_page // 4,
+            "bitwise_equal_to_unfused": bool(torch.equal(out, ref)),
+            "note": "atlas_attend_decode_regen: cold pages (page-table -1) generated in the fold's registers"}
 
 
 def workload_report(torch, np, workloads, atlas):
@@ -398,6 +430,9 @@ def main():
                          "traffic": measured_traffic("prefill_tiled_causal_8192"),
                          "traffic_unit": "HBM bytes per call (rocprofv3 FETCH_SIZE + WRITE_SIZE, copy-calibrated)"},
         }
+    if not args.no_workloads:
+        result["next"] = {"fused_regen_decode": fused_report(torch, np, d, atlas, dec_ms, regen_ms)}
+        print("bench: fused regeneration timed", file=sys.stderr, flush=True)
     if not args.no_workloads:
         # Every synthetic workload's throughput (the long-context decode and
         # the prefill are the step's own figures above).
