@@ -88,10 +88,31 @@ class RegenArgs(ctypes.Structure):
     ]
 
 
+class AppendArgs(ctypes.Structure):
+    _fields_ = [
+        ("dtype", ctypes.c_int32),
+        ("batch", ctypes.c_int32),
+        ("n_new", ctypes.c_int32),
+        ("num_kv_heads", ctypes.c_int32),
+        ("head_dim", ctypes.c_int32),
+        ("page_size", ctypes.c_int32),
+        ("num_phys_pages", ctypes.c_int32),
+        ("max_pages_per_seq", ctypes.c_int32),
+        ("k_new", ctypes.c_void_p),
+        ("v_new", ctypes.c_void_p),
+        ("page_table", ctypes.c_void_p),
+        ("start_pos", ctypes.c_void_p),
+        ("k_pages", ctypes.c_void_p),
+        ("v_pages", ctypes.c_void_p),
+    ]
+
+
 EXPORTS = ("atlas_abi_version", "atlas_status_str", "atlas_last_error",
            "atlas_decode_workspace_bytes", "atlas_prefill_workspace_bytes",
            "atlas_attend_decode", "atlas_attend_prefill", "atlas_regenerate_pages",
-           "atlas_attend_decode_regen")
+           "atlas_attend_decode_regen", "atlas_append_kv", "atlas_pool_create", "atlas_pool_destroy",
+           "atlas_pool_alloc", "atlas_pool_retain", "atlas_pool_release", "atlas_pool_free_pages",
+           "atlas_pool_refcount")
 
 
 def _load():
@@ -118,6 +139,20 @@ def _load():
     lib.atlas_attend_decode_regen.restype = ctypes.c_int32
     lib.atlas_attend_decode_regen.argtypes = [ctypes.POINTER(AttnArgs), ctypes.c_uint64, ctypes.c_int32,
                                               ctypes.c_void_p]
+    lib.atlas_append_kv.restype = ctypes.c_int32
+    lib.atlas_append_kv.argtypes = [ctypes.POINTER(AppendArgs), ctypes.c_void_p]
+    lib.atlas_pool_create.restype = ctypes.c_int32
+    lib.atlas_pool_create.argtypes = [ctypes.c_int32, ctypes.POINTER(ctypes.c_void_p)]
+    lib.atlas_pool_destroy.restype = None
+    lib.atlas_pool_destroy.argtypes = [ctypes.c_void_p]
+    for name in ("atlas_pool_alloc", "atlas_pool_retain", "atlas_pool_release"):
+        fn = getattr(lib, name)
+        fn.restype = ctypes.c_int32
+        fn.argtypes = [ctypes.c_void_p, ctypes.c_int32, ctypes.POINTER(ctypes.c_int32)]
+    lib.atlas_pool_free_pages.restype = ctypes.c_int32
+    lib.atlas_pool_free_pages.argtypes = [ctypes.c_void_p]
+    lib.atlas_pool_refcount.restype = ctypes.c_int32
+    lib.atlas_pool_refcount.argtypes = [ctypes.c_void_p, ctypes.c_int32]
     if lib.atlas_abi_version() != ABI_VERSION:
         raise ImportError(f"libatlas ABI {lib.atlas_abi_version()} != binding ABI {ABI_VERSION}")
     return lib
@@ -336,3 +371,83 @@ def atlas_regenerate_pages(k_pages, v_pages, jobs, seed: int, layer: int = 0, st
     st = lib.atlas_regenerate_pages(ctypes.byref(a), _stream(stream))
     if st != ATLAS_OK:
         raise AtlasError(st, "atlas_regenerate_pages")
+
+
+def atlas_append_kv(k_pages, v_pages, k_new, v_new, page_table, start_pos, stream=None):
+    """Write new tokens' K/V rows (k_new, v_new [B][n_new][Hkv][D]) into their pages:
+    token t of sequence b goes to position start_pos[b] + t (page_table[b][pos // P],
+    row pos % P) in both arenas."""
+    if k_pages.dtype not in _DTYPES:
+        raise ValueError("arena dtype must be float32 or bfloat16")
+    dev = k_pages.device
+    _check(k_pages, "k_pages", None, dev, 4)
+    _check(v_pages, "v_pages", k_pages.dtype, dev, 4)
+    _check(k_new, "k_new", k_pages.dtype, dev, 4)
+    _check(v_new, "v_new", k_pages.dtype, dev, 4)
+    _check(page_table, "page_table", torch.int32, dev, 2)
+    _check(start_pos, "start_pos", torch.int32, dev, 1)
+    num_phys, hkv, P, d = k_pages.shape
+    B, n_new, hk2, d2 = k_new.shape
+    if v_pages.shape != k_pages.shape or v_new.shape != k_new.shape or hk2 != hkv or d2 != d:
+        raise ValueError("k_new/v_new must be [B][n_new][Hkv][D] matching the arenas")
+    if page_table.shape[0] != B or start_pos.shape[0] != B:
+        raise ValueError("page_table and start_pos need one row per sequence")
+    a = AppendArgs()
+    a.dtype = _DTYPES[k_pages.dtype]
+    a.batch, a.n_new, a.num_kv_heads, a.head_dim = B, n_new, hkv, d
+    a.page_size, a.num_phys_pages, a.max_pages_per_seq = P, num_phys, page_table.shape[1]
+    a.k_new, a.v_new = _ptr(k_new), _ptr(v_new)
+    a.page_table, a.start_pos = _ptr(page_table), _ptr(start_pos)
+    a.k_pages, a.v_pages = _ptr(k_pages), _ptr(v_pages)
+    st = lib.atlas_append_kv(ctypes.byref(a), _stream(stream))
+    if st != ATLAS_OK:
+        raise AtlasError(st, "atlas_append_kv")
+
+
+class PagePool:
+    """Host-side page pool (reference-counted physical page ids) of the C ABI."""
+
+    def __init__(self, num_pages: int):
+        h = ctypes.c_void_p()
+        st = lib.atlas_pool_create(int(num_pages), ctypes.byref(h))
+        if st != ATLAS_OK:
+            raise AtlasError(st, "atlas_pool_create")
+        self._h = h
+
+    def close(self):
+        if self._h:
+            lib.atlas_pool_destroy(self._h)
+            self._h = None
+
+    def __del__(self):
+        self.close()
+
+    @staticmethod
+    def _ids(ids):
+        ids = [int(i) for i in ids]
+        return len(ids), (ctypes.c_int32 * max(len(ids), 1))(*ids)
+
+    def alloc(self, n: int) -> list:
+        buf = (ctypes.c_int32 * max(int(n), 1))()
+        st = lib.atlas_pool_alloc(self._h, int(n), buf)
+        if st != ATLAS_OK:
+            raise AtlasError(st, "atlas_pool_alloc")
+        return list(buf[:int(n)])
+
+    def retain(self, ids):
+        n, buf = self._ids(ids)
+        st = lib.atlas_pool_retain(self._h, n, buf)
+        if st != ATLAS_OK:
+            raise AtlasError(st, "atlas_pool_retain")
+
+    def release(self, ids):
+        n, buf = self._ids(ids)
+        st = lib.atlas_pool_release(self._h, n, buf)
+        if st != ATLAS_OK:
+            raise AtlasError(st, "atlas_pool_release")
+
+    def free_pages(self) -> int:
+        return int(lib.atlas_pool_free_pages(self._h))
+
+    def refcount(self, page: int) -> int:
+        return int(lib.atlas_pool_refcount(self._h, int(page)))

@@ -14,6 +14,7 @@
 #include <cstdio>
 #include <cstdlib>
 #include <cstring>
+#include <mutex>
 #include <vector>
 
 #include "../../include/atlas.h"
@@ -500,6 +501,175 @@ int32_t atlas_regenerate_pages(const atlas_regen_args *a, void *stream)
     if (e != hipSuccess)
         return fail(ATLAS_ERR_DEVICE, "regen launch: %s", hipGetErrorString(e));
     return ok();
+}
+
+int32_t atlas_append_kv(const atlas_append_args *a, void *stream_ptr)
+{
+    if (!a)
+        return fail(ATLAS_ERR_NULL, "args is NULL");
+    if (a->dtype != ATLAS_DTYPE_F32 && a->dtype != ATLAS_DTYPE_BF16)
+        return fail(ATLAS_ERR_UNSUPPORTED, "dtype %d has no kernel", a->dtype);
+    if (a->head_dim != 64 && a->head_dim != 128)
+        return fail(ATLAS_ERR_UNSUPPORTED, "head_dim %d has no kernel (64 or 128)", a->head_dim);
+    if (a->batch < 1 || a->n_new < 0 || a->num_kv_heads < 1 || a->page_size < 1 || a->num_phys_pages < 1 ||
+        a->max_pages_per_seq < 1)
+        return fail(ATLAS_ERR_SHAPE, "batch, num_kv_heads, page_size, num_phys_pages, max_pages_per_seq >= 1 "
+                                     "and n_new >= 0 required");
+    if (!is_pow2(a->page_size) || a->page_size > 4096)
+        return fail(ATLAS_ERR_UNSUPPORTED, "page_size %d: powers of two up to 4096 only", a->page_size);
+    int64_t t = 0;
+    if (!mul_ok(a->num_phys_pages, a->num_kv_heads, &t) || !mul_ok(t, a->page_size, &t) ||
+        !mul_ok(t, a->head_dim, &t) || !mul_ok(a->max_pages_per_seq, a->page_size, &t) || t > INT32_MAX ||
+        !mul_ok(a->batch, a->n_new, &t) || !mul_ok(t, a->num_kv_heads, &t) || !mul_ok(t, a->head_dim, &t))
+        return fail(ATLAS_ERR_RANGE, "sizes overflow");
+    if (a->n_new == 0)
+        return ok();
+    if (!a->k_new || !a->v_new || !a->page_table || !a->start_pos || !a->k_pages || !a->v_pages)
+        return fail(ATLAS_ERR_NULL, "k_new, v_new, page_table, start_pos, k_pages and v_pages are required");
+    hipStream_t stream = reinterpret_cast<hipStream_t>(stream_ptr);
+    if (validate_mode()) {
+        const int B = a->batch;
+        std::vector<int32_t> sp(B), pt((size_t)B * a->max_pages_per_seq);
+        hipError_t e = hipMemcpyAsync(sp.data(), a->start_pos, sizeof(int32_t) * B, hipMemcpyDeviceToHost, stream);
+        if (e == hipSuccess)
+            e = hipMemcpyAsync(pt.data(), a->page_table, sizeof(int32_t) * pt.size(), hipMemcpyDeviceToHost,
+                               stream);
+        if (e == hipSuccess)
+            e = hipStreamSynchronize(stream);
+        if (e != hipSuccess)
+            return fail(ATLAS_ERR_DEVICE, "validation copy failed: %s", hipGetErrorString(e));
+        const int64_t cap = (int64_t)a->max_pages_per_seq * a->page_size;
+        for (int b = 0; b < B; ++b) {
+            if (sp[b] < 0 || (int64_t)sp[b] + a->n_new > cap)
+                return fail(ATLAS_ERR_RANGE, "start_pos[%d] = %d: positions up to %lld exceed the %lld-token page table",
+                            b, sp[b], (long long)sp[b] + a->n_new - 1, (long long)cap);
+            for (int64_t p = sp[b]; p < (int64_t)sp[b] + a->n_new; p += a->page_size - (p % a->page_size)) {
+                const int32_t id = pt[(size_t)b * a->max_pages_per_seq + p / a->page_size];
+                if (id < 0 || id >= a->num_phys_pages)
+                    return fail(ATLAS_ERR_POOL, "page_table[%d][%lld] = %d outside the pool of %d pages", b,
+                                (long long)(p / a->page_size), id, a->num_phys_pages);
+            }
+        }
+    }
+    atlas::AppendArgs k{};
+    k.k_new = a->k_new;
+    k.v_new = a->v_new;
+    k.page_table = a->page_table;
+    k.start_pos = a->start_pos;
+    k.k_pages = a->k_pages;
+    k.v_pages = a->v_pages;
+    k.batch = a->batch;
+    k.n_new = a->n_new;
+    k.hkv = a->num_kv_heads;
+    k.row_bytes = a->head_dim * (a->dtype == ATLAS_DTYPE_F32 ? 4 : 2);
+    k.page_shift = log2i(a->page_size);
+    k.num_phys = a->num_phys_pages;
+    k.max_pages = a->max_pages_per_seq;
+    hipError_t e = atlas::launch_append(k, stream);
+    if (e != hipSuccess)
+        return fail(ATLAS_ERR_DEVICE, "append launch: %s", hipGetErrorString(e));
+    return ok();
+}
+
+}  // extern "C"
+
+// Host-side page pool: reference counts and a free list under one mutex.
+struct atlas_pool {
+    std::mutex mu;
+    std::vector<int32_t> refs;   // per page; 0 = free
+    std::vector<int32_t> free;   // stack of free ids (top = next to hand out)
+};
+
+extern "C" {
+
+int32_t atlas_pool_create(int32_t num_pages, atlas_pool **out)
+{
+    if (!out)
+        return fail(ATLAS_ERR_NULL, "out is NULL");
+    *out = nullptr;
+    if (num_pages < 1)
+        return fail(ATLAS_ERR_SHAPE, "num_pages must be >= 1");
+    atlas_pool *p = new (std::nothrow) atlas_pool;
+    if (!p)
+        return fail(ATLAS_ERR_RANGE, "out of host memory");
+    p->refs.assign(num_pages, 0);
+    p->free.resize(num_pages);
+    for (int32_t i = 0; i < num_pages; ++i)
+        p->free[i] = num_pages - 1 - i;  // id 0 on top
+    *out = p;
+    return ok();
+}
+
+void atlas_pool_destroy(atlas_pool *pool) { delete pool; }
+
+int32_t atlas_pool_alloc(atlas_pool *pool, int32_t n, int32_t *ids)
+{
+    if (!pool || (n > 0 && !ids))
+        return fail(ATLAS_ERR_NULL, "pool and ids are required");
+    if (n < 0)
+        return fail(ATLAS_ERR_RANGE, "n must be >= 0");
+    std::lock_guard<std::mutex> lock(pool->mu);
+    if ((size_t)n > pool->free.size())
+        return fail(ATLAS_ERR_POOL, "%d pages requested, %zu free", n, pool->free.size());
+    for (int32_t i = 0; i < n; ++i) {
+        ids[i] = pool->free.back();
+        pool->free.pop_back();
+        pool->refs[ids[i]] = 1;
+    }
+    return ok();
+}
+
+int32_t atlas_pool_retain(atlas_pool *pool, int32_t n, const int32_t *ids)
+{
+    if (!pool || (n > 0 && !ids))
+        return fail(ATLAS_ERR_NULL, "pool and ids are required");
+    if (n < 0)
+        return fail(ATLAS_ERR_RANGE, "n must be >= 0");
+    std::lock_guard<std::mutex> lock(pool->mu);
+    for (int32_t i = 0; i < n; ++i)
+        if (ids[i] < 0 || (size_t)ids[i] >= pool->refs.size() || pool->refs[ids[i]] == 0)
+            return fail(ATLAS_ERR_RANGE, "page %d is not in use", ids[i]);
+    for (int32_t i = 0; i < n; ++i)
+        ++pool->refs[ids[i]];
+    return ok();
+}
+
+int32_t atlas_pool_release(atlas_pool *pool, int32_t n, const int32_t *ids)
+{
+    if (!pool || (n > 0 && !ids))
+        return fail(ATLAS_ERR_NULL, "pool and ids are required");
+    if (n < 0)
+        return fail(ATLAS_ERR_RANGE, "n must be >= 0");
+    std::lock_guard<std::mutex> lock(pool->mu);
+    std::vector<int32_t> drop(pool->refs.size(), 0);
+    for (int32_t i = 0; i < n; ++i) {
+        if (ids[i] < 0 || (size_t)ids[i] >= pool->refs.size())
+            return fail(ATLAS_ERR_RANGE, "page %d outside the pool", ids[i]);
+        if (++drop[ids[i]] > pool->refs[ids[i]])
+            return fail(ATLAS_ERR_RANGE, "page %d released more often than it is referenced", ids[i]);
+    }
+    for (int32_t i = 0; i < n; ++i)
+        if (--pool->refs[ids[i]] == 0)
+            pool->free.push_back(ids[i]);
+    return ok();
+}
+
+int32_t atlas_pool_free_pages(const atlas_pool *pool)
+{
+    if (!pool)
+        return 0;
+    std::lock_guard<std::mutex> lock(const_cast<atlas_pool *>(pool)->mu);
+    return (int32_t)pool->free.size();
+}
+
+int32_t atlas_pool_refcount(const atlas_pool *pool, int32_t id)
+{
+    if (!pool)
+        return -1;
+    std::lock_guard<std::mutex> lock(const_cast<atlas_pool *>(pool)->mu);
+    if (id < 0 || (size_t)id >= pool->refs.size())
+        return -1;
+    return pool->refs[id];
 }
 
 }  // extern "C"

@@ -68,6 +68,18 @@ hipError_t launch_split_mfma(const SplitArgs &a, hipStream_t stream);   // bf16 
 hipError_t launch_merge(const SplitArgs &a, hipStream_t stream);
 hipError_t launch_regen(const RegenArgs &a, int dtype, hipStream_t stream);
 
+struct AppendArgs {
+    const void *k_new;          // [B][n_new][Hkv][row_bytes]
+    const void *v_new;
+    const int32_t *page_table;
+    const int32_t *start_pos;
+    void *k_pages;
+    void *v_pages;
+    int32_t batch, n_new, hkv, row_bytes, page_shift, num_phys, max_pages;
+};
+
+hipError_t launch_append(const AppendArgs &a, hipStream_t stream);
+
 struct PrefillArgs {
     const void *q;
     const void *k_pages;

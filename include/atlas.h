@@ -216,6 +216,70 @@ int32_t atlas_regenerate_pages(const atlas_regen_args *args, void *stream);
  */
 int32_t atlas_attend_decode_regen(const atlas_attn_args *args, uint64_t seed, int32_t layer, void *stream);
 
+/*
+ * Appending K/V rows: the decode step's write of each sequence's new tokens
+ * into their pages (CPUAttn README, cache-backed decode streams that grow by
+ * one token per step).  Token t of sequence b (t < n_new) sits at position
+ * p = start_pos[b] + t and is written, for every K/V head, into row p % P of
+ * physical page page_table[b][p / P] of both arenas; nothing else is
+ * written.  The new rows' layout is [B][n_new][Hkv][D] in the arenas' dtype.
+ * Device-resident values are trusted outside validation mode, where a target
+ * page outside the pool returns ATLAS_ERR_POOL and a position outside
+ * [0, max_pages_per_seq * P) returns ATLAS_ERR_RANGE before anything is
+ * written; otherwise rows whose page id or position is out of range are
+ * skipped (never written elsewhere).
+ */
+typedef struct atlas_append_args {
+    int32_t dtype;              /* ATLAS_DTYPE_* of the arenas and the new rows */
+    int32_t batch;              /* B >= 1 */
+    int32_t n_new;              /* tokens appended per sequence, >= 0 */
+    int32_t num_kv_heads;       /* Hkv */
+    int32_t head_dim;           /* D, 64 or 128 */
+    int32_t page_size;          /* P, power of two in [1, 4096] */
+    int32_t num_phys_pages;
+    int32_t max_pages_per_seq;
+    const void *k_new;          /* device [B][n_new][Hkv][D] */
+    const void *v_new;          /* device [B][n_new][Hkv][D] */
+    const int32_t *page_table;  /* device [B][max_pages_per_seq] */
+    const int32_t *start_pos;   /* device [B]: position of each sequence's first new token */
+    void *k_pages;              /* device arena [num_phys_pages][Hkv][P][D] */
+    void *v_pages;              /* device arena */
+} atlas_append_args;
+
+int32_t atlas_append_kv(const atlas_append_args *args, void *stream);
+
+/*
+ * Page pool: host-side bookkeeping of the physical pages of a pair of arenas
+ * (the caller owns the arenas).  Pages carry reference counts so that a
+ * prefix's pages can be shared by several sequences' page tables and return
+ * to the pool when the last user releases them.  CFR-Atlas README ("Core
+ * contract"): an exhausted pool is an error, never a silent eviction.  All
+ * functions are safe to call from several threads.
+ */
+typedef struct atlas_pool atlas_pool;
+
+/* A pool of num_pages (>= 1) free pages with ids 0 .. num_pages-1. */
+int32_t atlas_pool_create(int32_t num_pages, atlas_pool **out);
+void atlas_pool_destroy(atlas_pool *pool);
+
+/* Take n free pages (reference count 1), lowest free ids first after a
+ * fresh create; all or nothing: ATLAS_ERR_POOL when fewer than n are free. */
+int32_t atlas_pool_alloc(atlas_pool *pool, int32_t n, int32_t *ids);
+
+/* Add one reference to each listed page (each must be in use), e.g. when
+ * another sequence starts sharing a prefix.  ATLAS_ERR_RANGE if any id is
+ * out of range or free (then nothing changes). */
+int32_t atlas_pool_retain(atlas_pool *pool, int32_t n, const int32_t *ids);
+
+/* Drop one reference from each listed page (an id may repeat); pages whose
+ * count reaches 0 become free.  ATLAS_ERR_RANGE if any id is out of range or
+ * would drop below 0 (then nothing changes). */
+int32_t atlas_pool_release(atlas_pool *pool, int32_t n, const int32_t *ids);
+
+/* Number of free pages; reference count of one page (-1 if out of range). */
+int32_t atlas_pool_free_pages(const atlas_pool *pool);
+int32_t atlas_pool_refcount(const atlas_pool *pool, int32_t id);
+
 #ifdef __cplusplus
 }
 #endif

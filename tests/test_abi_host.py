@@ -24,7 +24,10 @@ def test_header_declares_the_boundary():
     assert names == sorted(["atlas_abi_version", "atlas_status_str", "atlas_last_error",
                             "atlas_decode_workspace_bytes", "atlas_prefill_workspace_bytes",
                             "atlas_attend_decode", "atlas_attend_prefill",
-                            "atlas_regenerate_pages", "atlas_attend_decode_regen"])
+                            "atlas_regenerate_pages", "atlas_attend_decode_regen", "atlas_append_kv",
+                            "atlas_pool_create", "atlas_pool_destroy", "atlas_pool_alloc",
+                            "atlas_pool_retain", "atlas_pool_release", "atlas_pool_free_pages",
+                            "atlas_pool_refcount"])
 
 
 def test_library_exports_every_declared_symbol():
@@ -127,6 +130,58 @@ def test_decode_regen_rejects_bad_arguments_before_launch():
     assert fn(ctypes.byref(_valid_args(workspace_bytes=16)), 7, 0, None) == A.ATLAS_ERR_WORKSPACE
     assert A.ATLAS_PAGE_REGENERATE == -1
     assert "#define ATLAS_PAGE_REGENERATE (-1)" in open(HEADER).read()
+
+
+def test_append_rejects_bad_arguments_before_launch():
+    from exact_paged_causal_amd import atlas as A
+    a = A.AppendArgs()
+    a.dtype, a.batch, a.n_new, a.num_kv_heads, a.head_dim = 0, 2, 3, 2, 64
+    a.page_size, a.num_phys_pages, a.max_pages_per_seq = 16, 8, 4
+    a.k_new = a.v_new = a.page_table = a.start_pos = a.k_pages = a.v_pages = FAKE
+    for field, value, status in [("dtype", 3, 4), ("head_dim", 80, 4), ("page_size", 12, 4),
+                                 ("batch", 0, 2), ("n_new", -1, 2), ("num_phys_pages", 0, 2),
+                                 ("max_pages_per_seq", 0, 2), ("k_new", None, 1), ("start_pos", None, 1)]:
+        saved = getattr(a, field)
+        setattr(a, field, value)
+        assert A.lib.atlas_append_kv(ctypes.byref(a), None) == status, field
+        setattr(a, field, saved)
+    a.n_new = 0   # nothing to write is not an error (and touches nothing)
+    a.k_new = None
+    assert A.lib.atlas_append_kv(ctypes.byref(a), None) == A.ATLAS_OK
+    assert ctypes.sizeof(A.AppendArgs) == 4 * 8 + 8 * 6
+    assert [f[0] for f in A.AppendArgs._fields_] == _struct_offsets_from_header("atlas_append_args")
+
+
+def test_page_pool_bookkeeping():
+    """Allocation order, all-or-nothing exhaustion, shared pages kept until the
+    last release, and errors that change nothing."""
+    from exact_paged_causal_amd import atlas as A
+    pool = A.PagePool(6)
+    assert pool.free_pages() == 6
+    a = pool.alloc(4)
+    assert a == [0, 1, 2, 3] and pool.free_pages() == 2
+    with pytest.raises(A.AtlasError) as ei:
+        pool.alloc(3)                                    # only 2 free: nothing handed out
+    assert ei.value.status == A.ATLAS_ERR_POOL and pool.free_pages() == 2
+    pool.retain([0, 1])                                  # a second sequence shares the prefix pages
+    assert [pool.refcount(i) for i in range(6)] == [2, 2, 1, 1, 0, 0]
+    pool.release([0, 1, 2, 3])                           # first sequence ends
+    assert [pool.refcount(i) for i in range(6)] == [1, 1, 0, 0, 0, 0] and pool.free_pages() == 4
+    with pytest.raises(A.AtlasError) as ei:
+        pool.release([0, 0])                             # would drop below zero: no change
+    assert ei.value.status == A.ATLAS_ERR_RANGE and pool.refcount(0) == 1
+    for bad in ([2], [7], [-1]):                         # free, outside, negative
+        with pytest.raises(A.AtlasError):
+            pool.retain(bad)
+    with pytest.raises(A.AtlasError):
+        pool.release([6])
+    pool.release([1, 0])
+    assert pool.free_pages() == 6 and pool.refcount(6) == -1
+    assert sorted(pool.alloc(6)) == list(range(6)) and pool.free_pages() == 0
+    assert pool.alloc(0) == []
+    pool.close()
+    h = ctypes.c_void_p()
+    assert A.lib.atlas_pool_create(0, ctypes.byref(h)) == A.ATLAS_ERR_SHAPE
 
 
 def test_regenerate_rejects_bad_arguments():
