@@ -18,7 +18,8 @@ reported under "workloads" with the two step workloads, and the long-context
 decode is run once more with its cold pages generated inside the attention
 kernel (atlas_attend_decode_regen) instead of regenerated into scratch
 ("next": "fused_regen_decode"; its output is compared bit for bit with the
-step's).
+step's); the K/V append of a decode step and of a whole prefill history is
+timed under "next": "append_kv".
 
 Prints one JSON line.  `--gpus N` with N > 1 exits: this path runs on one GPU.
 """
@@ -185,6 +186,34 @@ def fused_report(torch, np, d, atlas, dec_ms, regen_ms, calls=30):
             "generated_values": n_cold * per_page // 4,
             "bitwise_equal_to_unfused": bool(torch.equal(out, ref)),
             "note": "atlas_attend_decode_regen: cold pages (page-table -1) generated in the fold's registers"}
+
+
+def append_report(torch, np, workloads, atlas):
+    """K/V append: the long-context decode step's write of one new token per
+    sequence (B=8, Hkv=8, D=64, fp32, into pages of 512), and a bulk append of
+    a whole 8192-token bf16 history (Hkv=8, D=128, pages of 128) -- a copy
+    bound by HBM (each byte read once and written once)."""
+    rep = {}
+    for name, B, n_new, hkv, d, P, dtype in (("decode_step", 8, 1, 8, 64, 512, "f32"),
+                                             ("bulk_8192", 1, 8192, 8, 128, 128, "bf16")):
+        maxp = (65536 + P - 1) // P if name == "decode_step" else 8192 // P
+        phys = B * maxp
+        k = torch.zeros((phys, hkv, P, d), dtype=torch.float32 if dtype == "f32" else torch.bfloat16,
+                        device="cuda")
+        v = torch.zeros_like(k)
+        kn = workloads.randn((B, n_new, hkv, d), seed=5, dtype=dtype, device="cuda")
+        vn = workloads.randn((B, n_new, hkv, d), seed=6, dtype=dtype, device="cuda")
+        pt = torch.from_numpy(np.random.default_rng(9).permutation(phys).astype(np.int32).reshape(B, maxp)).cuda()
+        start = torch.full((B,), 65535 if name == "decode_step" else 0, dtype=torch.int32, device="cuda")
+        us = _median_call_us(torch, np, lambda: atlas.atlas_append_kv(k, v, kn, vn, pt, start))
+        nbytes = 2 * kn.numel() * kn.element_size()
+        rep[name] = {"us": round(us, 2), "bytes_written": nbytes,
+                     "GBs_read_plus_written": round(2 * nbytes / us / 1e3, 1)}
+        del k, v
+    rep["note"] = ("decode_step is launch-latency bound (32 KiB); bulk_8192 moves 32 MiB of K/V "
+                   "(read + write counted)")
+    torch.cuda.empty_cache()
+    return rep
 
 
 def workload_report(torch, np, workloads, atlas):
@@ -431,7 +460,8 @@ def main():
                          "traffic_unit": "HBM bytes per call (rocprofv3 FETCH_SIZE + WRITE_SIZE, copy-calibrated)"},
         }
     if not args.no_workloads:
-        result["next"] = {"fused_regen_decode": fused_report(torch, np, d, atlas, dec_ms, regen_ms)}
+        result["next"] = {"fused_regen_decode": fused_report(torch, np, d, atlas, dec_ms, regen_ms),
+                          "append_kv": append_report(torch, np, workloads, atlas)}
         print("bench: fused regeneration timed", file=sys.stderr, flush=True)
     if not args.no_workloads:
         # Every synthetic workload's throughput (the long-context decode and
