@@ -164,10 +164,10 @@ int32_t check_shapes(const atlas_attn_args *a, bool decode, Plan *p)
     p->max_context = (int)max_ctx;
     p->rows_total = rows;
 
-    // Path: the tiled kernel for long bf16 prefills without variants; else the
-    // split-KV kernels (matrix cores for bf16, vector ALUs for fp32).
-    const bool variants = a->window || a->sink_tokens || a->softcap;
-    if (!decode && a->dtype == ATLAS_DTYPE_BF16 && a->q_len >= 64 && !variants)
+    // Path: the tiled kernel for long bf16 prefills (window / sinks / softcap
+    // included); else the split-KV kernels (matrix cores for bf16, vector ALUs
+    // for fp32).
+    if (!decode && a->dtype == ATLAS_DTYPE_BF16 && a->q_len >= 64)
         p->path = Path::TiledPrefill;
     else if (a->dtype == ATLAS_DTYPE_BF16)
         p->path = Path::SplitMfma;
@@ -341,6 +341,9 @@ int32_t attend(const atlas_attn_args *a, void *stream_ptr, bool decode, const Re
         k.v_pages = a->v_pages;
         k.page_table = a->page_table;
         k.context_lens = a->context_lens;
+        k.window = a->window;
+        k.sinks = a->sink_tokens;
+        k.softcap = a->softcap;
         k.out = a->out;
         k.lse = a->lse;
         k.batch = a->batch;

@@ -86,6 +86,9 @@ struct PrefillArgs {
     const void *v_pages;
     const int32_t *page_table;
     const int32_t *context_lens;
+    const int32_t *window;      // may be null
+    const int32_t *sinks;       // may be null
+    const float *softcap;       // may be null
     float *out;
     float *lse;
     int32_t batch, q_len, hq, hkv, head_dim, page_shift, num_phys, max_pages, max_context;

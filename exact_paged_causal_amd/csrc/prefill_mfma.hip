@@ -10,8 +10,11 @@
 //                of the group) pairs, so a K/V tile staged in LDS serves all
 //                q-heads of the group (grouped-query attention);
 //   key blocks = 64 keys; block kb runs only while kb*64 <= the last row's
-//                position (causal block-stop); only blocks that reach past
-//                the first row's position apply the per-row causal mask;
+//                position (causal block-stop); with a sliding window the
+//                blocks before the lowest row's window start are skipped
+//                (except the blocks holding the sink keys); only blocks some
+//                row does not see whole apply the per-row mask; a softcap is
+//                applied to the scores before the mask;
 //   per wave   = 32 rows.  S^T = K Q^T on v_mfma_f32_32x32x16_bf16 (A = K
 //                from LDS, B = Q held in registers), so each lane owns one
 //                row's scores and the row max is lane-local plus one swap
@@ -107,6 +110,11 @@ __global__ __launch_bounds__(512) void prefill_kernel(PrefillArgs a)
     const int i1 = i0 + npos < a.q_len ? i0 + npos : a.q_len;
     const int pos_lo = ctx - a.q_len + i0;
     const int pos_hi = ctx - a.q_len + i1 - 1;
+    // Per-sequence variants: sliding window of W keys (0 = off), the first S
+    // keys always visible where a window is set, softcap cap (0 = off).
+    const int W = a.window ? a.window[b] : 0;
+    const int S = (a.sinks && W > 0) ? a.sinks[b] : 0;
+    const float cap = a.softcap ? a.softcap[b] : 0.0f;
 
     // This lane's row.
     const int r = wave * 32 + (lane & 31);
@@ -148,7 +156,6 @@ __global__ __launch_bounds__(512) void prefill_kernel(PrefillArgs a)
             sm.pid[t] = ((unsigned)pid < (unsigned)a.num_phys) ? pid : 0;
         }
     };
-    stage_pids(0);
 
     // Global -> registers for key block kb (zeros past the last visible key).
     // Thread t stages CH adjacent 16-byte pieces of one row: one page lookup.
@@ -204,24 +211,41 @@ __global__ __launch_bounds__(512) void prefill_kernel(PrefillArgs a)
     for (int s = 0; s < KS; ++s)
         asm volatile("" : "+v"(qf[s]));
 
+    // Key blocks the rows can see: with a window, the sink blocks and then
+    // the blocks from the lowest row's window start to the diagonal (blocks
+    // in between are skipped); otherwise every block up to the diagonal.
     const int kb_last = pos_hi >= 0 ? pos_hi / kBN : -1;
+    int first_win = 0, n_sink_blk = 0;
+    if (W > 0 && kb_last >= 0) {
+        const int lo_key = pos_lo - W + 1;
+        first_win = lo_key > 0 ? lo_key / kBN : 0;
+        n_sink_blk = S > 0 ? min((S + kBN - 1) / kBN, first_win) : 0;
+    }
+    const int n_iter = kb_last < 0 ? 0 : n_sink_blk + (kb_last - first_win + 1);
+    auto block_at = [&](int it) { return it < n_sink_blk ? it : first_win + (it - n_sink_blk); };
+
+    if (n_iter > 0)
+        stage_pids((block_at(0) * kBN) >> ps);
     __syncthreads();  // page ids staged
-    if (kb_last >= 0) {
-        fetch(0);
+    if (n_iter > 0) {
+        fetch(block_at(0));
         stash(0);
     }
     __syncthreads();
 
-    for (int kb = 0; kb <= kb_last; ++kb) {
-        const int cur = kb & 1;
-        if (kb < kb_last && ((((kb + 1) * kBN + kBN - 1) >> ps) - pid_base) >= kPidWindow) {
+    for (int it = 0; it < n_iter; ++it) {
+        const int kb = block_at(it);
+        const int cur = it & 1;
+        const bool more = it + 1 < n_iter;
+        const int kb_next = more ? block_at(it + 1) : kb;
+        if (more && (((kb_next * kBN + kBN - 1) >> ps) - pid_base) >= kPidWindow) {
             // Uniform across the workgroup: move the page-id window forward.
             __syncthreads();
-            stage_pids(((kb + 1) * kBN) >> ps);
+            stage_pids((kb_next * kBN) >> ps);
             __syncthreads();
         }
-        if (kb < kb_last)
-            fetch(kb + 1);
+        if (more)
+            fetch(kb_next);
 
         // S^T for the block: two 32-key tiles.
         __builtin_amdgcn_s_setprio(1);
@@ -248,14 +272,29 @@ __global__ __launch_bounds__(512) void prefill_kernel(PrefillArgs a)
 
         __builtin_amdgcn_s_setprio(0);
 
-        // Causal mask where the block reaches past the first row.
-        if (kb * kBN + kBN - 1 > pos_lo) {
+        // Softcap (before the mask): s' = cap tanh(s scale / cap), kept in the
+        // units of the raw product so that the scale below still applies.
+        if (cap > 0.0f) {
+            const float inv = a.scale / cap, back = cap / a.scale;
+#pragma unroll
+            for (int t = 0; t < 2; ++t)
+#pragma unroll
+                for (int e = 0; e < 16; ++e)
+                    st[t][e] = back * tanhf(st[t][e] * inv);
+        }
+        // Mask only blocks some row does not see whole: past the first row's
+        // position (causal), or not inside every row's window or sink range.
+        const int k0 = kb * kBN;
+        const bool all_causal = k0 + kBN - 1 <= pos_lo;
+        const bool all_window = W <= 0 || k0 > pos_hi - W || k0 + kBN - 1 < S;
+        if (!(all_causal && all_window)) {
 #pragma unroll
             for (int t = 0; t < 2; ++t)
 #pragma unroll
                 for (int e = 0; e < 16; ++e) {
-                    const int j = kb * kBN + 32 * t + 8 * (e >> 2) + 4 * half + (e & 3);
-                    if (j > pos)
+                    const int j = k0 + 32 * t + 8 * (e >> 2) + 4 * half + (e & 3);
+                    const bool vis = j <= pos && (W <= 0 || j > pos - W || j < S);
+                    if (!vis)
                         st[t][e] = -INFINITY;
                 }
         }
@@ -335,7 +374,7 @@ __global__ __launch_bounds__(512) void prefill_kernel(PrefillArgs a)
 
         __builtin_amdgcn_s_setprio(0);
 
-        if (kb < kb_last)
+        if (more)
             stash(cur ^ 1);
         __syncthreads();
     }

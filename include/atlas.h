@@ -182,10 +182,11 @@ int32_t atlas_attend_decode(const atlas_attn_args *args, void *stream);
 
 /*
  * Prefill / cache-backed short queries: q_len >= 1 queries per sequence, the
- * suffix of the history (requires q_len <= L_b).  bf16 with q_len >= 64 and
- * no window / sink / softcap arrays runs the tiled matrix-core kernel
- * (query x key tiles with causal block-stop: each query tile stops at the
- * last key tile its last row can see).  Its P.V product runs in fp16 with
+ * suffix of the history (requires q_len <= L_b).  bf16 with q_len >= 64 runs
+ * the tiled matrix-core kernel (query x key tiles with causal block-stop:
+ * each query tile stops at the last key tile its last row can see, and with
+ * a window it also skips the key tiles before its first row's window, except
+ * those holding sink keys).  Its P.V product runs in fp16 with
  * fp32 accumulation, so it requires |V| <= 65504 (validation mode checks
  * this and returns ATLAS_ERR_RANGE).  Every other case runs the split-KV
  * kernels of atlas_attend_decode with each (query, q-head) pair as a row.

@@ -54,6 +54,39 @@ def test_tiled_prefill_small(case):
     H.check_against_oracle(inp, out, lse, what=str(case))
 
 
+def wlv(*, hq, hkv, d, page, q_len, lens, window, sinks, softcap, seed=23):
+    w = wl(hq=hq, hkv=hkv, d=d, page=page, q_len=q_len, lens=lens, seed=seed)
+    w.window = np.asarray(window, np.int32)
+    w.sinks = np.asarray(sinks, np.int32)
+    w.softcap = np.asarray(softcap, np.float32)
+    return w
+
+
+VARIANT_CASES = [
+    # (hq, hkv, d, page, q_len, lens, window, sinks, softcap)
+    (4, 1, 128, 16, 200, (700, 300), (64, 0), (4, 0), (0.0, 0.0)),         # window + sinks / plain
+    (8, 2, 128, 32, 130, (900,), (1,), (0,), (0.0,)),                       # W = 1: own row only
+    (8, 2, 128, 32, 130, (900,), (1,), (3,), (2.0,)),                       # W = 1 + 3 sinks + cap 2
+    (8, 2, 64, 64, 300, (5000, 300), (100, 4096), (70, 4), (5.0, 0.0)),     # sinks span two blocks; W > ctx
+    (2, 2, 128, 128, 257, (3000,), (0,), (0,), (1.5,)),                     # softcap only
+    (32, 8, 128, 128, 512, (8192,), (4096,), (4,), (50.0,)),                # the mixed-decode variants on a long prefill
+]
+
+
+@pytest.mark.parametrize("case", VARIANT_CASES, ids=lambda c: f"h{c[0]}x{c[1]}-d{c[2]}-q{c[4]}-w{c[6][0]}")
+def test_tiled_prefill_variants(case):
+    """Window, sinks and softcap on the tiled path: key blocks before a
+    query block's window are skipped, partially visible ones masked."""
+    hq, hkv, d, page, q_len, lens, window, sinks, softcap = case
+    w = wlv(hq=hq, hkv=hkv, d=d, page=page, q_len=q_len, lens=lens, window=window, sinks=sinks,
+            softcap=softcap)
+    say(f"[prefill-tiled variants] {case}")
+    inp = H.build(w)
+    out, lse = H.run(inp, entry="prefill")
+    torch.cuda.synchronize()
+    H.check_against_oracle(inp, out, lse, what=str(case))
+
+
 def test_tiled_prefill_uneven_head_map():
     hm = [0, 1, 1, 0, 1]
     w = wl(hq=5, hkv=2, d=128, page=32, q_len=90, lens=(90, 150))
