@@ -19,7 +19,8 @@ decode is run once more with its cold pages generated inside the attention
 kernel (atlas_attend_decode_regen) instead of regenerated into scratch
 ("next": "fused_regen_decode"; its output is compared bit for bit with the
 step's); the K/V append of a decode step and of a whole prefill history is
-timed under "next": "append_kv".
+timed under "next": "append_kv", and the prefill shape with a window, sinks
+and a softcap under "next": "prefill_variants".
 
 Prints one JSON line.  `--gpus N` with N > 1 exits: this path runs on one GPU.
 """
@@ -186,6 +187,29 @@ def fused_report(torch, np, d, atlas, dec_ms, regen_ms, calls=30):
             "generated_values": n_cold * per_page // 4,
             "bitwise_equal_to_unfused": bool(torch.equal(out, ref)),
             "note": "atlas_attend_decode_regen: cold pages (page-table -1) generated in the fold's registers"}
+
+
+def prefill_variants_report(torch, np, p, atlas, calls=10):
+    """The causal-prefill shape (S=8192, Hq=32, Hkv=8, D=128, bf16) with the
+    mixed-decode workload's variants on the tiled kernel: window 4096, 4 sink
+    keys, softcap 50.  Throughput counts the visible (query, key) pairs only:
+    key blocks before a query block's window are skipped."""
+    pw = p["w"]
+    S, hq, d = pw.q_len, pw.hq, pw.head_dim
+    W, n_s, capv = 4096, 4, 50.0
+    win = torch.full((1,), W, dtype=torch.int32, device="cuda")
+    snk = torch.full((1,), n_s, dtype=torch.int32, device="cuda")
+    cap = torch.full((1,), capv, dtype=torch.float32, device="cuda")
+    out = torch.empty(1, S, hq, d, dtype=torch.float32, device="cuda")
+    call = lambda: atlas.atlas_attend_prefill(p["q"], p["k"], p["v"], p["pt"], p["ctx"], pw.scale, window=win,
+                                              sink_tokens=snk, softcap=cap, out=out)
+    us = _median_call_us(torch, np, call, calls=calls)
+    pos = np.arange(S, dtype=np.int64)
+    vis = np.minimum(pos + 1, W) + np.minimum(n_s, np.maximum(pos + 1 - W, 0))
+    flops = 4.0 * d * hq * float(vis.sum())
+    return {"us": round(us, 1), "flop": flops, "TFLOPs": round(flops / us / 1e6, 1),
+            "frac_mfma": round(flops / us / 1e6 / BF16_PEAK_TFLOPS, 4),
+            "note": "window 4096 + 4 sinks + softcap 50 on the causal-prefill shape; visible pairs only"}
 
 
 def append_report(torch, np, workloads, atlas):
@@ -462,6 +486,8 @@ def main():
     if not args.no_workloads:
         result["next"] = {"fused_regen_decode": fused_report(torch, np, d, atlas, dec_ms, regen_ms),
                           "append_kv": append_report(torch, np, workloads, atlas)}
+        if p is not None:
+            result["next"]["prefill_variants"] = prefill_variants_report(torch, np, p, atlas)
         print("bench: fused regeneration timed", file=sys.stderr, flush=True)
     if not args.no_workloads:
         # Every synthetic workload's throughput (the long-context decode and
