@@ -50,6 +50,17 @@ __device__ __forceinline__ float group_max(float x)
 // Hardware 2^x (v_exp_f32): exact 0 for -inf.
 __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
 
+// c * tanh(x * k) from one hardware exponential and one reciprocal, through
+// tanh(y) = 1 - 2 / (e^(2y) + 1) with the constants folded:
+// c - 2c / (2^(x * 2k log2 e) + 1).  Saturates to +-c (2^+big = inf, rcp(inf)
+// = 0).  Absolute error of the tanh factor below 1e-6 (two hardware ops of
+// about one ulp each on a value in (0, 1), plus two roundings).
+__device__ __forceinline__ float scaled_tanh_fast(float x, float k2log2e, float c, float neg2c)
+{
+    const float e = __builtin_amdgcn_exp2f(x * k2log2e);
+    return fmaf(neg2c, __builtin_amdgcn_rcpf(e + 1.0f), c);
+}
+
 __device__ __forceinline__ float bf16_lo(uint32_t pair) { return __uint_as_float(pair << 16); }
 __device__ __forceinline__ float bf16_hi(uint32_t pair) { return __uint_as_float(pair & 0xFFFF0000u); }
 

@@ -274,13 +274,14 @@ __global__ __launch_bounds__(512) void prefill_kernel(PrefillArgs a)
 
         // Softcap (before the mask): s' = cap tanh(s scale / cap), kept in the
         // units of the raw product so that the scale below still applies.
+        // The hardware-exponential tanh keeps the logit error under cap * 1e-6.
         if (cap > 0.0f) {
-            const float inv = a.scale / cap, back = cap / a.scale;
+            const float k2 = 2.0f * 1.4426950408889634f * a.scale / cap, back = cap / a.scale;
 #pragma unroll
             for (int t = 0; t < 2; ++t)
 #pragma unroll
                 for (int e = 0; e < 16; ++e)
-                    st[t][e] = back * tanhf(st[t][e] * inv);
+                    st[t][e] = scaled_tanh_fast(st[t][e], k2, back, -2.0f * back);
         }
         // Mask only blocks some row does not see whole: past the first row's
         // position (causal), or not inside every row's window or sink range.
