@@ -67,7 +67,7 @@ bool mul_ok(int64_t a, int64_t b, int64_t *out)
     return true;
 }
 
-enum class Path { SplitValu, SplitMfma, TiledPrefill };
+enum class Path { SplitValu, SplitMfma, TiledPrefill, TiledSplit };
 
 // Everything derived from the arguments before launching.
 struct Plan {
@@ -164,17 +164,19 @@ int32_t check_shapes(const atlas_attn_args *a, bool decode, Plan *p)
     p->max_context = (int)max_ctx;
     p->rows_total = rows;
 
-    // Path: the tiled kernel for long bf16 prefills (window / sinks / softcap
-    // included); else the split-KV kernels (matrix cores for bf16, vector ALUs
-    // for fp32).
+    // Path: the tiled kernels for long prefills (window / sinks / softcap
+    // included; fp32 on split fp16 operands); else the split-KV kernels
+    // (matrix cores for bf16, vector ALUs for fp32).
     if (!decode && a->dtype == ATLAS_DTYPE_BF16 && a->q_len >= 64)
         p->path = Path::TiledPrefill;
+    else if (!decode && a->dtype == ATLAS_DTYPE_F32 && a->q_len >= 64)
+        p->path = Path::TiledSplit;
     else if (a->dtype == ATLAS_DTYPE_BF16)
         p->path = Path::SplitMfma;
     else
         p->path = Path::SplitValu;
 
-    if (p->path == Path::TiledPrefill) {
+    if (p->path == Path::TiledPrefill || p->path == Path::TiledSplit) {
         p->workspace = kWorkspaceHeader;
         return ok();
     }
@@ -286,7 +288,7 @@ int32_t validate_device(const atlas_attn_args *a, const Plan &p, hipStream_t str
     s.num_phys = a->num_phys_pages;
     s.max_pages = a->max_pages_per_seq;
     s.max_context = p.max_context;
-    s.check_v_f16 = p.path == Path::TiledPrefill ? 1 : 0;
+    s.check_f16 = p.path == Path::TiledPrefill ? 1 : (p.path == Path::TiledSplit ? 2 : 0);
     int flag = 0;
     e = hipMemsetAsync(s.flag, 0, sizeof(int), stream);
     if (e == hipSuccess)
@@ -300,7 +302,11 @@ int32_t validate_device(const atlas_attn_args *a, const Plan &p, hipStream_t str
     if (flag & 1)
         return fail(ATLAS_ERR_NONFINITE, "NaN or Inf in q or in the K/V rows the contexts cover");
     if (flag & 2)
-        return fail(ATLAS_ERR_RANGE, "a V value exceeds 65504, the fp16 range of the tiled prefill's P.V product");
+        return fail(ATLAS_ERR_RANGE, p.path == Path::TiledSplit
+                                         ? "a Q, K or V value exceeds 65504, the fp16 range of the fp32 tiled "
+                                           "prefill's split operands"
+                                         : "a V value exceeds 65504, the fp16 range of the tiled prefill's P.V "
+                                           "product");
     return ok();
 }
 
@@ -334,7 +340,7 @@ int32_t attend(const atlas_attn_args *a, void *stream_ptr, bool decode, const Re
             return st;
     }
 
-    if (p.path == Path::TiledPrefill) {
+    if (p.path == Path::TiledPrefill || p.path == Path::TiledSplit) {
         atlas::PrefillArgs k{};
         k.q = a->q;
         k.k_pages = a->k_pages;
@@ -357,7 +363,8 @@ int32_t attend(const atlas_attn_args *a, void *stream_ptr, bool decode, const Re
         k.max_context = p.max_context;
         k.scale = a->scale;
         k.groups = p.groups;
-        hipError_t e = atlas::launch_prefill_mfma(k, stream);
+        hipError_t e = p.path == Path::TiledPrefill ? atlas::launch_prefill_mfma(k, stream)
+                                                     : atlas::launch_prefill_split(k, stream);
         if (e == hipErrorNotSupported)
             return fail(ATLAS_ERR_UNSUPPORTED, "no tiled prefill kernel for this shape");
         if (e != hipSuccess)

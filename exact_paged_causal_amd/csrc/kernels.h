@@ -97,7 +97,8 @@ struct PrefillArgs {
     HeadGroups groups;
 };
 
-hipError_t launch_prefill_mfma(const PrefillArgs &a, hipStream_t stream);
+hipError_t launch_prefill_mfma(const PrefillArgs &a, hipStream_t stream);   // bf16 Q/K/V
+hipError_t launch_prefill_split(const PrefillArgs &a, hipStream_t stream);  // fp32 Q/K/V, split fp16 operands
 
 // Validation-mode NaN/Inf scan of q and the K/V rows each context covers.
 struct ScanArgs {
@@ -106,9 +107,10 @@ struct ScanArgs {
     const void *v_pages;
     const int32_t *page_table;
     const int32_t *context_lens;
-    int *flag;                  // bit 0: NaN/Inf; bit 1: |V| beyond fp16 range (cleared by the caller)
+    int *flag;                  // bit 0: NaN/Inf; bit 1: beyond the fp16 range (cleared by the caller)
     int32_t batch, q_len, hq, hkv, head_dim, page_shift, num_phys, max_pages, max_context;
-    int32_t check_v_f16;        // also flag |V| > 65504 (the tiled prefill's fp16 P.V product)
+    int32_t check_f16;          // flag values beyond 65504: 1 = V (the bf16 tiled prefill's fp16 P.V
+                                // product), 2 = Q, K and V (the fp32 tiled prefill's split operands)
 };
 
 hipError_t launch_scan(const ScanArgs &a, int dtype, hipStream_t stream);

@@ -1,0 +1,518 @@
+// prefill_split.hip -- tiled causal prefill for fp32 Q/K/V on the gfx950
+// fp16 matrix cores, with every operand split into two fp16 parts.
+//
+// CPUAttn README: the method is defined on FP32 tensors, and its parallel
+// lowering is the fused QK -> RowNorm -> PV tile pipeline whose causal mask
+// stops each query block at its last reachable key block.  The fp32 matrix
+// instructions of gfx950 run at one sixteenth of the fp16 rate, so this
+// kernel keeps fp32 accuracy on the fp16 ones instead:
+//
+//   split      = an fp32 value x is carried as hi = fp16(x) and
+//                lo = fp16(x - hi) (the subtraction is exact in fp32), so
+//                hi + lo equals x to about 2^-22 relative, or to 2^-25
+//                absolute where lo falls into the fp16 subnormal range;
+//   range      = so that this absolute floor is negligible against the
+//                row's own scale, every Q row and every K row is first
+//                multiplied by the power of two that brings its largest
+//                magnitude into [2^14, 2^15) (exact); the Q factor folds into
+//                the row's exponent constant, the K factors (kept in LDS) are
+//                applied to the 32 scores of each lane after the QK product.
+//                V and P need no scaling: their floor is absolute and far
+//                below the bar after the softmax weighting;
+//   products   = x y is taken as hi_x hi_y + lo_x hi_y + hi_x lo_y on
+//                v_mfma_f32_32x32x16_f16 (fp16 products are exact in the
+//                fp32 accumulator; the dropped lo_x lo_y is below 2^-22 |x y|):
+//                S^T = K Q^T with Q split once into registers and K split
+//                while it is staged into LDS; P = 2^(s log2(e) scale - m) is
+//                computed in fp32, summed in fp32 for the denominator and
+//                split for O^T += V^T P^T, with V split while it is staged;
+//   tiles      = as in the bf16 kernel: 256 rows (query position x q-head of
+//                one K/V head) per 512-thread workgroup, 32 rows per wave,
+//                64-key blocks, causal block-stop, window blocks skipped,
+//                lazy rescaling (the reference max may lag by up to 2^8),
+//                one LDS double buffer and one barrier per block, page ids
+//                staged in LDS, heavy-first XCD-grouped grid;
+//   softcap    = library tanhf (the hardware-exponential tanh of the bf16
+//                kernel is too coarse for the fp32 bar).
+//
+// Precondition: |q|, |k|, |v| <= 65504 (fp16 range of the hi parts);
+// validation mode checks it.
+#include "device.h"
+#include "kernels.h"
+
+namespace atlas {
+namespace {
+
+typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
+typedef _Float16 f16x2 __attribute__((ext_vector_type(2)));
+typedef float f32x2 __attribute__((ext_vector_type(2)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef short i16x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) i16x4 lds_i16x4;
+
+constexpr int kWaves = 8;
+constexpr int kRows = 32 * kWaves;     // rows per workgroup
+constexpr int kBN = 64;                // keys per block
+constexpr int kPad = 24;               // row padding (elements): a 16-byte-odd row stride
+constexpr float kRescaleSlack = 8.0f;  // log2 units the running max may lag
+constexpr int kPidWindow = 1024;       // page ids staged in LDS at a time
+
+template <int D>
+struct alignas(16) SplitSmem {
+    alignas(16) uint16_t kh[2][kBN][D + kPad];  // fp16 bits of the K hi parts
+    alignas(16) uint16_t kl[2][kBN][D + kPad];  // K lo parts
+    alignas(16) uint16_t vh[2][kBN][D + kPad];  // V hi parts
+    alignas(16) uint16_t vl[2][kBN][D + kPad];  // V lo parts
+    alignas(16) float kscale[2][kBN];           // 2^-shift of each staged K row
+    alignas(16) int32_t pid[kPidWindow];        // physical ids of pages [pid_base, pid_base + kPidWindow)
+};
+
+// Power-of-two shift that brings a largest magnitude m into [2^14, 2^15)
+// (0 for m = 0; clamped so that 2^+-shift stays a normal fp32 number).
+__device__ __forceinline__ int range_shift(float m)
+{
+    int e;
+    frexpf(m, &e);  // m = f 2^e, f in [0.5, 1)
+    const int s = 15 - e;
+    return m > 0.0f ? (s < -100 ? -100 : (s > 100 ? 100 : s)) : 0;
+}
+
+__device__ __forceinline__ uint32_t f16bits2(f16x2 h) { return __builtin_bit_cast(uint32_t, h); }
+
+struct HiLo {
+    uint32_t hi, lo;
+};
+
+// Two fp32 values -> (hi pair, lo pair) of fp16 bits.
+__device__ __forceinline__ HiLo split2(float x0, float x1)
+{
+    const f16x2 h = __builtin_convertvector(f32x2{x0, x1}, f16x2);
+    const f32x2 hf = __builtin_convertvector(h, f32x2);
+    return {f16bits2(h), f16bits2(__builtin_convertvector(f32x2{x0 - hf[0], x1 - hf[1]}, f16x2))};
+}
+
+template <int D>
+__global__ __launch_bounds__(512) void prefill_split_kernel(PrefillArgs a)
+{
+    constexpr int KS = D / 16;            // k-steps of the QK product
+    constexpr int DT = D / 32;            // 32-dim tiles of the output
+    constexpr int CPR = D / 4;            // 16-byte chunks (4 floats) per K/V row
+    constexpr int CH = kBN * CPR / 512;   // chunks per thread per tile: 4 (D=128) or 2 (D=64)
+    __shared__ SplitSmem<D> sm;
+
+    const int tid = threadIdx.x;
+    const int wave = tid >> 6;
+    const int lane = tid & 63;
+    const int half = lane >> 5;
+
+    // Heavy-first workgroup order; consecutive ids cycle over (b, K/V head).
+    const int per_q = a.batch * a.hkv;
+    const int qb_rev = blockIdx.x / per_q;
+    const int rem = blockIdx.x - qb_rev * per_q;
+    const int b = rem / a.hkv;
+    const int g = rem - b * a.hkv;
+    const int qblock = a.n_qblocks - 1 - qb_rev;
+    const int G = a.groups.max_group;
+    const int npos = kRows / G;
+    const int gstart = a.groups.start[g];
+    const int gsize = a.groups.start[g + 1] - gstart;
+
+    int ctx = a.context_lens[b];
+    ctx = ctx < 0 ? 0 : (ctx > a.max_context ? a.max_context : ctx);
+    const int i0 = qblock * npos;
+    const int i1 = i0 + npos < a.q_len ? i0 + npos : a.q_len;
+    const int pos_lo = ctx - a.q_len + i0;
+    const int pos_hi = ctx - a.q_len + i1 - 1;
+    const int W = a.window ? a.window[b] : 0;
+    const int S = (a.sinks && W > 0) ? a.sinks[b] : 0;
+    const float cap = a.softcap ? a.softcap[b] : 0.0f;
+
+    // This lane's row.
+    const int r = wave * 32 + (lane & 31);
+    const int ri = r / G;
+    const int rj = r - ri * G;
+    const int qi = i0 + ri;
+    const bool row_ok = ri < npos && qi < i1 && rj < gsize;
+    const int pos = row_ok ? ctx - a.q_len + qi : -1;
+    const int h = row_ok ? a.groups.list[gstart + rj] : 0;
+
+    // Q^T as the B operand, range-scaled and split: dims 16s + 8 half .. +7
+    // of this lane's row (the other lane half holds the rest of the row).
+    f16x8 qh[KS], ql[KS];
+    float row_factor;  // 2^-shift of this row's Q scaling
+    {
+        const float *qrow = reinterpret_cast<const float *>(a.q) +
+                            (((int64_t)b * a.q_len + (row_ok ? qi : 0)) * a.hq + h) * D;
+        f32x4 x[2 * KS];
+        float mx = 0.0f;
+#pragma unroll
+        for (int s = 0; s < 2 * KS; ++s) {
+            x[s] = row_ok ? *reinterpret_cast<const f32x4 *>(qrow + 16 * (s >> 1) + 8 * half + 4 * (s & 1))
+                          : f32x4{0.0f, 0.0f, 0.0f, 0.0f};
+            mx = fmaxf(mx, fmaxf(fmaxf(fabsf(x[s][0]), fabsf(x[s][1])), fmaxf(fabsf(x[s][2]), fabsf(x[s][3]))));
+        }
+        mx = fmaxf(mx, __shfl_xor(mx, 32));
+        const int sh = range_shift(mx);
+        row_factor = ldexpf(1.0f, -sh);
+#pragma unroll
+        for (int s = 0; s < KS; ++s) {
+            const f32x4 x0 = x[2 * s], x1 = x[2 * s + 1];
+            const HiLo a0 = split2(ldexpf(x0[0], sh), ldexpf(x0[1], sh));
+            const HiLo a1 = split2(ldexpf(x0[2], sh), ldexpf(x0[3], sh));
+            const HiLo a2 = split2(ldexpf(x1[0], sh), ldexpf(x1[1], sh));
+            const HiLo a3 = split2(ldexpf(x1[2], sh), ldexpf(x1[3], sh));
+            qh[s] = __builtin_bit_cast(f16x8, u32x4{a0.hi, a1.hi, a2.hi, a3.hi});
+            ql[s] = __builtin_bit_cast(f16x8, u32x4{a0.lo, a1.lo, a2.lo, a3.lo});
+        }
+    }
+
+    const int ps = a.page_shift;
+    const int pmask = (1 << ps) - 1;
+    const float *kpages = reinterpret_cast<const float *>(a.k_pages);
+    const float *vpages = reinterpret_cast<const float *>(a.v_pages);
+    const int32_t *ptab = a.page_table + (int64_t)b * a.max_pages;
+
+    int pid_base = 0;
+    auto stage_pids = [&](int first_page) {
+        pid_base = first_page;
+        const int last_page = pos_hi >= 0 ? pos_hi >> ps : -1;
+        for (int t = tid; t < kPidWindow && first_page + t <= last_page; t += 512) {
+            const int pid = ptab[first_page + t];
+            sm.pid[t] = ((unsigned)pid < (unsigned)a.num_phys) ? pid : 0;
+        }
+    };
+
+    // Global -> registers for key block kb (zeros past the last visible key):
+    // thread t stages CH adjacent 16-byte pieces of one K row (then, in a
+    // second phase, of the same V row).  K is fetched at the top of an
+    // iteration and stashed after the QK products; V is fetched then and
+    // stashed at the end, so only one tensor's staging registers are live.
+    const int srow = (tid * CH) / CPR;
+    const int scol = (tid * CH) - srow * CPR;
+    f32x4 reg[CH];
+    auto fetch = [&](const float *pages, int kb) {
+        const int j = kb * kBN + srow;
+        if (j <= pos_hi) {
+            const int pid = sm.pid[(j >> ps) - pid_base];
+            const int64_t off = ((((int64_t)pid * a.hkv + g) << ps) + (j & pmask)) * D + scol * 4;
+#pragma unroll
+            for (int u = 0; u < CH; ++u)
+                reg[u] = *reinterpret_cast<const f32x4 *>(pages + off + 4 * u);
+        } else {
+#pragma unroll
+            for (int u = 0; u < CH; ++u)
+                reg[u] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
+        }
+    };
+    // Registers -> the hi and lo rows of an LDS buffer.  K rows are first
+    // range-scaled: the eight threads of a row (aligned lanes) share its
+    // maximum, and its factor goes to kscale.
+    auto stash = [&](uint16_t (*hi)[D + kPad], uint16_t (*lo)[D + kPad], float *kscale) {
+        int sh = 0;
+        if (kscale) {
+            float mx = 0.0f;
+#pragma unroll
+            for (int u = 0; u < CH; ++u)
+                mx = fmaxf(mx, fmaxf(fmaxf(fabsf(reg[u][0]), fabsf(reg[u][1])),
+                                     fmaxf(fabsf(reg[u][2]), fabsf(reg[u][3]))));
+            sh = range_shift(group_max<8>(mx));
+            if ((tid & 7) == 0)
+                kscale[srow] = ldexpf(1.0f, -sh);
+        }
+        uint32_t hw[2 * CH], lw[2 * CH];
+#pragma unroll
+        for (int u = 0; u < CH; ++u) {
+            const HiLo x0 = split2(ldexpf(reg[u][0], sh), ldexpf(reg[u][1], sh));
+            const HiLo x1 = split2(ldexpf(reg[u][2], sh), ldexpf(reg[u][3], sh));
+            hw[2 * u] = x0.hi;
+            lw[2 * u] = x0.lo;
+            hw[2 * u + 1] = x1.hi;
+            lw[2 * u + 1] = x1.lo;
+        }
+#pragma unroll
+        for (int w4 = 0; w4 < CH / 2; ++w4) {
+            const int col = scol * 4 + 8 * w4;
+            *reinterpret_cast<u32x4 *>(&hi[srow][col]) = u32x4{hw[4 * w4], hw[4 * w4 + 1], hw[4 * w4 + 2], hw[4 * w4 + 3]};
+            *reinterpret_cast<u32x4 *>(&lo[srow][col]) = u32x4{lw[4 * w4], lw[4 * w4 + 1], lw[4 * w4 + 2], lw[4 * w4 + 3]};
+        }
+    };
+
+    // Scores leave the QK product in the row's scaled units (raw x 2^shift);
+    // the softcap brings them back to raw units.
+    const float c_log2 = cap > 0.0f ? a.scale * kLog2e : a.scale * kLog2e * row_factor;
+    float m_ref = -INFINITY;  // reference max (log2 units) the accumulator is scaled to
+    float l_part = 0.0f;      // this lane-half's share of the softmax denominator (fp32)
+    f32x16 acc[DT];
+#pragma unroll
+    for (int t = 0; t < DT; ++t)
+        acc[t] = f32x16{};
+
+#pragma unroll
+    for (int s = 0; s < KS; ++s) {
+        asm volatile("" : "+v"(qh[s]));
+        asm volatile("" : "+v"(ql[s]));
+    }
+
+    // Key blocks the rows can see (sink blocks, then the window up to the
+    // diagonal; every block up to the diagonal without a window).
+    const int kb_last = pos_hi >= 0 ? pos_hi / kBN : -1;
+    int first_win = 0, n_sink_blk = 0;
+    if (W > 0 && kb_last >= 0) {
+        const int lo_key = pos_lo - W + 1;
+        first_win = lo_key > 0 ? lo_key / kBN : 0;
+        n_sink_blk = S > 0 ? min((S + kBN - 1) / kBN, first_win) : 0;
+    }
+    const int n_iter = kb_last < 0 ? 0 : n_sink_blk + (kb_last - first_win + 1);
+    auto block_at = [&](int it) { return it < n_sink_blk ? it : first_win + (it - n_sink_blk); };
+
+    if (n_iter > 0)
+        stage_pids((block_at(0) * kBN) >> ps);
+    __syncthreads();
+    if (n_iter > 0) {
+        fetch(kpages, block_at(0));
+        stash(sm.kh[0], sm.kl[0], sm.kscale[0]);
+        fetch(vpages, block_at(0));
+        stash(sm.vh[0], sm.vl[0], nullptr);
+    }
+    __syncthreads();
+
+    for (int it = 0; it < n_iter; ++it) {
+        const int kb = block_at(it);
+        const int cur = it & 1;
+        const bool more = it + 1 < n_iter;
+        const int kb_next = more ? block_at(it + 1) : kb;
+        if (more && (((kb_next * kBN + kBN - 1) >> ps) - pid_base) >= kPidWindow) {
+            __syncthreads();
+            stage_pids((kb_next * kBN) >> ps);
+            __syncthreads();
+        }
+        if (more)
+            fetch(kpages, kb_next);
+
+        // S^T for the block: two 32-key tiles, three split products per
+        // k-step; consecutive products alternate between the two tiles.
+        __builtin_amdgcn_s_setprio(1);
+        f32x16 st[2] = {f32x16{}, f32x16{}};
+#pragma unroll
+        for (int s = 0; s < KS; ++s) {
+            f16x8 kfh[2], kfl[2];
+#pragma unroll
+            for (int t = 0; t < 2; ++t) {
+                kfh[t] = *reinterpret_cast<const f16x8 *>(&sm.kh[cur][32 * t + (lane & 31)][16 * s + 8 * half]);
+                kfl[t] = *reinterpret_cast<const f16x8 *>(&sm.kl[cur][32 * t + (lane & 31)][16 * s + 8 * half]);
+            }
+#pragma unroll
+            for (int t = 0; t < 2; ++t)
+                st[t] = __builtin_amdgcn_mfma_f32_32x32x16_f16(kfh[t], qh[s], st[t], 0, 0, 0);
+#pragma unroll
+            for (int t = 0; t < 2; ++t)
+                st[t] = __builtin_amdgcn_mfma_f32_32x32x16_f16(kfl[t], qh[s], st[t], 0, 0, 0);
+#pragma unroll
+            for (int t = 0; t < 2; ++t)
+                st[t] = __builtin_amdgcn_mfma_f32_32x32x16_f16(kfh[t], ql[s], st[t], 0, 0, 0);
+        }
+        // K operand reads one k-step (four reads) ahead of their products.
+        __builtin_amdgcn_sched_group_barrier(0x100, 4, 0);
+#pragma unroll
+        for (int i = 0; i < KS - 1; ++i) {
+#pragma unroll
+            for (int m = 0; m < 4; ++m) {
+                __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+                __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+            }
+            __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);
+        }
+        __builtin_amdgcn_sched_group_barrier(0x008, 6, 0);
+
+        __builtin_amdgcn_s_setprio(0);
+
+        // The other buffer was last read before the previous barrier.
+        if (more) {
+            stash(sm.kh[cur ^ 1], sm.kl[cur ^ 1], sm.kscale[cur ^ 1]);
+            fetch(vpages, kb_next);
+        }
+
+        // Undo the K rows' range scaling: lane half h holds keys
+        // 32t + 8g + 4h + {0..3} in elements 4g .. 4g + 3 of tile t.
+#pragma unroll
+        for (int t = 0; t < 2; ++t)
+#pragma unroll
+            for (int g4 = 0; g4 < 4; ++g4) {
+                const f32x4 f = *reinterpret_cast<const f32x4 *>(&sm.kscale[cur][32 * t + 8 * g4 + 4 * half]);
+#pragma unroll
+                for (int i = 0; i < 4; ++i)
+                    st[t][4 * g4 + i] *= f[i];
+            }
+
+        // Softcap (before the mask), from the row's scaled units to the units
+        // of the raw product.
+        if (cap > 0.0f) {
+            const float inv = row_factor * a.scale / cap, back = cap / a.scale;
+#pragma unroll
+            for (int t = 0; t < 2; ++t)
+#pragma unroll
+                for (int e = 0; e < 16; ++e)
+                    st[t][e] = back * tanhf(st[t][e] * inv);
+        }
+        // Mask only blocks some row does not see whole.
+        const int k0 = kb * kBN;
+        const bool all_causal = k0 + kBN - 1 <= pos_lo;
+        const bool all_window = W <= 0 || k0 > pos_hi - W || k0 + kBN - 1 < S;
+        if (!(all_causal && all_window)) {
+#pragma unroll
+            for (int t = 0; t < 2; ++t)
+#pragma unroll
+                for (int e = 0; e < 16; ++e) {
+                    const int j = k0 + 32 * t + 8 * (e >> 2) + 4 * half + (e & 3);
+                    const bool vis = j <= pos && (W <= 0 || j > pos - W || j < S);
+                    if (!vis)
+                        st[t][e] = -INFINITY;
+                }
+        }
+
+        // Online softmax (lane = one row, two lane halves share it).
+        float mx = st[0][0];
+#pragma unroll
+        for (int t = 0; t < 2; ++t)
+#pragma unroll
+            for (int e = 0; e < 16; ++e)
+                mx = fmaxf(mx, st[t][e]);
+        mx = fmaxf(mx, __shfl_xor(mx, 32));
+        const float m_blk = mx * c_log2;
+        if (m_blk > m_ref + kRescaleSlack) {
+            const float alpha = fast_exp2(m_ref - m_blk);
+            l_part *= alpha;
+#pragma unroll
+            for (int t = 0; t < DT; ++t)
+                acc[t] *= alpha;
+            m_ref = m_blk;
+        }
+        const float msafe = m_ref == -INFINITY ? 0.0f : m_ref;
+
+        // P^T as split B operands: tile t, k-step ks -> elements 8ks..8ks+7.
+        uint32_t ph[2][2][4], pl[2][2][4];
+#pragma unroll
+        for (int t = 0; t < 2; ++t) {
+#pragma unroll
+            for (int e = 0; e < 16; e += 2) {
+                const float p0 = fast_exp2(fmaf(st[t][e], c_log2, -msafe));
+                const float p1 = fast_exp2(fmaf(st[t][e + 1], c_log2, -msafe));
+                l_part += p0 + p1;
+                const HiLo pp = split2(p0, p1);
+                ph[t][e >> 3][(e & 7) >> 1] = pp.hi;
+                pl[t][e >> 3][(e & 7) >> 1] = pp.lo;
+            }
+        }
+
+        // O^T += V^T P^T, split: per pair of output tiles, hi.hi, lo.hi and
+        // hi.lo products alternating between the two accumulators.  V^T via
+        // transposed LDS reads: lane 16q+j loads V[key0 + j/4][d0 + 4(j%4) .. +3]
+        // and receives V[key0 + k][d0 + j] (k=0..3).
+        const int q16 = lane >> 4;
+        const int j16 = lane & 15;
+        __builtin_amdgcn_s_setprio(1);
+#pragma unroll
+        for (int t = 0; t < 2; ++t) {
+#pragma unroll
+            for (int ks = 0; ks < 2; ++ks) {
+                const f16x8 pbh = __builtin_bit_cast(f16x8, u32x4{ph[t][ks][0], ph[t][ks][1], ph[t][ks][2], ph[t][ks][3]});
+                const f16x8 pbl = __builtin_bit_cast(f16x8, u32x4{pl[t][ks][0], pl[t][ks][1], pl[t][ks][2], pl[t][ks][3]});
+                const int key0 = 32 * t + 16 * ks + 4 * half + (j16 >> 2);
+#pragma unroll
+                for (int dp = 0; dp < DT; dp += 2) {
+                    f16x8 vah[2], val[2];
+#pragma unroll
+                    for (int u = 0; u < 2; ++u) {
+                        const int dim0 = 32 * (dp + u) + 16 * (q16 & 1) + 4 * (j16 & 3);
+                        const i16x4 h0 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4 *)(&sm.vh[cur][key0][dim0]));
+                        const i16x4 h1 =
+                            __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4 *)(&sm.vh[cur][key0 + 8][dim0]));
+                        const i16x4 l0 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4 *)(&sm.vl[cur][key0][dim0]));
+                        const i16x4 l1 =
+                            __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4 *)(&sm.vl[cur][key0 + 8][dim0]));
+                        // Whole-vector concatenation (element-wise extraction
+                        // of these reads is mis-compiled by this toolchain).
+                        vah[u] = __builtin_bit_cast(f16x8, __builtin_shufflevector(h0, h1, 0, 1, 2, 3, 4, 5, 6, 7));
+                        val[u] = __builtin_bit_cast(f16x8, __builtin_shufflevector(l0, l1, 0, 1, 2, 3, 4, 5, 6, 7));
+                    }
+#pragma unroll
+                    for (int u = 0; u < 2; ++u)
+                        acc[dp + u] = __builtin_amdgcn_mfma_f32_32x32x16_f16(vah[u], pbh, acc[dp + u], 0, 0, 0);
+#pragma unroll
+                    for (int u = 0; u < 2; ++u)
+                        acc[dp + u] = __builtin_amdgcn_mfma_f32_32x32x16_f16(val[u], pbh, acc[dp + u], 0, 0, 0);
+#pragma unroll
+                    for (int u = 0; u < 2; ++u)
+                        acc[dp + u] = __builtin_amdgcn_mfma_f32_32x32x16_f16(vah[u], pbl, acc[dp + u], 0, 0, 0);
+                }
+            }
+        }
+        // Each group of six products (one pair of output tiles) has its eight
+        // transposed reads issued during the previous group.
+        constexpr int kGroups = 4 * (DT / 2);
+        __builtin_amdgcn_sched_group_barrier(0x100, 8, 0);
+#pragma unroll
+        for (int i = 0; i < kGroups - 1; ++i) {
+#pragma unroll
+            for (int m = 0; m < 2; ++m) {
+                __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+                __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
+                __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+                __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+                __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+                __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+            }
+        }
+        __builtin_amdgcn_sched_group_barrier(0x008, 6, 0);
+
+        __builtin_amdgcn_s_setprio(0);
+
+        if (more)
+            stash(sm.vh[cur ^ 1], sm.vl[cur ^ 1], nullptr);
+        __syncthreads();
+    }
+
+    // Epilogue: O = O^T / l, lse = (m + log2 l) ln 2.
+    const float l_row = l_part + __shfl_xor(l_part, 32);
+    if (!row_ok)
+        return;
+    float *orow = a.out + (((int64_t)b * a.q_len + qi) * a.hq + h) * D;
+    const bool any = l_row > 0.0f;
+    const float inv = any ? 1.0f / l_row : __builtin_nanf("");
+#pragma unroll
+    for (int dt = 0; dt < DT; ++dt)
+#pragma unroll
+        for (int e4 = 0; e4 < 4; ++e4) {
+            const f32x4 o = {acc[dt][4 * e4 + 0] * inv, acc[dt][4 * e4 + 1] * inv,
+                             acc[dt][4 * e4 + 2] * inv, acc[dt][4 * e4 + 3] * inv};
+            __builtin_nontemporal_store(o, reinterpret_cast<f32x4 *>(orow + 32 * dt + 8 * e4 + 4 * half));
+        }
+    if (a.lse && half == 0)
+        __builtin_nontemporal_store(any ? (m_ref + log2f(l_row)) * kLn2 : -INFINITY,
+                                    a.lse + ((int64_t)b * a.q_len + qi) * a.hq + h);
+}
+
+}  // namespace
+
+hipError_t launch_prefill_split(const PrefillArgs &a, hipStream_t stream)
+{
+    if (a.head_dim != 64 && a.head_dim != 128)
+        return hipErrorNotSupported;
+    if (a.groups.max_group < 1 || a.groups.max_group > kRows)
+        return hipErrorNotSupported;
+    const int npos = kRows / a.groups.max_group;
+    PrefillArgs k = a;
+    k.n_qblocks = (a.q_len + npos - 1) / npos;
+    const int64_t blocks = (int64_t)k.n_qblocks * a.batch * a.hkv;
+    if (blocks > 0x7FFFFFFF)
+        return hipErrorInvalidValue;
+    if (a.head_dim == 64)
+        hipLaunchKernelGGL(prefill_split_kernel<64>, dim3((unsigned)blocks), dim3(512), 0, stream, k);
+    else
+        hipLaunchKernelGGL(prefill_split_kernel<128>, dim3((unsigned)blocks), dim3(512), 0, stream, k);
+    return hipGetLastError();
+}
+
+}  // namespace atlas

@@ -4,9 +4,10 @@
 // inputs before they reach the cache.  In validation mode the C ABI runs this
 // scan first: every query element, and every K/V element of the rows each
 // sequence's context covers (rows past the context are never read and are
-// not scanned).  For the tiled bf16 prefill it also flags V values outside
-// the fp16 range its P.V product uses.  Hits set bits of a flag word, which
-// the host reads back.
+// not scanned).  For the tiled prefills it also flags values outside the
+// fp16 range their matrix products use: V for the bf16 kernel (its P.V
+// product), Q, K and V for the fp32 kernel (split into fp16 parts).  Hits set
+// bits of a flag word, which the host reads back.
 #include "device.h"
 #include "kernels.h"
 
@@ -56,8 +57,10 @@ __global__ __launch_bounds__(256) void scan_kernel(ScanArgs a)
     if (lp == a.max_pages) {
         const int64_t n = (int64_t)a.q_len * a.hq * a.head_dim;
         const E *q = reinterpret_cast<const E *>(a.q) + (int64_t)b * n;
-        for (int64_t i = threadIdx.x; i < n; i += 256)
+        for (int64_t i = threadIdx.x; i < n; i += 256) {
             bad |= !finite_elem<E>(q[i]);
+            wide |= a.check_f16 == 2 && beyond_f16<E>(q[i]);
+        }
     } else {
         const int P = 1 << a.page_shift;
         const int rows = ctx - lp * P < P ? ctx - lp * P : P;
@@ -70,10 +73,12 @@ __global__ __launch_bounds__(256) void scan_kernel(ScanArgs a)
                     const int64_t h = i / ((int64_t)rows * a.head_dim);
                     const int64_t rest = i - h * rows * a.head_dim;
                     const int64_t off = ((int64_t)pid * a.hkv + h) * per_head + rest;
+                    const E kk = reinterpret_cast<const E *>(a.k_pages)[off];
                     const E vv = reinterpret_cast<const E *>(a.v_pages)[off];
-                    bad |= !finite_elem<E>(reinterpret_cast<const E *>(a.k_pages)[off]);
+                    bad |= !finite_elem<E>(kk);
                     bad |= !finite_elem<E>(vv);
-                    wide |= a.check_v_f16 && beyond_f16<E>(vv);
+                    wide |= a.check_f16 != 0 && beyond_f16<E>(vv);
+                    wide |= a.check_f16 == 2 && beyond_f16<E>(kk);
                 }
             }
         }

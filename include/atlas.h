@@ -188,8 +188,13 @@ int32_t atlas_attend_decode(const atlas_attn_args *args, void *stream);
  * a window it also skips the key tiles before its first row's window, except
  * those holding sink keys).  Its P.V product runs in fp16 with
  * fp32 accumulation, so it requires |V| <= 65504 (validation mode checks
- * this and returns ATLAS_ERR_RANGE).  Every other case runs the split-KV
- * kernels of atlas_attend_decode with each (query, q-head) pair as a row.
+ * this and returns ATLAS_ERR_RANGE).  fp32 with q_len >= 64 runs the same
+ * tiling on the fp16 matrix cores with every operand split into two fp16
+ * parts (hi = fp16(x), lo = fp16(x - hi)) and each product taken as
+ * hi.hi + lo.hi + hi.lo, which keeps fp32 accuracy (CPUAttn defines the
+ * method on FP32 tensors); it requires |q|, |k|, |v| <= 65504 (validation
+ * mode: ATLAS_ERR_RANGE).  Every other case runs the split-KV kernels of
+ * atlas_attend_decode with each (query, q-head) pair as a row.
  */
 int32_t atlas_attend_prefill(const atlas_attn_args *args, void *stream);
 
