@@ -19,8 +19,10 @@ decode is run once more with its cold pages generated inside the attention
 kernel (atlas_attend_decode_regen) instead of regenerated into scratch
 ("next": "fused_regen_decode"; its output is compared bit for bit with the
 step's); the K/V append of a decode step and of a whole prefill history is
-timed under "next": "append_kv", and the prefill shape with a window, sinks
-and a softcap under "next": "prefill_variants".
+timed under "next": "append_kv", the prefill shape with a window, sinks
+and a softcap under "next": "prefill_variants", and the same shape with
+fp32 Q/K/V (split fp16 operands on the matrix cores) under
+"next": "prefill_f32".
 
 Prints one JSON line.  `--gpus N` with N > 1 exits: this path runs on one GPU.
 """
@@ -210,6 +212,29 @@ def prefill_variants_report(torch, np, p, atlas, calls=10):
     return {"us": round(us, 1), "flop": flops, "TFLOPs": round(flops / us / 1e6, 1),
             "frac_mfma": round(flops / us / 1e6 / BF16_PEAK_TFLOPS, 4),
             "note": "window 4096 + 4 sinks + softcap 50 on the causal-prefill shape; visible pairs only"}
+
+
+def prefill_f32_report(torch, np, workloads, atlas, calls=10):
+    """The causal-prefill shape (S=8192, Hq=32, Hkv=8, D=128, pages of 128)
+    with fp32 Q/K/V: the tiled kernel on split fp16 operands.  TFLOP/s counts
+    the method's 4 D flop per (q-head, visible pair); each of its products
+    issues three fp16 matrix products, so the matrix cores run 3x that."""
+    w = workloads.make("causal_prefill", dtype="f32")
+    lay = workloads.page_layout(w)
+    k, v = _arena(torch, workloads, np, w, lay)
+    q = workloads.randn(workloads.query_shape(w), seed=w.seed * 100 + 1, dtype="f32", device="cuda")
+    pt = torch.from_numpy(lay.page_table).cuda()
+    ctx = torch.from_numpy(w.context_lens).cuda()
+    out = torch.empty(workloads.query_shape(w), dtype=torch.float32, device="cuda")
+    lse = torch.empty(w.batch, w.q_len, w.hq, dtype=torch.float32, device="cuda")
+    call = lambda: atlas.atlas_attend_prefill(q, k, v, pt, ctx, w.scale, out=out, lse=lse)
+    us = _median_call_us(torch, np, call, calls=calls)
+    S = w.q_len
+    flops = 4.0 * w.head_dim * w.hq * S * (S + 1) / 2
+    tf = flops / us / 1e6
+    return {"us": round(us, 1), "flop": flops, "TFLOPs": round(tf, 1),
+            "frac_mfma_fp16": round(3.0 * tf / BF16_PEAK_TFLOPS, 4),
+            "note": "fp32 Q/K/V; every product as three fp16 matrix products (hi.hi + lo.hi + hi.lo)"}
 
 
 def append_report(torch, np, workloads, atlas):
@@ -488,6 +513,7 @@ def main():
                           "append_kv": append_report(torch, np, workloads, atlas)}
         if p is not None:
             result["next"]["prefill_variants"] = prefill_variants_report(torch, np, p, atlas)
+            result["next"]["prefill_f32"] = prefill_f32_report(torch, np, workloads, atlas)
         print("bench: fused regeneration timed", file=sys.stderr, flush=True)
     if not args.no_workloads:
         # Every synthetic workload's throughput (the long-context decode and
