@@ -54,6 +54,13 @@ def _load():
                                           ctypes.c_uint32, ctypes.c_uint32, ctypes.c_int64,
                                           ctypes.c_int64, ctypes.c_int, ctypes.c_int, ctypes.c_void_p]
         lib.oracle_regen_rows.restype = None
+        lib.oracle_attend_mods.argtypes = [ctypes.c_int, ctypes.c_void_p, ctypes.c_int64, ctypes.c_int,
+                                           ctypes.c_int, ctypes.c_int, ctypes.c_void_p, ctypes.c_void_p,
+                                           ctypes.c_void_p, ctypes.c_void_p, ctypes.c_double,
+                                           ctypes.c_int64, ctypes.c_int64, ctypes.c_double,
+                                           ctypes.c_int, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int,
+                                           ctypes.c_void_p, ctypes.c_void_p]
+        lib.oracle_attend_mods.restype = ctypes.c_int
         lib.oracle_attend.argtypes = [ctypes.c_int, ctypes.c_void_p, ctypes.c_int64, ctypes.c_int,
                                       ctypes.c_int, ctypes.c_int, ctypes.c_void_p, ctypes.c_void_p,
                                       ctypes.c_void_p, ctypes.c_void_p, ctypes.c_double,
@@ -108,12 +115,15 @@ def bf16_bits_to_f32(bits: np.ndarray) -> np.ndarray:
 
 
 def attend(q, k, v, pos, head_map, scale: float, window: int = 0, n_sinks: int = 0,
-           softcap: float = 0.0):
-    """Full-KV causal attention for one sequence in fp64 (two-pass softmax).
+           softcap: float = 0.0, causal: bool = True, alibi=None, mask=None, allow_empty: bool = False):
+    """Full-KV attention for one sequence in fp64 (two-pass softmax).
 
     q [nq][hq][D], k/v [hkv][n_kv][D] (fp32 arrays; bf16 data widened
-    exactly), pos [nq] absolute query positions, head_map [hq].
-    Returns (out [nq][hq][D] fp64, lse [nq][hq] fp64)."""
+    exactly), pos [nq] absolute query positions, head_map [hq].  causal=False
+    lets every row see all n_kv keys; alibi [hq] adds -slope * |pos - j| to
+    each logit (after the softcap); mask [nq][n_kv] (booleans) additionally
+    hides keys; allow_empty makes rows with no visible key NaN (lse -inf)
+    instead of an error.  Returns (out [nq][hq][D] fp64, lse [nq][hq] fp64)."""
     lib = _load()
     q = np.ascontiguousarray(q, dtype=np.float32)
     k = np.ascontiguousarray(k, dtype=np.float32)
@@ -124,11 +134,20 @@ def attend(q, k, v, pos, head_map, scale: float, window: int = 0, n_sinks: int =
     hkv, n_kv, dk = k.shape
     if v.shape != k.shape or dk != dims or pos.shape[0] != nq or hm.shape[0] != hq:
         raise ValueError("oracle.attend: inconsistent shapes")
+    al = None if alibi is None else np.ascontiguousarray(alibi, dtype=np.float64).reshape(-1)
+    if al is not None and al.shape[0] != hq:
+        raise ValueError("oracle.attend: alibi needs one slope per q-head")
+    mk = None if mask is None else np.ascontiguousarray(mask, dtype=bool).astype(np.uint8)
+    if mk is not None and mk.shape != (nq, n_kv):
+        raise ValueError("oracle.attend: mask must be [nq][n_kv]")
     out = np.empty((nq, hq, dims), dtype=np.float64)
     lse = np.empty((nq, hq), dtype=np.float64)
-    rc = lib.oracle_attend(nq, pos.ctypes.data, n_kv, hq, hkv, dims, q.ctypes.data, k.ctypes.data,
-                           v.ctypes.data, hm.ctypes.data, float(scale), int(window), int(n_sinks),
-                           float(softcap), out.ctypes.data, lse.ctypes.data)
+    rc = lib.oracle_attend_mods(nq, pos.ctypes.data, n_kv, hq, hkv, dims, q.ctypes.data, k.ctypes.data,
+                                v.ctypes.data, hm.ctypes.data, float(scale), int(window), int(n_sinks),
+                                float(softcap), 1 if causal else 0,
+                                None if al is None else al.ctypes.data,
+                                None if mk is None else mk.ctypes.data, 1 if allow_empty else 0,
+                                out.ctypes.data, lse.ctypes.data)
     if rc != 0:
         raise ValueError("oracle.attend: empty visible set or position out of range")
     return out, lse

@@ -169,7 +169,11 @@ static int oracle_visible(int64_t j, int64_t pos, int64_t window, int64_t n_sink
 }
 
 /*
- * Full-KV attention for one sequence, two-pass fp64 softmax.
+ * Full-KV attention for one sequence, two-pass fp64 softmax, with the score
+ * and mask modifications of the CPUAttn operator model ("Operator model":
+ * standard or causal Parallel attention whose score_mod / mask_mod are
+ * elementwise expressions; "Parallel lowering": arbitrary masks keep their
+ * elementwise meaning).
  *   nq          number of query rows
  *   pos[nq]     absolute position of each query row (0 <= pos < n_kv)
  *   n_kv        number of K/V rows supplied (history length)
@@ -177,19 +181,27 @@ static int oracle_visible(int64_t j, int64_t pos, int64_t window, int64_t n_sink
  *   k, v        [hkv][n_kv][dims]       key / value rows
  *   head_map    [hq] -> K/V head
  *   scale       score scale
- *   window      0 = off, else keys with pos - window < j <= pos
+ *   window      0 = off, else keys with pos - window < j <= pos (causal only)
  *   n_sinks     keys j < n_sinks stay visible when a window is set
  *   softcap     0 = off, else s -> softcap * tanh(s / softcap)
+ *   causal      1: key j needs j <= pos; 0: every key j < n_kv
+ *   alibi       [hq] slopes or NULL: the logit gains -slope_h * |pos - j|
+ *               after the softcap
+ *   mask        [nq][n_kv] bytes or NULL: key j of row i also needs
+ *               mask[i][j] != 0
+ *   allow_empty 0: a row with no visible key is an error; 1: its output is
+ *               NaN and its lse -inf
  *   out         [nq][hq][dims]  fp64
  *   lse         [nq][hq]        fp64, natural log of the softmax denominator
  *                               plus the maximum (i.e. log sum exp s_j)
- * Returns 0, or -1 when some row has no visible key or a position is out of
- * range.
+ * Returns 0, or -1 when a row has no visible key (allow_empty = 0) or a
+ * position is out of range.
  */
-int oracle_attend(int nq, const int32_t *pos, int64_t n_kv, int hq, int hkv, int dims,
-                  const float *q, const float *k, const float *v, const int32_t *head_map,
-                  double scale, int64_t window, int64_t n_sinks, double softcap,
-                  double *out, double *lse)
+int oracle_attend_mods(int nq, const int32_t *pos, int64_t n_kv, int hq, int hkv, int dims,
+                       const float *q, const float *k, const float *v, const int32_t *head_map,
+                       double scale, int64_t window, int64_t n_sinks, double softcap,
+                       int causal, const double *alibi, const uint8_t *mask, int allow_empty,
+                       double *out, double *lse)
 {
     for (int i = 0; i < nq; ++i)
         if (pos[i] < 0 || pos[i] >= n_kv)
@@ -212,12 +224,16 @@ int oracle_attend(int nq, const int32_t *pos, int64_t n_kv, int hq, int hkv, int
             const float *vh = v + (int64_t)g * n_kv * dims;
             double *orow = out + ((int64_t)i * hq + h) * dims;
             int64_t p = pos[i];
+            /* causal: the keys up to the row's position; else the whole history */
+            int64_t j_end = causal ? p + 1 : n_kv;
 
             /* pass 1: scores and their maximum over the visible set */
             double m = -INFINITY;
             int64_t n_visible = 0;
-            for (int64_t j = 0; j <= p; ++j) {
-                if (!oracle_visible(j, p, window, n_sinks))
+            for (int64_t j = 0; j < j_end; ++j) {
+                if (causal && !oracle_visible(j, p, window, n_sinks))
+                    continue;
+                if (mask && !mask[(int64_t)i * n_kv + j])
                     continue;
                 double s = 0.0;
                 for (int d = 0; d < dims; ++d)
@@ -225,14 +241,22 @@ int oracle_attend(int nq, const int32_t *pos, int64_t n_kv, int hq, int hkv, int
                 s *= scale;
                 if (softcap > 0.0)
                     s = softcap * tanh(s / softcap);
+                if (alibi)
+                    s -= alibi[h] * (double)(p > j ? p - j : j - p);
                 score[j] = s;
                 if (s > m)
                     m = s;
                 ++n_visible;
             }
             if (n_visible == 0) {
-                #pragma omp atomic write
-                failed = 1;
+                if (!allow_empty) {
+                    #pragma omp atomic write
+                    failed = 1;
+                } else {
+                    for (int d = 0; d < dims; ++d)
+                        orow[d] = NAN;
+                    lse[(int64_t)i * hq + h] = -INFINITY;
+                }
                 continue;
             }
 
@@ -240,8 +264,10 @@ int oracle_attend(int nq, const int32_t *pos, int64_t n_kv, int hq, int hkv, int
             double l = 0.0;
             for (int d = 0; d < dims; ++d)
                 orow[d] = 0.0;
-            for (int64_t j = 0; j <= p; ++j) {
-                if (!oracle_visible(j, p, window, n_sinks))
+            for (int64_t j = 0; j < j_end; ++j) {
+                if (causal && !oracle_visible(j, p, window, n_sinks))
+                    continue;
+                if (mask && !mask[(int64_t)i * n_kv + j])
                     continue;
                 double w = exp(score[j] - m);
                 l += w;
@@ -255,6 +281,16 @@ int oracle_attend(int nq, const int32_t *pos, int64_t n_kv, int hq, int hkv, int
         free(score);
     }
     return failed ? -1 : 0;
+}
+
+/* Causal attention without mods (the method's plain form). */
+int oracle_attend(int nq, const int32_t *pos, int64_t n_kv, int hq, int hkv, int dims,
+                  const float *q, const float *k, const float *v, const int32_t *head_map,
+                  double scale, int64_t window, int64_t n_sinks, double softcap,
+                  double *out, double *lse)
+{
+    return oracle_attend_mods(nq, pos, n_kv, hq, hkv, dims, q, k, v, head_map, scale, window, n_sinks,
+                              softcap, 1, NULL, NULL, 0, out, lse);
 }
 
 /* Number of OpenMP threads a parallel region would use (1 without OpenMP). */
