@@ -107,9 +107,19 @@ class AppendArgs(ctypes.Structure):
     ]
 
 
+class AttnMods(ctypes.Structure):
+    """atlas_attn_mods: causal flag, mask row length, ALiBi slopes, mask bits."""
+    _fields_ = [
+        ("causal", ctypes.c_int32),
+        ("mask_words", ctypes.c_int32),
+        ("alibi_slopes", ctypes.c_void_p),
+        ("mask_bits", ctypes.c_void_p),
+    ]
+
+
 EXPORTS = ("atlas_abi_version", "atlas_status_str", "atlas_last_error",
            "atlas_decode_workspace_bytes", "atlas_prefill_workspace_bytes",
-           "atlas_attend_decode", "atlas_attend_prefill", "atlas_regenerate_pages",
+           "atlas_attend_decode", "atlas_attend_prefill", "atlas_attend_mods", "atlas_regenerate_pages",
            "atlas_attend_decode_regen", "atlas_append_kv", "atlas_pool_create", "atlas_pool_destroy",
            "atlas_pool_alloc", "atlas_pool_retain", "atlas_pool_release", "atlas_pool_free_pages",
            "atlas_pool_refcount")
@@ -134,6 +144,8 @@ def _load():
         fn = getattr(lib, name)
         fn.restype = ctypes.c_int32
         fn.argtypes = [ctypes.POINTER(AttnArgs), ctypes.c_void_p]
+    lib.atlas_attend_mods.restype = ctypes.c_int32
+    lib.atlas_attend_mods.argtypes = [ctypes.POINTER(AttnArgs), ctypes.POINTER(AttnMods), ctypes.c_void_p]
     lib.atlas_regenerate_pages.restype = ctypes.c_int32
     lib.atlas_regenerate_pages.argtypes = [ctypes.POINTER(RegenArgs), ctypes.c_void_p]
     lib.atlas_attend_decode_regen.restype = ctypes.c_int32
@@ -342,6 +354,39 @@ def atlas_attend_prefill(q, k_pages, v_pages, page_table, context_lens, scale, *
                    page_table, context_lens, scale, out, lse, workspace, stream,
                    head_map=head_map, window=window, sink_tokens=sink_tokens, softcap=softcap,
                    split_tokens=split_tokens, want_lse=want_lse)
+
+
+def atlas_attend_mods(q, k_pages, v_pages, page_table, context_lens, scale, *, causal: bool = True,
+                      alibi_slopes=None, mask_bits=None, head_map=None, window=None, sink_tokens=None,
+                      softcap=None, out=None, lse=None, workspace=None, split_tokens=0, stream=None,
+                      want_lse=True):
+    """atlas_attend_prefill with modifications: causal=False lets every row see the whole
+    context; alibi_slopes (f32 [Hq] device tensor) adds -slope * |pos - j| to each logit;
+    mask_bits (int32/uint32 [B][q_len][words] device tensor, bit j & 31 of word j >> 5 = key j
+    visible) hides keys.  Rows with no visible key come back NaN with lse -inf.
+    Returns (out [B][q_len][Hq][D] f32, lse [B][q_len][Hq] f32)."""
+    mods = AttnMods()
+    mods.causal = 1 if causal else 0
+    keep = []
+    if alibi_slopes is not None:
+        _check(alibi_slopes, "alibi_slopes", torch.float32, q.device, 1)
+        if alibi_slopes.shape[0] != q.shape[2]:
+            raise ValueError("alibi_slopes needs one slope per q-head")
+        mods.alibi_slopes = _ptr(alibi_slopes)
+        keep.append(alibi_slopes)
+    if mask_bits is not None:
+        if mask_bits.dtype not in (torch.int32, torch.uint32) or mask_bits.device != q.device or \
+                mask_bits.dim() != 3 or not mask_bits.is_contiguous():
+            raise ValueError("mask_bits must be a contiguous 32-bit [B][q_len][words] tensor on q's device")
+        if tuple(mask_bits.shape[:2]) != tuple(q.shape[:2]):
+            raise ValueError("mask_bits must be [B][q_len][words]")
+        mods.mask_bits = _ptr(mask_bits)
+        mods.mask_words = mask_bits.shape[2]
+        keep.append(mask_bits)
+    return _attend("atlas_attend_mods", atlas_prefill_workspace_bytes, q, k_pages, v_pages,
+                   page_table, context_lens, scale, out, lse, workspace, stream,
+                   extra=(ctypes.byref(mods),), head_map=head_map, window=window, sink_tokens=sink_tokens,
+                   softcap=softcap, split_tokens=split_tokens, want_lse=want_lse)
 
 
 def atlas_regenerate_pages(k_pages, v_pages, jobs, seed: int, layer: int = 0, stream=None):

@@ -316,10 +316,43 @@ struct RegenSpec {
     int32_t layer;
 };
 
-int32_t attend(const atlas_attn_args *a, void *stream_ptr, bool decode, const RegenSpec *regen = nullptr)
+// Host checks of atlas_attn_mods (NULL: none) and their kernel form.
+int32_t check_mods(const atlas_attn_args *a, const Plan &p, const atlas_attn_mods *m, atlas::Mods *out)
+{
+    *out = atlas::Mods{};
+    out->causal = 1;
+    if (!m)
+        return ok();
+    if (m->causal != 0 && m->causal != 1)
+        return fail(ATLAS_ERR_RANGE, "mods->causal must be 0 or 1 (got %d)", m->causal);
+    if (!m->causal && (a->window || a->sink_tokens))
+        return fail(ATLAS_ERR_UNSUPPORTED, "window and sink_tokens apply to causal rows only");
+    if (m->mask_bits) {
+        const int64_t need = ((int64_t)p.max_context + 31) / 32;
+        if (m->mask_words < need)
+            return fail(ATLAS_ERR_SHAPE, "mask_words %d < %lld (max_pages_per_seq * page_size / 32, rounded up)",
+                        m->mask_words, (long long)need);
+        int64_t t = 0;
+        if (!mul_ok((int64_t)a->batch * a->q_len, m->mask_words, &t) || t > INT64_C(1) << 40)
+            return fail(ATLAS_ERR_RANGE, "mask size overflows");
+    }
+    out->alibi = m->alibi_slopes;
+    out->mask = m->mask_bits;
+    out->mask_words = m->mask_bits ? m->mask_words : 0;
+    out->causal = m->causal;
+    out->any = (!m->causal || m->alibi_slopes || m->mask_bits) ? 1 : 0;
+    return ok();
+}
+
+int32_t attend(const atlas_attn_args *a, void *stream_ptr, bool decode, const RegenSpec *regen = nullptr,
+               const atlas_attn_mods *mods_in = nullptr)
 {
     Plan p;
     int32_t st = check_shapes(a, decode, &p);
+    if (st != ATLAS_OK)
+        return st;
+    atlas::Mods mods;
+    st = check_mods(a, p, mods_in, &mods);
     if (st != ATLAS_OK)
         return st;
     if (regen) {
@@ -362,6 +395,7 @@ int32_t attend(const atlas_attn_args *a, void *stream_ptr, bool decode, const Re
         k.max_pages = a->max_pages_per_seq;
         k.max_context = p.max_context;
         k.scale = a->scale;
+        k.mods = mods;
         k.groups = p.groups;
         hipError_t e = p.path == Path::TiledPrefill ? atlas::launch_prefill_mfma(k, stream)
                                                      : atlas::launch_prefill_split(k, stream);
@@ -401,6 +435,7 @@ int32_t attend(const atlas_attn_args *a, void *stream_ptr, bool decode, const Re
     k.rows_per_item = p.rows_per_item;
     k.n_chunks = p.n_chunks;
     k.scale = a->scale;
+    k.mods = mods;
     k.groups = p.groups;
     if (regen) {
         k.regen_seed = regen->seed;
@@ -465,6 +500,11 @@ size_t atlas_prefill_workspace_bytes(const atlas_attn_args *args) { return works
 int32_t atlas_attend_decode(const atlas_attn_args *args, void *stream) { return attend(args, stream, true); }
 
 int32_t atlas_attend_prefill(const atlas_attn_args *args, void *stream) { return attend(args, stream, false); }
+
+int32_t atlas_attend_mods(const atlas_attn_args *args, const atlas_attn_mods *mods, void *stream)
+{
+    return attend(args, stream, false, nullptr, mods);
+}
 
 int32_t atlas_attend_decode_regen(const atlas_attn_args *args, uint64_t seed, int32_t layer, void *stream)
 {

@@ -21,6 +21,20 @@ struct HeadGroups {
     int32_t pad;
 };
 
+// Score and mask modifications of atlas_attend_mods.  any = 0 selects the
+// plain causal kernels; otherwise key j of a row at position pos of sequence
+// b (query i) is visible when (causal ? j <= pos : j < context) and, with a
+// mask, bit j of mask row (b, i) is set; the logit gains -alibi[h] |pos - j|
+// after the softcap.
+struct Mods {
+    const float *alibi;         // [hq] slopes or null
+    const uint32_t *mask;       // [B][q_len][mask_words] bits or null
+    int32_t mask_words;
+    int32_t causal;
+    int32_t any;
+    int32_t pad;
+};
+
 // Everything a split-KV work item and the merge pass need.
 struct SplitArgs {
     const void *q;
@@ -47,6 +61,7 @@ struct SplitArgs {
     uint64_t regen_seed;
     int32_t regen_layer;
     int32_t regen;              // 0: every page is read from the arenas
+    Mods mods;
     HeadGroups groups;
 };
 
@@ -94,6 +109,7 @@ struct PrefillArgs {
     int32_t batch, q_len, hq, hkv, head_dim, page_shift, num_phys, max_pages, max_context;
     int32_t n_qblocks;          // query blocks per (sequence, K/V head)
     float scale;
+    Mods mods;
     HeadGroups groups;
 };
 

@@ -37,7 +37,9 @@ __global__ __launch_bounds__(64) void merge_kernel(SplitArgs a)
     const ChunkRows cr = chunk_rows(rr / a.rows_per_item, a.rows_per_item, gsize, a.q_len, ctx);
     const int W = a.window ? a.window[b] : 0;
     const int S = a.sinks ? a.sinks[b] : 0;
-    const SplitPlan plan = plan_splits(cr.pos_min, cr.pos_max, W, S, a.split_tokens);
+    // Non-causal rows (atlas_attend_mods) were planned over [0, ctx).
+    const SplitPlan plan = (a.mods.any && !a.mods.causal) ? plan_splits(ctx - 1, ctx - 1, 0, 0, a.split_tokens)
+                                                          : plan_splits(cr.pos_min, cr.pos_max, W, S, a.split_tokens);
     const int n = plan.n_splits;
 
     const float *ml = a.ws_ml + row_id * a.max_splits * 2;

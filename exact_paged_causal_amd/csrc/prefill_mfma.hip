@@ -37,6 +37,13 @@
 //                hardware deals workgroups to the 8 XCDs round-robin) and
 //                share its L2.
 //
+// Modifications (MODS instances, atlas_attend_mods): non-causal rows take
+// every key block of the context, with only the block past the last key
+// masked; an ALiBi slope adds -slope |pos - j| (as -slope/scale |pos - j| in
+// the units of the raw product, after the softcap) and mask bits hide keys
+// per (row, key), both applied per element in every block (each lane loads
+// the two mask words of its row for the block ahead of the QK products).
+//
 // Precondition of the fp16 P.V product: |V| <= 65504 (validation mode
 // checks it).  Scores use bf16 K and Q exactly (products are exact in fp32).
 #include "device.h"
@@ -78,7 +85,7 @@ __device__ __forceinline__ uint32_t bf16pair_to_f16pair(uint32_t x)
     return __builtin_bit_cast(uint32_t, __builtin_convertvector(f, f16x2));
 }
 
-template <int D>
+template <int D, bool MODS>
 __global__ __launch_bounds__(512) void prefill_kernel(PrefillArgs a)
 {
     constexpr int KS = D / 16;            // k-steps of the QK product
@@ -115,6 +122,10 @@ __global__ __launch_bounds__(512) void prefill_kernel(PrefillArgs a)
     const int W = a.window ? a.window[b] : 0;
     const int S = (a.sinks && W > 0) ? a.sinks[b] : 0;
     const float cap = a.softcap ? a.softcap[b] : 0.0f;
+    // Last key any row of the block can see: the diagonal, or the whole
+    // context for non-causal rows.
+    const bool causal = !MODS || a.mods.causal;
+    const int key_hi = causal ? pos_hi : (pos_hi >= 0 ? ctx - 1 : -1);
 
     // This lane's row.
     const int r = wave * 32 + (lane & 31);
@@ -124,6 +135,12 @@ __global__ __launch_bounds__(512) void prefill_kernel(PrefillArgs a)
     const bool row_ok = ri < npos && qi < i1 && rj < gsize;
     const int pos = row_ok ? ctx - a.q_len + qi : -1;
     const int h = row_ok ? a.groups.list[gstart + rj] : 0;
+    // MODS: this row's last visible key, ALiBi slope in raw-product units and
+    // mask row.
+    const int posv = causal ? pos : (row_ok ? ctx - 1 : -1);
+    const float slope_raw = (MODS && row_ok && a.mods.alibi) ? a.mods.alibi[h] / a.scale : 0.0f;
+    const uint32_t *mrow =
+        (MODS && row_ok && a.mods.mask) ? a.mods.mask + ((int64_t)b * a.q_len + qi) * a.mods.mask_words : nullptr;
 
     bf16x8 qf[KS];
     {
@@ -150,7 +167,7 @@ __global__ __launch_bounds__(512) void prefill_kernel(PrefillArgs a)
     int pid_base = 0;
     auto stage_pids = [&](int first_page) {
         pid_base = first_page;
-        const int last_page = pos_hi >= 0 ? pos_hi >> ps : -1;
+        const int last_page = key_hi >= 0 ? key_hi >> ps : -1;
         for (int t = tid; t < kPidWindow && first_page + t <= last_page; t += 512) {
             const int pid = ptab[first_page + t];
             sm.pid[t] = ((unsigned)pid < (unsigned)a.num_phys) ? pid : 0;
@@ -164,7 +181,7 @@ __global__ __launch_bounds__(512) void prefill_kernel(PrefillArgs a)
     uint4 kreg[CH], vreg[CH];
     auto fetch = [&](int kb) {
         const int j = kb * kBN + srow;
-        if (j <= pos_hi) {
+        if (j <= key_hi) {
             const int pid = sm.pid[(j >> ps) - pid_base];
             const int64_t off = ((((int64_t)pid * a.hkv + g) << ps) + (j & pmask)) * D + scol * 8;
 #pragma unroll
@@ -214,7 +231,7 @@ __global__ __launch_bounds__(512) void prefill_kernel(PrefillArgs a)
     // Key blocks the rows can see: with a window, the sink blocks and then
     // the blocks from the lowest row's window start to the diagonal (blocks
     // in between are skipped); otherwise every block up to the diagonal.
-    const int kb_last = pos_hi >= 0 ? pos_hi / kBN : -1;
+    const int kb_last = key_hi >= 0 ? key_hi / kBN : -1;
     int first_win = 0, n_sink_blk = 0;
     if (W > 0 && kb_last >= 0) {
         const int lo_key = pos_lo - W + 1;
@@ -246,6 +263,15 @@ __global__ __launch_bounds__(512) void prefill_kernel(PrefillArgs a)
         }
         if (more)
             fetch(kb_next);
+        // MODS: the row's mask words for this block's two 32-key tiles (words
+        // past the row's end hold keys beyond every context and are clamped).
+        uint32_t mw0 = ~0u, mw1 = ~0u;
+        if (MODS && mrow) {
+            const int w = (kb * kBN) >> 5;
+            const int wl = a.mods.mask_words - 1;
+            mw0 = mrow[w < wl ? w : wl];
+            mw1 = mrow[w + 1 < wl ? w + 1 : wl];
+        }
 
         // S^T for the block: two 32-key tiles.
         __builtin_amdgcn_s_setprio(1);
@@ -286,6 +312,23 @@ __global__ __launch_bounds__(512) void prefill_kernel(PrefillArgs a)
         // Mask only blocks some row does not see whole: past the first row's
         // position (causal), or not inside every row's window or sink range.
         const int k0 = kb * kBN;
+        if constexpr (MODS) {
+            // ALiBi bias and mask bits on every element; non-causal rows mask
+            // only keys past the context.
+            if (slope_raw != 0.0f || mrow || k0 + kBN - 1 > (causal ? pos_lo : key_hi) ||
+                !(W <= 0 || k0 > pos_hi - W || k0 + kBN - 1 < S)) {
+#pragma unroll
+                for (int t = 0; t < 2; ++t)
+#pragma unroll
+                    for (int e = 0; e < 16; ++e) {
+                        const int jo = 32 * t + 8 * (e >> 2) + 4 * half + (e & 3);
+                        const int j = k0 + jo;
+                        const uint32_t mw = t ? mw1 : mw0;
+                        const bool vis = j <= posv && (W <= 0 || j > pos - W || j < S) && ((mw >> (jo & 31)) & 1u);
+                        st[t][e] = vis ? st[t][e] - slope_raw * fabsf((float)(pos - j)) : -INFINITY;
+                    }
+            }
+        } else {
         const bool all_causal = k0 + kBN - 1 <= pos_lo;
         const bool all_window = W <= 0 || k0 > pos_hi - W || k0 + kBN - 1 < S;
         if (!(all_causal && all_window)) {
@@ -298,6 +341,7 @@ __global__ __launch_bounds__(512) void prefill_kernel(PrefillArgs a)
                     if (!vis)
                         st[t][e] = -INFINITY;
                 }
+        }
         }
 
         // Online softmax (lane = one row, two lane halves share it).
@@ -416,10 +460,12 @@ hipError_t launch_prefill_mfma(const PrefillArgs &a, hipStream_t stream)
     const int64_t blocks = (int64_t)k.n_qblocks * a.batch * a.hkv;
     if (blocks > 0x7FFFFFFF)
         return hipErrorInvalidValue;
+    void (*kernel)(PrefillArgs);
     if (a.head_dim == 64)
-        hipLaunchKernelGGL(prefill_kernel<64>, dim3((unsigned)blocks), dim3(512), 0, stream, k);
+        kernel = a.mods.any ? prefill_kernel<64, true> : prefill_kernel<64, false>;
     else
-        hipLaunchKernelGGL(prefill_kernel<128>, dim3((unsigned)blocks), dim3(512), 0, stream, k);
+        kernel = a.mods.any ? prefill_kernel<128, true> : prefill_kernel<128, false>;
+    hipLaunchKernelGGL(kernel, dim3((unsigned)blocks), dim3(512), 0, stream, k);
     return hipGetLastError();
 }
 

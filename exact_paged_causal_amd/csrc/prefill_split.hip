@@ -35,6 +35,10 @@
 //   softcap    = library tanhf (the hardware-exponential tanh of the bf16
 //                kernel is too coarse for the fp32 bar).
 //
+// Modifications (MODS instances, atlas_attend_mods) as in the bf16 kernel:
+// non-causal rows take every key block of the context; ALiBi bias (in the
+// units the scores have after the softcap step) and mask bits per element.
+//
 // Precondition: |q|, |k|, |v| <= 65504 (fp16 range of the hi parts);
 // validation mode checks it.
 #include "device.h"
@@ -93,7 +97,7 @@ __device__ __forceinline__ HiLo split2(float x0, float x1)
     return {f16bits2(h), f16bits2(__builtin_convertvector(f32x2{x0 - hf[0], x1 - hf[1]}, f16x2))};
 }
 
-template <int D>
+template <int D, bool MODS>
 __global__ __launch_bounds__(512) void prefill_split_kernel(PrefillArgs a)
 {
     constexpr int KS = D / 16;            // k-steps of the QK product
@@ -128,6 +132,10 @@ __global__ __launch_bounds__(512) void prefill_split_kernel(PrefillArgs a)
     const int W = a.window ? a.window[b] : 0;
     const int S = (a.sinks && W > 0) ? a.sinks[b] : 0;
     const float cap = a.softcap ? a.softcap[b] : 0.0f;
+    // Last key any row of the block can see (the whole context when rows are
+    // not causal).
+    const bool causal = !MODS || a.mods.causal;
+    const int key_hi = causal ? pos_hi : (pos_hi >= 0 ? ctx - 1 : -1);
 
     // This lane's row.
     const int r = wave * 32 + (lane & 31);
@@ -137,6 +145,9 @@ __global__ __launch_bounds__(512) void prefill_split_kernel(PrefillArgs a)
     const bool row_ok = ri < npos && qi < i1 && rj < gsize;
     const int pos = row_ok ? ctx - a.q_len + qi : -1;
     const int h = row_ok ? a.groups.list[gstart + rj] : 0;
+    const int posv = causal ? pos : (row_ok ? ctx - 1 : -1);
+    const uint32_t *mrow =
+        (MODS && row_ok && a.mods.mask) ? a.mods.mask + ((int64_t)b * a.q_len + qi) * a.mods.mask_words : nullptr;
 
     // Q^T as the B operand, range-scaled and split: dims 16s + 8 half .. +7
     // of this lane's row (the other lane half holds the rest of the row).
@@ -177,7 +188,7 @@ __global__ __launch_bounds__(512) void prefill_split_kernel(PrefillArgs a)
     int pid_base = 0;
     auto stage_pids = [&](int first_page) {
         pid_base = first_page;
-        const int last_page = pos_hi >= 0 ? pos_hi >> ps : -1;
+        const int last_page = key_hi >= 0 ? key_hi >> ps : -1;
         for (int t = tid; t < kPidWindow && first_page + t <= last_page; t += 512) {
             const int pid = ptab[first_page + t];
             sm.pid[t] = ((unsigned)pid < (unsigned)a.num_phys) ? pid : 0;
@@ -194,7 +205,7 @@ __global__ __launch_bounds__(512) void prefill_split_kernel(PrefillArgs a)
     f32x4 reg[CH];
     auto fetch = [&](const float *pages, int kb) {
         const int j = kb * kBN + srow;
-        if (j <= pos_hi) {
+        if (j <= key_hi) {
             const int pid = sm.pid[(j >> ps) - pid_base];
             const int64_t off = ((((int64_t)pid * a.hkv + g) << ps) + (j & pmask)) * D + scol * 4;
 #pragma unroll
@@ -242,6 +253,10 @@ __global__ __launch_bounds__(512) void prefill_split_kernel(PrefillArgs a)
     // Scores leave the QK product in the row's scaled units (raw x 2^shift);
     // the softcap brings them back to raw units.
     const float c_log2 = cap > 0.0f ? a.scale * kLog2e : a.scale * kLog2e * row_factor;
+    // MODS: ALiBi slope in the units of the scores after the softcap step.
+    const float slope_u = (MODS && row_ok && a.mods.alibi)
+                              ? a.mods.alibi[h] / (cap > 0.0f ? a.scale : a.scale * row_factor)
+                              : 0.0f;
     float m_ref = -INFINITY;  // reference max (log2 units) the accumulator is scaled to
     float l_part = 0.0f;      // this lane-half's share of the softmax denominator (fp32)
     f32x16 acc[DT];
@@ -257,7 +272,7 @@ __global__ __launch_bounds__(512) void prefill_split_kernel(PrefillArgs a)
 
     // Key blocks the rows can see (sink blocks, then the window up to the
     // diagonal; every block up to the diagonal without a window).
-    const int kb_last = pos_hi >= 0 ? pos_hi / kBN : -1;
+    const int kb_last = key_hi >= 0 ? key_hi / kBN : -1;
     int first_win = 0, n_sink_blk = 0;
     if (W > 0 && kb_last >= 0) {
         const int lo_key = pos_lo - W + 1;
@@ -290,6 +305,13 @@ __global__ __launch_bounds__(512) void prefill_split_kernel(PrefillArgs a)
         }
         if (more)
             fetch(kpages, kb_next);
+        uint32_t mw0 = ~0u, mw1 = ~0u;
+        if (MODS && mrow) {
+            const int w = (kb * kBN) >> 5;
+            const int wl = a.mods.mask_words - 1;
+            mw0 = mrow[w < wl ? w : wl];
+            mw1 = mrow[w + 1 < wl ? w + 1 : wl];
+        }
 
         // S^T for the block: two 32-key tiles, three split products per
         // k-step; consecutive products alternate between the two tiles.
@@ -358,15 +380,20 @@ __global__ __launch_bounds__(512) void prefill_split_kernel(PrefillArgs a)
         }
         // Mask only blocks some row does not see whole.
         const int k0 = kb * kBN;
-        const bool all_causal = k0 + kBN - 1 <= pos_lo;
+        const bool all_causal = k0 + kBN - 1 <= (causal ? pos_lo : key_hi);
         const bool all_window = W <= 0 || k0 > pos_hi - W || k0 + kBN - 1 < S;
-        if (!(all_causal && all_window)) {
+        if (!(all_causal && all_window) || (MODS && (slope_u != 0.0f || mrow))) {
 #pragma unroll
             for (int t = 0; t < 2; ++t)
 #pragma unroll
                 for (int e = 0; e < 16; ++e) {
-                    const int j = k0 + 32 * t + 8 * (e >> 2) + 4 * half + (e & 3);
-                    const bool vis = j <= pos && (W <= 0 || j > pos - W || j < S);
+                    const int jo = 32 * t + 8 * (e >> 2) + 4 * half + (e & 3);
+                    const int j = k0 + jo;
+                    bool vis = j <= posv && (W <= 0 || j > pos - W || j < S);
+                    if constexpr (MODS) {
+                        vis = vis && (((t ? mw1 : mw0) >> (jo & 31)) & 1u);
+                        st[t][e] -= slope_u * fabsf((float)(pos - j));
+                    }
                     if (!vis)
                         st[t][e] = -INFINITY;
                 }
@@ -508,10 +535,12 @@ hipError_t launch_prefill_split(const PrefillArgs &a, hipStream_t stream)
     const int64_t blocks = (int64_t)k.n_qblocks * a.batch * a.hkv;
     if (blocks > 0x7FFFFFFF)
         return hipErrorInvalidValue;
+    void (*kernel)(PrefillArgs);
     if (a.head_dim == 64)
-        hipLaunchKernelGGL(prefill_split_kernel<64>, dim3((unsigned)blocks), dim3(512), 0, stream, k);
+        kernel = a.mods.any ? prefill_split_kernel<64, true> : prefill_split_kernel<64, false>;
     else
-        hipLaunchKernelGGL(prefill_split_kernel<128>, dim3((unsigned)blocks), dim3(512), 0, stream, k);
+        kernel = a.mods.any ? prefill_split_kernel<128, true> : prefill_split_kernel<128, false>;
+    hipLaunchKernelGGL(kernel, dim3((unsigned)blocks), dim3(512), 0, stream, k);
     return hipGetLastError();
 }
 

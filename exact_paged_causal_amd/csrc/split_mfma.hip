@@ -66,7 +66,9 @@ __device__ __forceinline__ void split_hi_lo(float p0, float p1, uint32_t &hi, ui
     lo = __builtin_bit_cast(uint32_t, __builtin_convertvector(f32x2{r0, r1}, bf16x2));
 }
 
-template <int D>
+// MODS instances (atlas_attend_mods): non-causal rows plan and mask over
+// [0, ctx); ALiBi slopes and mask bits per (row, key).
+template <int D, bool MODS>
 __global__ __launch_bounds__(256) void split_mfma_kernel(SplitArgs a)
 {
     constexpr int KS = D / 32;                 // QK k-steps
@@ -96,7 +98,9 @@ __global__ __launch_bounds__(256) void split_mfma_kernel(SplitArgs a)
     const int W = a.window ? a.window[b] : 0;
     const int S = a.sinks ? a.sinks[b] : 0;
     const float cap = a.softcap ? a.softcap[b] : 0.0f;
-    const SplitPlan plan = plan_splits(cr.pos_min, cr.pos_max, W, S, a.split_tokens);
+    const bool causal = !MODS || a.mods.causal;
+    const SplitPlan plan = causal ? plan_splits(cr.pos_min, cr.pos_max, W, S, a.split_tokens)
+                                  : plan_splits(ctx - 1, ctx - 1, 0, 0, a.split_tokens);
     if (split >= plan.n_splits)
         return;
     int ka, kb;
@@ -117,6 +121,11 @@ __global__ __launch_bounds__(256) void split_mfma_kernel(SplitArgs a)
     const int qi = row_ok ? rr / gsize : 0;
     const int h = row_ok ? a.groups.list[gstart + rr % gsize] : 0;
     const int pos = row_ok ? ctx - a.q_len + qi : -1;
+    // MODS: bound of the visible keys, ALiBi slope and mask row of this row.
+    const int posv = (MODS && !causal && row_ok) ? ctx - 1 : pos;
+    const float slope = (MODS && row_ok && a.mods.alibi) ? a.mods.alibi[h] : 0.0f;
+    const uint32_t *mrow =
+        (MODS && row_ok && a.mods.mask) ? a.mods.mask + ((int64_t)b * a.q_len + qi) * a.mods.mask_words : nullptr;
     bf16x8 qf[KS];
     {
         const uint16_t *qrow = reinterpret_cast<const uint16_t *>(a.q) +
@@ -199,7 +208,17 @@ __global__ __launch_bounds__(256) void split_mfma_kernel(SplitArgs a)
                 float sc = st[t][j] * qk_scale;
                 if (cap > 0.0f)
                     sc = cap * tanhf(sc / cap);
-                const bool vis = key < kb && key <= pos && (W <= 0 || key > pos - W || key < S);
+                bool vis;
+                if constexpr (MODS) {
+                    sc -= slope * fabsf((float)(pos - key));
+                    vis = key < kb && key <= posv && (W <= 0 || key > pos - W || key < S);
+                    if (mrow) {
+                        const int km = key < kb ? key : kb - 1;  // in-bounds word
+                        vis = vis && ((mrow[km >> 5] >> (km & 31)) & 1u);
+                    }
+                } else {
+                    vis = key < kb && key <= pos && (W <= 0 || key > pos - W || key < S);
+                }
                 x[4 * t + j] = vis ? sc * kLog2e : -INFINITY;
             }
         float mx = x[0];
@@ -320,10 +339,12 @@ hipError_t launch_split_mfma(const SplitArgs &a, hipStream_t stream)
     if (a.rows_per_item != kRowsMax)
         return hipErrorInvalidValue;
     dim3 grid(a.max_splits, a.hkv * a.n_chunks, a.batch);
+    void (*kernel)(SplitArgs);
     if (a.head_dim == 64)
-        hipLaunchKernelGGL(split_mfma_kernel<64>, grid, dim3(256), 0, stream, a);
+        kernel = a.mods.any ? split_mfma_kernel<64, true> : split_mfma_kernel<64, false>;
     else
-        hipLaunchKernelGGL(split_mfma_kernel<128>, grid, dim3(256), 0, stream, a);
+        kernel = a.mods.any ? split_mfma_kernel<128, true> : split_mfma_kernel<128, false>;
+    hipLaunchKernelGGL(kernel, grid, dim3(256), 0, stream, a);
     return hipGetLastError();
 }
 

@@ -25,6 +25,11 @@
 // so the fold sees the same bits a regenerated scratch page would hold.
 // Their loads still go out (to page 0, cached) so that the prefetch stays
 // unconditional.
+//
+// Modifications (MODS instances, atlas_attend_mods): non-causal rows see
+// every key of the context (the split plan then spans [0, L)); an ALiBi slope
+// per q-head adds -slope |pos - j| to the logit after the softcap; mask bits
+// hide keys per (row, key).
 #include "device.h"
 #include "kernels.h"
 #include "philox.h"
@@ -47,7 +52,7 @@ struct Elem<float> {
     }
 };
 
-template <typename E, int D, int MC, int KU, bool REGEN>
+template <typename E, int D, int MC, int KU, bool REGEN, bool MODS>
 __global__ __launch_bounds__(256) void split_valu_kernel(SplitArgs a)
 {
     constexpr int EPC = Elem<E>::kPer16;                 // elements per 16-byte piece
@@ -85,7 +90,11 @@ __global__ __launch_bounds__(256) void split_valu_kernel(SplitArgs a)
     const int W = a.window ? a.window[b] : 0;
     const int S = a.sinks ? a.sinks[b] : 0;
     const float cap = a.softcap ? a.softcap[b] : 0.0f;
-    const SplitPlan plan = plan_splits(cr.pos_min, cr.pos_max, W, S, a.split_tokens);
+    // Non-causal rows see keys [0, ctx): plan and mask as if every row sat at
+    // the last position.
+    const bool causal = !MODS || a.mods.causal;
+    const SplitPlan plan = causal ? plan_splits(cr.pos_min, cr.pos_max, W, S, a.split_tokens)
+                                  : plan_splits(ctx - 1, ctx - 1, 0, 0, a.split_tokens);
     if (split >= plan.n_splits)
         return;
     int ka, kb;
@@ -101,16 +110,29 @@ __global__ __launch_bounds__(256) void split_valu_kernel(SplitArgs a)
         s_pid[t] = (REGEN && pid == -1) ? -1 : (((unsigned)pid < (unsigned)a.num_phys) ? pid : 0);
     }
 
-    // Query slices and positions of the chunk's rows.
+    // Query slices and positions of the chunk's rows (MODS: also the bound
+    // of the visible keys, the ALiBi slope and the mask row).
     float q[MC][DPL];
     int pos[MC];
+    int posv[MC];
+    float slope[MC];
+    const uint32_t *mrow[MC];
 #pragma unroll
     for (int r = 0; r < MC; ++r) {
         const int rr = cr.r0 + r;
+        posv[r] = -1;
+        slope[r] = 0.0f;
+        mrow[r] = nullptr;
         if (rr < cr.r1) {
             const int i = rr / gsize;
             const int h = a.groups.list[gstart + rr % gsize];
             pos[r] = ctx - a.q_len + i;
+            if constexpr (MODS) {
+                posv[r] = causal ? pos[r] : ctx - 1;
+                slope[r] = a.mods.alibi ? a.mods.alibi[h] : 0.0f;
+                if (a.mods.mask)
+                    mrow[r] = a.mods.mask + ((int64_t)b * a.q_len + i) * a.mods.mask_words;
+            }
             const E *qrow = reinterpret_cast<const E *>(a.q) +
                             (((int64_t)b * a.q_len + i) * a.hq + h) * D;
 #pragma unroll
@@ -217,7 +239,17 @@ __global__ __launch_bounds__(256) void split_valu_kernel(SplitArgs a)
                 if (cap > 0.0f)
                     s = cap * tanhf(s / cap);
                 const int j = key[u];
-                const bool vis = j < kb && j <= pos[r] && (W <= 0 || j > pos[r] - W || j < S);
+                bool vis;
+                if constexpr (MODS) {
+                    s -= slope[r] * fabsf((float)(pos[r] - j));
+                    vis = j < kb && j <= posv[r] && (W <= 0 || j > pos[r] - W || j < S);
+                    if (mrow[r]) {
+                        const int jm = j < kb ? j : kb - 1;  // in-bounds word
+                        vis = vis && ((mrow[r][jm >> 5] >> (jm & 31)) & 1u);
+                    }
+                } else {
+                    vis = j < kb && j <= pos[r] && (W <= 0 || j > pos[r] - W || j < S);
+                }
                 s2[u] = vis ? s * kLog2e : -INFINITY;
             }
             float mx = s2[0];
@@ -337,9 +369,11 @@ hipError_t launch_one(const SplitArgs &a, hipStream_t stream)
     constexpr int KU = (D == 64) ? ((MC <= 2) ? 8 : (MC * DPL <= 16 ? 4 : 2)) : ((MC <= 2) ? 4 : 2);
     dim3 grid(a.max_splits, a.hkv * a.n_chunks, a.batch);
     if (a.regen)
-        hipLaunchKernelGGL((split_valu_kernel<E, D, MC, KU, true>), grid, dim3(256), 0, stream, a);
+        hipLaunchKernelGGL((split_valu_kernel<E, D, MC, KU, true, false>), grid, dim3(256), 0, stream, a);
+    else if (a.mods.any)
+        hipLaunchKernelGGL((split_valu_kernel<E, D, MC, KU, false, true>), grid, dim3(256), 0, stream, a);
     else
-        hipLaunchKernelGGL((split_valu_kernel<E, D, MC, KU, false>), grid, dim3(256), 0, stream, a);
+        hipLaunchKernelGGL((split_valu_kernel<E, D, MC, KU, false, false>), grid, dim3(256), 0, stream, a);
     return hipGetLastError();
 }
 

@@ -198,6 +198,44 @@ int32_t atlas_attend_decode(const atlas_attn_args *args, void *stream);
  */
 int32_t atlas_attend_prefill(const atlas_attn_args *args, void *stream);
 
+/*
+ * Score and mask modifications.  CPUAttn ("Operator model") defines Parallel
+ * attention as standard (non-causal) or causal, with elementwise score and
+ * mask expressions, and its tiled lowering keeps an arbitrary mask's
+ * elementwise meaning ("Parallel lowerings").  Here:
+ *   causal        1: key j is visible to a query at position pos only if
+ *                 j <= pos (the rule of atlas_attend_prefill); 0: every key
+ *                 j < L_b is visible (window and sink_tokens must be NULL,
+ *                 else ATLAS_ERR_UNSUPPORTED).
+ *   alibi_slopes  device [num_q_heads] fp32, or NULL: the logit of key j for
+ *                 q-head h gains -alibi_slopes[h] * |pos - j|, after the
+ *                 softcap and before the mask (ALiBi-style linear bias).
+ *   mask_bits     device [batch][q_len][mask_words] uint32, or NULL: key j of
+ *                 query row i of sequence b is visible only if bit (j & 31)
+ *                 of word (j >> 5) of row (b, i) is set; ANDed with the
+ *                 causal / window / sink rule.  Bits of keys >= L_b are
+ *                 ignored.
+ *   mask_words    words per mask row, >= ceil(max_pages_per_seq * page_size
+ *                 / 32) when mask_bits is set (else ATLAS_ERR_SHAPE).
+ * A row whose visible set is empty gets NaN output and lse = -inf.
+ */
+typedef struct atlas_attn_mods {
+    int32_t causal;
+    int32_t mask_words;
+    const float *alibi_slopes;
+    const uint32_t *mask_bits;
+} atlas_attn_mods;
+
+/*
+ * atlas_attend_prefill with modifications (mods may be NULL: no
+ * modification).  Same arguments, workspace (atlas_prefill_workspace_bytes)
+ * and outputs; q_len >= 1.  bf16 with q_len >= 64 runs the tiled
+ * matrix-core kernel (non-causal rows take every key block of the context;
+ * masked and biased elements are applied per element inside the tiles);
+ * every other case runs the split-KV kernels.
+ */
+int32_t atlas_attend_mods(const atlas_attn_args *args, const atlas_attn_mods *mods, void *stream);
+
 /* Regenerate whole pages (all heads, all P tokens) into the arenas. */
 int32_t atlas_regenerate_pages(const atlas_regen_args *args, void *stream);
 

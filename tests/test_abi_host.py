@@ -23,7 +23,7 @@ def test_header_declares_the_boundary():
     names = _declared_functions()
     assert names == sorted(["atlas_abi_version", "atlas_status_str", "atlas_last_error",
                             "atlas_decode_workspace_bytes", "atlas_prefill_workspace_bytes",
-                            "atlas_attend_decode", "atlas_attend_prefill",
+                            "atlas_attend_decode", "atlas_attend_prefill", "atlas_attend_mods",
                             "atlas_regenerate_pages", "atlas_attend_decode_regen", "atlas_append_kv",
                             "atlas_pool_create", "atlas_pool_destroy", "atlas_pool_alloc",
                             "atlas_pool_retain", "atlas_pool_release", "atlas_pool_free_pages",
@@ -58,6 +58,8 @@ def test_binding_structs_mirror_the_header():
     assert [f[0] for f in A.RegenJob._fields_] == _struct_offsets_from_header("atlas_regen_job")
     assert ctypes.sizeof(A.AttnArgs) == 4 * 12 + 8 * 13
     assert ctypes.sizeof(A.RegenArgs) == 8 + 4 * 8 + 8 * 3
+    assert [f[0] for f in A.AttnMods._fields_] == _struct_offsets_from_header("atlas_attn_mods")
+    assert ctypes.sizeof(A.AttnMods) == 4 * 2 + 8 * 2
 
 
 FAKE = 0x10000  # never dereferenced: every case below fails host validation first
@@ -130,6 +132,26 @@ def test_decode_regen_rejects_bad_arguments_before_launch():
     assert fn(ctypes.byref(_valid_args(workspace_bytes=16)), 7, 0, None) == A.ATLAS_ERR_WORKSPACE
     assert A.ATLAS_PAGE_REGENERATE == -1
     assert "#define ATLAS_PAGE_REGENERATE (-1)" in open(HEADER).read()
+
+
+def test_mods_reject_bad_arguments_before_launch():
+    """atlas_attend_mods: causal must be 0 or 1, windows and sinks need
+    causal rows, and a mask row must cover the largest context
+    (max_pages_per_seq * page_size = 64 keys -> 2 words)."""
+    from exact_paged_causal_amd import atlas as A
+    fn = A.lib.atlas_attend_mods
+    m = A.AttnMods(2, 0, None, None)
+    assert fn(ctypes.byref(_valid_args()), ctypes.byref(m), None) == A.ATLAS_ERR_RANGE
+    win = (ctypes.c_int32 * 2)(16, 16)
+    a = _valid_args(window=ctypes.addressof(win))
+    m = A.AttnMods(0, 0, None, None)
+    assert fn(ctypes.byref(a), ctypes.byref(m), None) == A.ATLAS_ERR_UNSUPPORTED
+    assert "causal" in A.atlas_last_error()
+    m = A.AttnMods(1, 1, None, FAKE)
+    assert fn(ctypes.byref(_valid_args()), ctypes.byref(m), None) == A.ATLAS_ERR_SHAPE
+    assert "mask_words" in A.atlas_last_error()
+    m = A.AttnMods(1, 2, None, FAKE)             # enough words: the call gets past the mods checks
+    assert fn(ctypes.byref(_valid_args(q=None)), ctypes.byref(m), None) == A.ATLAS_ERR_NULL
 
 
 def test_append_rejects_bad_arguments_before_launch():

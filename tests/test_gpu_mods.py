@@ -1,0 +1,191 @@
+"""GPU parity of atlas_attend_mods (non-causal rows, ALiBi slopes, mask bits)
+against the fp64 oracle, through the C ABI, on the split-KV kernels
+(q_len < 64 and decode) and the tiled prefill kernels (q_len >= 64, bf16 and
+fp32).  Rows with nothing visible must come back NaN with lse = -inf.  Each
+test prints its case before running."""
+import math
+
+import numpy as np
+import pytest
+import torch
+
+import harness as H
+import oracle
+import workloads
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _gpu():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    import exact_paged_causal_amd  # noqa: F401  (fails loudly if libatlas.so is missing)
+    yield
+
+
+def say(*a):
+    print(*a, flush=True)
+
+
+def alibi_slopes(hq):
+    """The geometric ALiBi slopes 2^(-8 (h + 1) / Hq)."""
+    return (2.0 ** (-8.0 * (np.arange(hq) + 1) / hq)).astype(np.float32)
+
+
+def pack_mask(mask, words):
+    """[B][q_len][n] booleans -> [B][q_len][words] int32, bit j & 31 of word
+    j >> 5 = key j."""
+    B, nq, n = mask.shape
+    bits = np.zeros((B, nq, words * 32), bool)
+    bits[..., :n] = mask
+    packed = np.packbits(bits, axis=-1, bitorder="little")
+    return torch.from_numpy(np.ascontiguousarray(packed).view("<u4").astype(np.uint32).view(np.int32)).cuda()
+
+
+def make_mask(w, density, seed, empty_rows=0):
+    """Random keep-mask over every row's keys, each row's own position kept;
+    the first `empty_rows` rows of sequence 0 hide everything."""
+    L = int(w.page_size * ((int(w.context_lens.max()) + w.page_size - 1) // w.page_size))
+    rng = np.random.default_rng(seed)
+    m = rng.random((w.batch, w.q_len, L)) < density
+    for b in range(w.batch):
+        ctx = int(w.context_lens[b])
+        m[b, np.arange(w.q_len), ctx - w.q_len + np.arange(w.q_len)] = True
+    if empty_rows:
+        m[0, :empty_rows] = False
+    return m
+
+
+def run_mods(inp, causal, slopes, mask):
+    import exact_paged_causal_amd as atlas
+    w = inp.w
+    max_ctx = int(inp.layout.page_table.shape[1]) * w.page_size
+    words = (max_ctx + 31) // 32
+    return atlas.atlas_attend_mods(
+        inp.q, inp.k, inp.v, inp.page_table, inp.context_lens, w.scale, causal=causal,
+        alibi_slopes=None if slopes is None else torch.from_numpy(slopes).cuda(),
+        mask_bits=None if mask is None else pack_mask(mask, words),
+        window=inp.window, sink_tokens=inp.sinks, softcap=inp.softcap)
+
+
+def check_mods(inp, out, lse, causal, slopes, mask, what, rows=None):
+    w = inp.w
+    src = H.OracleSource(inp)
+    out_h, lse_h = H.to_f32_numpy(out), H.to_f32_numpy(lse)
+    hm = oracle.default_head_map(w.hq, w.hkv)
+    for b in range(w.batch):
+        k, v = src.kv(b)
+        L = int(w.context_lens[b])
+        sel = np.arange(w.q_len) if rows is None else np.asarray(rows)
+        q = H.to_f32_numpy(inp.q[b])[sel]
+        pos = (L - w.q_len + np.arange(w.q_len))[sel].astype(np.int32)
+        win = int(w.window[b]) if w.window is not None else 0
+        snk = int(w.sinks[b]) if (w.sinks is not None and win > 0) else 0
+        cap = float(w.softcap[b]) if w.softcap is not None else 0.0
+        ro, rl = oracle.attend(q, k, v, pos, hm, w.scale, win, snk, cap, causal=causal,
+                               alibi=None if slopes is None else slopes.astype(np.float64),
+                               mask=None if mask is None else mask[b][sel][:, :L], allow_empty=True)
+        got_o, got_l = out_h[b][sel], lse_h[b][sel]
+        empty = np.isneginf(rl)
+        assert np.isnan(got_o[empty]).all() and np.isneginf(got_l[empty]).all(), f"{what}: empty rows"
+        H.assert_close(got_o[~empty], ro[~empty], w.dtype, f"{what} out[b={b}]")
+        H.assert_close(got_l[~empty], rl[~empty], w.dtype, f"{what} lse[b={b}]")
+
+
+def wl(dtype, hq, hkv, d, page, q_len, lens, seed=41, window=None, sinks=None, softcap=None):
+    lens = np.asarray(lens, np.int32)
+    w = workloads.Workload("mods_case", seed=seed, batch=len(lens), hq=hq, hkv=hkv, head_dim=d, page_size=page,
+                           dtype=dtype, q_len=q_len, context_lens=lens, scale=1.0 / math.sqrt(d),
+                           shuffle_pages=True)
+    if window is not None:
+        w.window = np.asarray(window, np.int32)
+        w.sinks = np.asarray(sinks, np.int32)
+        w.softcap = np.asarray(softcap, np.float32)
+    return w
+
+
+CASES = [
+    # (dtype, hq, hkv, d, page, q_len, lens, causal, alibi, mask density or None)
+    ("f32", 8, 2, 64, 16, 1, (300, 77), True, True, 0.7),        # decode-shaped, split path
+    ("f32", 8, 2, 64, 16, 16, (256, 40), False, True, None),     # short non-causal suffix
+    ("f32", 4, 1, 128, 8, 37, (37, 100), False, False, 0.5),
+    ("bf16", 8, 2, 128, 16, 20, (500, 33), False, False, 0.5),
+    ("bf16", 4, 4, 64, 32, 1, (1000,), True, True, 0.3),
+    ("bf16", 8, 2, 128, 16, 100, (100, 300), False, True, None),  # tiled
+    ("bf16", 2, 2, 64, 64, 257, (400, 257), False, False, 0.6),
+    ("bf16", 6, 2, 128, 1, 70, (80,), False, True, 0.8),          # tiled, one-token pages
+    ("bf16", 16, 1, 64, 64, 96, (200,), True, True, 0.5),
+    ("f32", 8, 2, 128, 16, 100, (100, 300), False, True, 0.7),    # fp32 tiled
+    ("f32", 4, 1, 64, 32, 70, (500,), True, True, None),
+    ("f32", 2, 2, 128, 128, 257, (3000,), False, False, 0.4),
+]
+
+
+@pytest.mark.parametrize("case", CASES, ids=lambda c: f"{c[0]}-h{c[1]}x{c[2]}-d{c[3]}-p{c[4]}-q{c[5]}-"
+                                                     f"{'c' if c[7] else 'nc'}{'-alibi' if c[8] else ''}"
+                                                     f"{'-mask' if c[9] else ''}")
+def test_mods_match_oracle(case):
+    dtype, hq, hkv, d, page, q_len, lens, causal, alibi, density = case
+    say(f"[mods] {case}")
+    w = wl(dtype, hq, hkv, d, page, q_len, lens)
+    inp = H.build(w, poison=True)
+    slopes = alibi_slopes(hq) if alibi else None
+    mask = make_mask(w, density, seed=7) if density else None
+    out, lse = run_mods(inp, causal, slopes, mask)
+    torch.cuda.synchronize()
+    check_mods(inp, out, lse, causal, slopes, mask, str(case))
+
+
+@pytest.mark.parametrize("dtype,q_len", [("bf16", 130), ("f32", 130), ("bf16", 9), ("f32", 1)])
+def test_mods_with_window_sinks_softcap(dtype, q_len):
+    w = wl(dtype, 8, 2, 128, 32, q_len, (900, 400), window=(200, 64), sinks=(3, 0), softcap=(5.0, 0.0))
+    say(f"[mods] window / sinks / softcap + ALiBi + mask, {dtype} q_len={q_len}")
+    inp = H.build(w)
+    slopes = alibi_slopes(8)
+    mask = make_mask(w, 0.8, seed=8)
+    out, lse = run_mods(inp, True, slopes, mask)
+    torch.cuda.synchronize()
+    check_mods(inp, out, lse, True, slopes, mask, f"variants {dtype} {q_len}")
+
+
+@pytest.mark.parametrize("dtype,q_len", [("bf16", 100), ("f32", 100), ("bf16", 12), ("f32", 12)])
+def test_fully_masked_rows_are_nan(dtype, q_len):
+    w = wl(dtype, 4, 2, 64, 16, q_len, (150, 120))
+    say(f"[mods] fully masked rows, {dtype} q_len={q_len}")
+    inp = H.build(w)
+    mask = make_mask(w, 0.5, seed=9, empty_rows=5)
+    out, lse = run_mods(inp, False, None, mask)
+    torch.cuda.synchronize()
+    assert torch.isnan(out[0, :5]).all() and torch.isneginf(lse[0, :5]).all()
+    check_mods(inp, out, lse, False, None, mask, f"empty rows {dtype}")
+
+
+@pytest.mark.parametrize("dtype,q_len", [("bf16", 100), ("f32", 100), ("bf16", 10), ("f32", 1)])
+def test_no_op_mods_equal_the_plain_call(dtype, q_len):
+    """causal = 1 without slopes or mask runs the plain kernels: bit-identical
+    to atlas_attend_prefill."""
+    import exact_paged_causal_amd as atlas
+    w = wl(dtype, 8, 2, 128, 16, q_len, (300, q_len + 5))
+    say(f"[mods] no-op mods, {dtype} q_len={q_len}")
+    inp = H.build(w)
+    o1, l1 = run_mods(inp, True, None, None)
+    o1, l1 = o1.clone(), l1.clone()
+    o2, l2 = atlas.atlas_attend_prefill(inp.q, inp.k, inp.v, inp.page_table, inp.context_lens, w.scale)
+    torch.cuda.synchronize()
+    assert torch.equal(o1, o2) and torch.equal(l1, l2)
+
+
+@pytest.mark.parametrize("causal", [True, False])
+def test_mods_causal_prefill_full_size_sampled(causal):
+    """The causal-prefill shape (S=8192, Hq=32, Hkv=8, D=128, bf16) with ALiBi
+    slopes, causal and non-causal: every head of a sample of rows."""
+    w = workloads.make("causal_prefill")
+    say(f"[mods] causal_prefill shape with ALiBi, causal={causal}")
+    inp = H.build(w)
+    slopes = alibi_slopes(w.hq)
+    out, lse = run_mods(inp, causal, slopes, None)
+    torch.cuda.synchronize()
+    rows = [0, 1, 63, 64, 4095, 4096, 8190, 8191]
+    check_mods(inp, out, lse, causal, slopes, None, f"full size causal={causal}", rows=rows)
+    assert not torch.isnan(out).any()
