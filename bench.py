@@ -22,7 +22,8 @@ step's); the K/V append of a decode step and of a whole prefill history is
 timed under "next": "append_kv", the prefill shape with a window, sinks
 and a softcap under "next": "prefill_variants", and the same shape with
 fp32 Q/K/V (split fp16 operands on the matrix cores) under
-"next": "prefill_f32".
+"next": "prefill_f32", and atlas_attend_mods on the same bf16 shape (ALiBi
+causal and non-causal, a block-diagonal document mask) under "next": "mods".
 
 Prints one JSON line.  `--gpus N` with N > 1 exits: this path runs on one GPU.
 """
@@ -235,6 +236,37 @@ def prefill_f32_report(torch, np, workloads, atlas, calls=10):
     return {"us": round(us, 1), "flop": flops, "TFLOPs": round(tf, 1),
             "frac_mfma_fp16": round(3.0 * tf / BF16_PEAK_TFLOPS, 4),
             "note": "fp32 Q/K/V; every product as three fp16 matrix products (hi.hi + lo.hi + hi.lo)"}
+
+
+def mods_report(torch, np, p, atlas, calls=10):
+    """atlas_attend_mods on the causal-prefill shape (S=8192, Hq=32, Hkv=8,
+    D=128, bf16): ALiBi slopes 2^(-8(h+1)/Hq) on causal and on non-causal rows,
+    and a causal block-diagonal mask of four 2048-token documents (packed
+    sequences).  TFLOP/s counts the visible pairs; the tiled kernel applies
+    the mask per element and does not skip blocks a mask hides entirely."""
+    pw = p["w"]
+    S, hq, d = pw.q_len, pw.hq, pw.head_dim
+    slopes = torch.tensor(2.0 ** (-8.0 * (np.arange(hq) + 1) / hq), dtype=torch.float32, device="cuda")
+    doc = 2048
+    words = (int(p["pt"].shape[1]) * pw.page_size + 31) // 32
+    j = np.arange(words * 32)
+    qpos = np.arange(S)
+    keep = (j[None, :] // doc == qpos[:, None] // doc) & (j[None, :] <= qpos[:, None])
+    bits = np.packbits(keep, axis=-1, bitorder="little").view("<u4").astype(np.uint32).view(np.int32)
+    mask = torch.from_numpy(np.ascontiguousarray(bits)[None]).cuda()
+    out = torch.empty(1, S, hq, d, dtype=torch.float32, device="cuda")
+    lse = torch.empty(1, S, hq, dtype=torch.float32, device="cuda")
+    rep = {}
+    for name, kw, pairs in (("alibi_causal", dict(alibi_slopes=slopes), S * (S + 1) / 2),
+                            ("alibi_noncausal", dict(alibi_slopes=slopes, causal=False), float(S) * S),
+                            ("document_mask", dict(mask_bits=mask), (S // doc) * doc * (doc + 1) / 2)):
+        call = lambda: atlas.atlas_attend_mods(p["q"], p["k"], p["v"], p["pt"], p["ctx"], pw.scale, out=out,
+                                               lse=lse, **kw)
+        us = _median_call_us(torch, np, call, calls=calls)
+        fl = 4.0 * d * hq * pairs
+        rep[name] = {"us": round(us, 1), "flop": fl, "TFLOPs": round(fl / us / 1e6, 1)}
+    rep["note"] = "bf16 tiled kernel; TFLOP/s over visible pairs; masked blocks are computed, not skipped"
+    return rep
 
 
 def append_report(torch, np, workloads, atlas):
@@ -514,6 +546,7 @@ def main():
         if p is not None:
             result["next"]["prefill_variants"] = prefill_variants_report(torch, np, p, atlas)
             result["next"]["prefill_f32"] = prefill_f32_report(torch, np, workloads, atlas)
+            result["next"]["mods"] = mods_report(torch, np, p, atlas)
         print("bench: fused regeneration timed", file=sys.stderr, flush=True)
     if not args.no_workloads:
         # Every synthetic workload's throughput (the long-context decode and
