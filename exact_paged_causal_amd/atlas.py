@@ -117,12 +117,31 @@ class AttnMods(ctypes.Structure):
     ]
 
 
+class CacheConfig(ctypes.Structure):
+    """atlas_cache_config."""
+    _fields_ = [
+        ("hot_cache_bytes", ctypes.c_int64),
+        ("page_bytes", ctypes.c_int64),
+        ("page_size", ctypes.c_int32),
+        ("recent_tokens", ctypes.c_int32),
+        ("admit_regenerated", ctypes.c_int32),
+        ("reserved", ctypes.c_int32),
+    ]
+
+
+class CacheStats(ctypes.Structure):
+    """atlas_cache_stats."""
+    _fields_ = [(n, ctypes.c_int64) for n in ("capacity_pages", "resident_pages", "resident_bytes", "hits",
+                                              "misses", "admitted", "evicted")]
+
+
 EXPORTS = ("atlas_abi_version", "atlas_status_str", "atlas_last_error",
            "atlas_decode_workspace_bytes", "atlas_prefill_workspace_bytes",
            "atlas_attend_decode", "atlas_attend_prefill", "atlas_attend_mods", "atlas_regenerate_pages",
            "atlas_attend_decode_regen", "atlas_append_kv", "atlas_pool_create", "atlas_pool_destroy",
            "atlas_pool_alloc", "atlas_pool_retain", "atlas_pool_release", "atlas_pool_free_pages",
-           "atlas_pool_refcount")
+           "atlas_pool_refcount", "atlas_cache_create", "atlas_cache_destroy", "atlas_cache_plan",
+           "atlas_cache_drop_sequence", "atlas_cache_get_stats")
 
 
 def _load():
@@ -165,6 +184,18 @@ def _load():
     lib.atlas_pool_free_pages.argtypes = [ctypes.c_void_p]
     lib.atlas_pool_refcount.restype = ctypes.c_int32
     lib.atlas_pool_refcount.argtypes = [ctypes.c_void_p, ctypes.c_int32]
+    lib.atlas_cache_create.restype = ctypes.c_int32
+    lib.atlas_cache_create.argtypes = [ctypes.POINTER(CacheConfig), ctypes.POINTER(ctypes.c_void_p)]
+    lib.atlas_cache_destroy.restype = None
+    lib.atlas_cache_destroy.argtypes = [ctypes.c_void_p]
+    i32p, i64p = ctypes.POINTER(ctypes.c_int32), ctypes.POINTER(ctypes.c_int64)
+    lib.atlas_cache_plan.restype = ctypes.c_int32
+    lib.atlas_cache_plan.argtypes = [ctypes.c_void_p, ctypes.c_int32, ctypes.c_int32, i64p, i32p, ctypes.c_int32,
+                                     i32p, i32p, ctypes.c_int32, i32p]
+    lib.atlas_cache_drop_sequence.restype = ctypes.c_int32
+    lib.atlas_cache_drop_sequence.argtypes = [ctypes.c_void_p, ctypes.c_int64]
+    lib.atlas_cache_get_stats.restype = ctypes.c_int32
+    lib.atlas_cache_get_stats.argtypes = [ctypes.c_void_p, ctypes.POINTER(CacheStats)]
     if lib.atlas_abi_version() != ABI_VERSION:
         raise ImportError(f"libatlas ABI {lib.atlas_abi_version()} != binding ABI {ABI_VERSION}")
     return lib
@@ -496,3 +527,59 @@ class PagePool:
 
     def refcount(self, page: int) -> int:
         return int(lib.atlas_pool_refcount(self._h, int(page)))
+
+
+class HotCache:
+    """Byte-bounded hot-page cache of the C ABI (atlas_cache_*): plans which
+    pages of a call are resident (a hot-pool slot) and which are regenerated
+    in the kernel (ATLAS_PAGE_REGENERATE)."""
+
+    _h = None
+
+    def __init__(self, hot_cache_bytes: int, page_bytes: int, page_size: int, recent_tokens: int = 0,
+                 admit_regenerated: bool = True):
+        cfg = CacheConfig(int(hot_cache_bytes), int(page_bytes), int(page_size), int(recent_tokens),
+                          1 if admit_regenerated else 0, 0)
+        h = ctypes.c_void_p()
+        st = lib.atlas_cache_create(ctypes.byref(cfg), ctypes.byref(h))
+        if st != ATLAS_OK:
+            raise AtlasError(st, "atlas_cache_create")
+        self._h = h
+
+    def close(self):
+        if self._h:
+            lib.atlas_cache_destroy(self._h)
+            self._h = None
+
+    def __del__(self):
+        self.close()
+
+    def plan(self, layer: int, seq_ids, context_lens, max_pages_per_seq: int):
+        """Returns (page_table int32 [B][max_pages_per_seq], jobs int32 [n][3]) as numpy arrays."""
+        import numpy as np
+        ids = np.ascontiguousarray(seq_ids, dtype=np.int64)
+        ctx = np.ascontiguousarray(context_lens, dtype=np.int32)
+        B = ids.shape[0]
+        pt = np.empty((B, int(max_pages_per_seq)), dtype=np.int32)
+        max_jobs = B * int(max_pages_per_seq)  # >= the pages of the call
+        jobs = np.empty((max_jobs, 3), dtype=np.int32)
+        n = ctypes.c_int32()
+        i32p, i64p = ctypes.POINTER(ctypes.c_int32), ctypes.POINTER(ctypes.c_int64)
+        st = lib.atlas_cache_plan(self._h, int(layer), B, ids.ctypes.data_as(i64p), ctx.ctypes.data_as(i32p),
+                                  int(max_pages_per_seq), pt.ctypes.data_as(i32p), jobs.ctypes.data_as(i32p),
+                                  max_jobs, ctypes.byref(n))
+        if st != ATLAS_OK:
+            raise AtlasError(st, "atlas_cache_plan")
+        return pt, jobs[:n.value].copy()
+
+    def drop_sequence(self, seq_id: int):
+        st = lib.atlas_cache_drop_sequence(self._h, int(seq_id))
+        if st != ATLAS_OK:
+            raise AtlasError(st, "atlas_cache_drop_sequence")
+
+    def stats(self) -> dict:
+        out = CacheStats()
+        st = lib.atlas_cache_get_stats(self._h, ctypes.byref(out))
+        if st != ATLAS_OK:
+            raise AtlasError(st, "atlas_cache_get_stats")
+        return {n: int(getattr(out, n)) for n, _ in CacheStats._fields_}

@@ -20,10 +20,13 @@
 #include "../../include/atlas.h"
 #include "kernels.h"
 #include "plan.h"
+#include "status.h"
+
+namespace atlas {
 
 namespace {
-
 thread_local char g_last_error[512] = "";
+}
 
 int32_t fail(int32_t status, const char *fmt, ...)
 {
@@ -39,6 +42,15 @@ int32_t ok()
     g_last_error[0] = '\0';
     return ATLAS_OK;
 }
+
+const char *last_error() { return g_last_error; }
+
+}  // namespace atlas
+
+namespace {
+
+using atlas::fail;
+using atlas::ok;
 
 bool validate_mode()
 {
@@ -491,7 +503,7 @@ const char *atlas_status_str(int32_t status)
     }
 }
 
-const char *atlas_last_error(void) { return g_last_error; }
+const char *atlas_last_error(void) { return atlas::last_error(); }
 
 size_t atlas_decode_workspace_bytes(const atlas_attn_args *args) { return workspace_bytes(args, true); }
 

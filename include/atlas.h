@@ -324,6 +324,75 @@ int32_t atlas_pool_release(atlas_pool *pool, int32_t n, const int32_t *ids);
 int32_t atlas_pool_free_pages(const atlas_pool *pool);
 int32_t atlas_pool_refcount(const atlas_pool *pool, int32_t id);
 
+/*
+ * Byte-bounded hot-page cache (host side).  The CFR-Atlas README keeps
+ * selected K/V pages in a byte-bounded hot cache and regenerates the rest;
+ * the library owns residency, eviction and accounting, the caller picks the
+ * budget (Config::hot_cache_bytes) and the admission policy
+ * (admit_regenerated_pages, KeepRecent { recent_tokens }), and admission
+ * changes latency and residency only, never the attention result ("Core
+ * contract").
+ *
+ * The resident pages occupy a hot pool of physical pages 0 .. capacity - 1
+ * (capacity = hot_cache_bytes / page_bytes) in the caller's arenas; pages not
+ * in the pool are regenerated inside atlas_attend_decode_regen, so cold pages
+ * need no scratch memory.  A page is identified by (sequence id, layer,
+ * logical page).  All functions are thread-safe per cache; on an error
+ * nothing changes.
+ */
+typedef struct atlas_cache atlas_cache;
+
+typedef struct atlas_cache_config {
+    int64_t hot_cache_bytes;    /* residency budget */
+    int64_t page_bytes;         /* bytes one resident page occupies (K and V of all K/V heads) */
+    int32_t page_size;          /* tokens per page */
+    int32_t recent_tokens;      /* KeepRecent: pages holding any of a sequence's last recent_tokens
+                                   tokens are admitted first, evicting if needed (0: off) */
+    int32_t admit_regenerated;  /* 1: a call's other non-resident pages take the free slots */
+    int32_t reserved;           /* 0 */
+} atlas_cache_config;
+
+typedef struct atlas_cache_stats {
+    int64_t capacity_pages;
+    int64_t resident_pages;
+    int64_t resident_bytes;
+    int64_t hits;               /* resident pages read, summed over calls */
+    int64_t misses;             /* pages left to in-kernel regeneration, summed over calls */
+    int64_t admitted;           /* pages admitted (each one regeneration job) */
+    int64_t evicted;
+} atlas_cache_stats;
+
+/* Create / destroy.  ATLAS_ERR_SHAPE for non-positive sizes, ATLAS_ERR_RANGE
+ * for a capacity above 2^24 pages or admit_regenerated outside {0, 1}. */
+int32_t atlas_cache_create(const atlas_cache_config *config, atlas_cache **out);
+void atlas_cache_destroy(atlas_cache *cache);
+
+/*
+ * Plan one attention call of `layer` over `batch` sequences (host arrays):
+ * seq_ids [batch] (distinct), context_lens [batch] in [1, max_pages_per_seq *
+ * page_size].  In order: the call's resident pages are hits; with
+ * recent_tokens, each sequence's recent pages that are not resident are
+ * admitted, newest first, into a free slot or in place of the least recently
+ * used page this call does not read (pages outside every recent window
+ * before those inside one; O(capacity) per eviction); with
+ * admit_regenerated, the call's other non-resident pages take the slots
+ * still free, in (sequence, page) order.  Writes page_table [batch]
+ * [max_pages_per_seq] (host): each page's slot, or ATLAS_PAGE_REGENERATE for
+ * pages left cold and for entries past the context; and admit_jobs
+ * [*n_jobs][3] = (batch row, logical page, slot) for atlas_regenerate_pages,
+ * which must run before the attention call reads the admitted slots.
+ * max_jobs must be >= min(pages in the call, capacity) (ATLAS_ERR_SHAPE).
+ */
+int32_t atlas_cache_plan(atlas_cache *cache, int32_t layer, int32_t batch, const int64_t *seq_ids,
+                         const int32_t *context_lens, int32_t max_pages_per_seq, int32_t *page_table,
+                         int32_t *admit_jobs, int32_t max_jobs, int32_t *n_jobs);
+
+/* Free every resident page of a sequence (all layers), e.g. when it ends. */
+int32_t atlas_cache_drop_sequence(atlas_cache *cache, int64_t seq_id);
+
+/* Residency and counters. */
+int32_t atlas_cache_get_stats(atlas_cache *cache, atlas_cache_stats *out);
+
 #ifdef __cplusplus
 }
 #endif

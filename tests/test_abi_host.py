@@ -27,7 +27,8 @@ def test_header_declares_the_boundary():
                             "atlas_regenerate_pages", "atlas_attend_decode_regen", "atlas_append_kv",
                             "atlas_pool_create", "atlas_pool_destroy", "atlas_pool_alloc",
                             "atlas_pool_retain", "atlas_pool_release", "atlas_pool_free_pages",
-                            "atlas_pool_refcount"])
+                            "atlas_pool_refcount", "atlas_cache_create", "atlas_cache_destroy",
+                            "atlas_cache_plan", "atlas_cache_drop_sequence", "atlas_cache_get_stats"])
 
 
 def test_library_exports_every_declared_symbol():
@@ -60,6 +61,9 @@ def test_binding_structs_mirror_the_header():
     assert ctypes.sizeof(A.RegenArgs) == 8 + 4 * 8 + 8 * 3
     assert [f[0] for f in A.AttnMods._fields_] == _struct_offsets_from_header("atlas_attn_mods")
     assert ctypes.sizeof(A.AttnMods) == 4 * 2 + 8 * 2
+    assert [f[0] for f in A.CacheConfig._fields_] == _struct_offsets_from_header("atlas_cache_config")
+    assert [f[0] for f in A.CacheStats._fields_] == _struct_offsets_from_header("atlas_cache_stats")
+    assert ctypes.sizeof(A.CacheConfig) == 8 * 2 + 4 * 4 and ctypes.sizeof(A.CacheStats) == 8 * 7
 
 
 FAKE = 0x10000  # never dereferenced: every case below fails host validation first
