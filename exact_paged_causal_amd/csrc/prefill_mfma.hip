@@ -313,9 +313,40 @@ __global__ __launch_bounds__(512) void prefill_kernel(PrefillArgs a)
         // position (causal), or not inside every row's window or sink range.
         const int k0 = kb * kBN;
         if constexpr (MODS) {
-            // ALiBi bias and mask bits on every element; non-causal rows mask
-            // only keys past the context.
-            if (slope_raw != 0.0f || mrow || k0 + kBN - 1 > (causal ? pos_lo : key_hi) ||
+            // ALiBi: on a block wholly at or left of this row's position the
+            // bias -slope |pos - j| is linear in j, c + slope (j - k0 - 4 half)
+            // with c per lane and block, one FMA with a constant per element;
+            // wholly right of it (non-causal rows) the mirror image; only
+            // blocks crossing the position take the absolute value.
+            if (slope_raw != 0.0f) {
+                if (k0 + kBN - 1 <= pos) {
+                    const float c = slope_raw * (float)(k0 + 4 * half - pos);
+#pragma unroll
+                    for (int t = 0; t < 2; ++t)
+#pragma unroll
+                        for (int e = 0; e < 16; ++e)
+                            st[t][e] += fmaf(slope_raw, (float)(32 * t + 8 * (e >> 2) + (e & 3)), c);
+                } else if (k0 >= pos) {
+                    const float c = slope_raw * (float)(pos - k0 - 4 * half);
+#pragma unroll
+                    for (int t = 0; t < 2; ++t)
+#pragma unroll
+                        for (int e = 0; e < 16; ++e)
+                            st[t][e] += fmaf(-slope_raw, (float)(32 * t + 8 * (e >> 2) + (e & 3)), c);
+                } else {
+#pragma unroll
+                    for (int t = 0; t < 2; ++t)
+#pragma unroll
+                        for (int e = 0; e < 16; ++e) {
+                            const int j = k0 + 32 * t + 8 * (e >> 2) + 4 * half + (e & 3);
+                            st[t][e] -= slope_raw * fabsf((float)(pos - j));
+                        }
+                }
+            }
+            // Mask bits on every element when given; otherwise only blocks
+            // some row does not see whole (non-causal rows: keys past the
+            // context).
+            if (mrow || k0 + kBN - 1 > (causal ? pos_lo : key_hi) ||
                 !(W <= 0 || k0 > pos_hi - W || k0 + kBN - 1 < S)) {
 #pragma unroll
                 for (int t = 0; t < 2; ++t)
@@ -325,7 +356,8 @@ __global__ __launch_bounds__(512) void prefill_kernel(PrefillArgs a)
                         const int j = k0 + jo;
                         const uint32_t mw = t ? mw1 : mw0;
                         const bool vis = j <= posv && (W <= 0 || j > pos - W || j < S) && ((mw >> (jo & 31)) & 1u);
-                        st[t][e] = vis ? st[t][e] - slope_raw * fabsf((float)(pos - j)) : -INFINITY;
+                        if (!vis)
+                            st[t][e] = -INFINITY;
                     }
             }
         } else {

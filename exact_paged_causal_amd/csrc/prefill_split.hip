@@ -378,11 +378,42 @@ __global__ __launch_bounds__(512) void prefill_split_kernel(PrefillArgs a)
                 for (int e = 0; e < 16; ++e)
                     st[t][e] = back * tanhf(st[t][e] * inv);
         }
-        // Mask only blocks some row does not see whole.
         const int k0 = kb * kBN;
+        if constexpr (MODS) {
+            // ALiBi: linear in j on blocks wholly on one side of this row's
+            // position (one FMA with a constant per element), the absolute
+            // value only on blocks crossing it.
+            if (slope_u != 0.0f) {
+                if (k0 + kBN - 1 <= pos) {
+                    const float c = slope_u * (float)(k0 + 4 * half - pos);
+#pragma unroll
+                    for (int t = 0; t < 2; ++t)
+#pragma unroll
+                        for (int e = 0; e < 16; ++e)
+                            st[t][e] += fmaf(slope_u, (float)(32 * t + 8 * (e >> 2) + (e & 3)), c);
+                } else if (k0 >= pos) {
+                    const float c = slope_u * (float)(pos - k0 - 4 * half);
+#pragma unroll
+                    for (int t = 0; t < 2; ++t)
+#pragma unroll
+                        for (int e = 0; e < 16; ++e)
+                            st[t][e] += fmaf(-slope_u, (float)(32 * t + 8 * (e >> 2) + (e & 3)), c);
+                } else {
+#pragma unroll
+                    for (int t = 0; t < 2; ++t)
+#pragma unroll
+                        for (int e = 0; e < 16; ++e) {
+                            const int j = k0 + 32 * t + 8 * (e >> 2) + 4 * half + (e & 3);
+                            st[t][e] -= slope_u * fabsf((float)(pos - j));
+                        }
+                }
+            }
+        }
+        // Mask only blocks some row does not see whole (and, with mask bits,
+        // every block).
         const bool all_causal = k0 + kBN - 1 <= (causal ? pos_lo : key_hi);
         const bool all_window = W <= 0 || k0 > pos_hi - W || k0 + kBN - 1 < S;
-        if (!(all_causal && all_window) || (MODS && (slope_u != 0.0f || mrow))) {
+        if (!(all_causal && all_window) || (MODS && mrow)) {
 #pragma unroll
             for (int t = 0; t < 2; ++t)
 #pragma unroll
@@ -390,10 +421,8 @@ __global__ __launch_bounds__(512) void prefill_split_kernel(PrefillArgs a)
                     const int jo = 32 * t + 8 * (e >> 2) + 4 * half + (e & 3);
                     const int j = k0 + jo;
                     bool vis = j <= posv && (W <= 0 || j > pos - W || j < S);
-                    if constexpr (MODS) {
+                    if constexpr (MODS)
                         vis = vis && (((t ? mw1 : mw0) >> (jo & 31)) & 1u);
-                        st[t][e] -= slope_u * fabsf((float)(pos - j));
-                    }
                     if (!vis)
                         st[t][e] = -INFINITY;
                 }
