@@ -245,8 +245,9 @@ def mods_report(torch, np, p, atlas, calls=10):
     """atlas_attend_mods on the causal-prefill shape (S=8192, Hq=32, Hkv=8,
     D=128, bf16): ALiBi slopes 2^(-8(h+1)/Hq) on causal and on non-causal rows,
     and a causal block-diagonal mask of four 2048-token documents (packed
-    sequences).  TFLOP/s counts the visible pairs; the tiled kernel applies
-    the mask per element and does not skip blocks a mask hides entirely."""
+    sequences).  TFLOP/s counts the visible pairs; the tiled kernel drops the
+    key blocks a mask hides from every row of a query block and applies the
+    mask per element inside the others."""
     pw = p["w"]
     S, hq, d = pw.q_len, pw.hq, pw.head_dim
     slopes = torch.tensor(2.0 ** (-8.0 * (np.arange(hq) + 1) / hq), dtype=torch.float32, device="cuda")
@@ -268,7 +269,7 @@ def mods_report(torch, np, p, atlas, calls=10):
         us = _median_call_us(torch, np, call, calls=calls)
         fl = 4.0 * d * hq * pairs
         rep[name] = {"us": round(us, 1), "flop": fl, "TFLOPs": round(fl / us / 1e6, 1)}
-    rep["note"] = "bf16 tiled kernel; TFLOP/s over visible pairs; masked blocks are computed, not skipped"
+    rep["note"] = "bf16 tiled kernel; TFLOP/s over visible pairs; key blocks a mask hides entirely are skipped"
     return rep
 
 

@@ -69,6 +69,7 @@ constexpr int kBN = 64;              // keys per block
 constexpr int kPad = 24;             // LDS row padding (elements): conflict-free K rows, best transposed V reads
 constexpr float kRescaleSlack = 8.0f;  // log2 units the running max may lag
 constexpr int kPidWindow = 2048;       // page ids staged in LDS at a time
+constexpr int kMaxListed = 4096;       // candidate key blocks a mask can thin out (longer: all computed)
 
 // 16-byte alignment lets every K/V row piece move with one ds_read_b128 /
 // ds_write_b128 (without it the compiler splits them into 4-byte pairs).
@@ -241,20 +242,65 @@ __global__ __launch_bounds__(512) void prefill_kernel(PrefillArgs a)
     const int n_iter = kb_last < 0 ? 0 : n_sink_blk + (kb_last - first_win + 1);
     auto block_at = [&](int it) { return it < n_sink_blk ? it : first_win + (it - n_sink_blk); };
 
-    if (n_iter > 0)
-        stage_pids((block_at(0) * kBN) >> ps);
+    // MODS with mask bits: the candidate blocks whose mask words are zero for
+    // every row of this workgroup are dropped; the rest are listed in order
+    // (wave 0 compacts the flags with a ballot).  The test is conservative:
+    // a listed block may still be wholly hidden by the causal or window rule.
+    __shared__ int32_t s_blk[MODS ? kMaxListed : 1];
+    __shared__ uint8_t s_flag[MODS ? kMaxListed : 1];
+    __shared__ int32_t s_count;
+    int n_run = n_iter;
+    bool listed = false;
+    if constexpr (MODS) {
+        if (a.mods.mask && n_iter > 0 && n_iter <= kMaxListed) {
+            listed = true;
+            for (int i = tid; i < n_iter; i += 512)
+                s_flag[i] = 0;
+            __syncthreads();
+            const int rows_pos = i1 - i0;
+            const int wl = a.mods.mask_words - 1;
+            for (int idx = tid; idx < n_iter * rows_pos; idx += 512) {
+                const int c = idx / rows_pos;
+                const int pp = idx - c * rows_pos;
+                const uint32_t *m = a.mods.mask + ((int64_t)b * a.q_len + i0 + pp) * a.mods.mask_words;
+                const int w = (block_at(c) * kBN) >> 5;
+                if ((m[w < wl ? w : wl] | m[w + 1 < wl ? w + 1 : wl]) != 0u)
+                    s_flag[c] = 1;
+            }
+            __syncthreads();
+            if (wave == 0) {
+                int base = 0;
+                for (int c0 = 0; c0 < n_iter; c0 += 64) {
+                    const int c = c0 + lane;
+                    const bool f = c < n_iter && s_flag[c];
+                    const uint64_t bal = __ballot(f);
+                    if (f)
+                        s_blk[base + __popcll(bal & ((1ull << lane) - 1ull))] = block_at(c);
+                    base += __popcll(bal);
+                }
+                if (lane == 0)
+                    s_count = base;
+            }
+            __syncthreads();
+            n_run = s_count;
+        }
+    }
+    auto run_block = [&](int it) { return (MODS && listed) ? s_blk[it] : block_at(it); };
+
+    if (n_run > 0)
+        stage_pids((run_block(0) * kBN) >> ps);
     __syncthreads();  // page ids staged
-    if (n_iter > 0) {
-        fetch(block_at(0));
+    if (n_run > 0) {
+        fetch(run_block(0));
         stash(0);
     }
     __syncthreads();
 
-    for (int it = 0; it < n_iter; ++it) {
-        const int kb = block_at(it);
+    for (int it = 0; it < n_run; ++it) {
+        const int kb = run_block(it);
         const int cur = it & 1;
-        const bool more = it + 1 < n_iter;
-        const int kb_next = more ? block_at(it + 1) : kb;
+        const bool more = it + 1 < n_run;
+        const int kb_next = more ? run_block(it + 1) : kb;
         if (more && (((kb_next * kBN + kBN - 1) >> ps) - pid_base) >= kPidWindow) {
             // Uniform across the workgroup: move the page-id window forward.
             __syncthreads();

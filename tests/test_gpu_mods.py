@@ -189,3 +189,25 @@ def test_mods_causal_prefill_full_size_sampled(causal):
     rows = [0, 1, 63, 64, 4095, 4096, 8190, 8191]
     check_mods(inp, out, lse, causal, slopes, None, f"full size causal={causal}", rows=rows)
     assert not torch.isnan(out).any()
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+def test_block_sparse_document_mask(dtype):
+    """Causal rows inside documents of 150 tokens (block-diagonal mask): the
+    bf16 tiled kernel drops the key blocks no row of a query block sees.
+    The first 64 query positions of sequence 0 see nothing at all (a whole
+    query block with no listed key block): NaN with lse = -inf."""
+    w = wl(dtype, 8, 2, 128, 16, 700, (700, 900))
+    say(f"[mods] document mask, {dtype}")
+    inp = H.build(w, poison=True)
+    L = int(inp.layout.page_table.shape[1]) * w.page_size
+    mask = np.zeros((w.batch, w.q_len, L), bool)
+    j = np.arange(L)
+    for b in range(w.batch):
+        pos = int(w.context_lens[b]) - w.q_len + np.arange(w.q_len)
+        mask[b] = (j[None, :] // 150) == (pos[:, None] // 150)
+    mask[0, :64] = False
+    out, lse = run_mods(inp, True, None, mask)
+    torch.cuda.synchronize()
+    assert torch.isnan(out[0, :64]).all() and torch.isneginf(lse[0, :64]).all()
+    check_mods(inp, out, lse, True, None, mask, f"document mask {dtype}")
