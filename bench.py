@@ -26,7 +26,8 @@ fp32 Q/K/V (split fp16 operands on the matrix cores) under
 causal and non-causal, a block-diagonal document mask) under "next": "mods";
 the long-context decode through the hot-page cache (atlas_cache_plan ->
 regenerate admitted pages -> decode with the rest generated in the kernel)
-under "next": "hot_cache".
+under "next": "hot_cache"; short prefill chunks behind a 32768-token history
+(the tiled kernels with key splits) under "next": "chunked_prefill".
 
 Prints one JSON line.  `--gpus N` with N > 1 exits: this path runs on one GPU.
 """
@@ -326,6 +327,33 @@ def cache_report(torch, np, workloads, atlas, calls=10):
     return rep
 
 
+def chunked_prefill_report(torch, np, workloads, atlas, calls=10):
+    """Prefill chunks of 128 and 512 queries behind a 32768-token history
+    (B=1, Hq=32, Hkv=8, D=128, pages of 128), bf16 and fp32: few query blocks,
+    so the tiled kernels split each block's keys across workgroups and the
+    LSE merge combines them.  TFLOP/s over the visible pairs."""
+    rep = {}
+    for dtype, q_len in (("bf16", 128), ("bf16", 512), ("f32", 512)):
+        L = 32768
+        w = workloads.make("causal_prefill", dtype=dtype, q_len=q_len, context_lens=np.array([L], np.int32))
+        lay = workloads.page_layout(w)
+        k, v = _arena(torch, workloads, np, w, lay)
+        q = workloads.randn(workloads.query_shape(w), seed=3, dtype=dtype, device="cuda")
+        pt = torch.from_numpy(lay.page_table).cuda()
+        ctx = torch.from_numpy(w.context_lens).cuda()
+        args, _ = atlas.make_attn_args(q, k, v, pt, ctx, w.scale)
+        ws = torch.empty(atlas.atlas_prefill_workspace_bytes(args), dtype=torch.uint8, device="cuda")
+        out = torch.empty(workloads.query_shape(w), dtype=torch.float32, device="cuda")
+        lse = torch.empty(1, q_len, w.hq, dtype=torch.float32, device="cuda")
+        call = lambda: atlas.atlas_attend_prefill(q, k, v, pt, ctx, w.scale, out=out, lse=lse, workspace=ws)
+        us = _median_call_us(torch, np, call, calls=calls)
+        fl = 4.0 * w.head_dim * w.hq * (q_len * L - q_len * (q_len - 1) / 2)
+        rep[f"{dtype}_q{q_len}_L{L}"] = {"us": round(us, 1), "flop": fl, "TFLOPs": round(fl / us / 1e6, 1)}
+        del k, v
+    rep["note"] = "tiled prefill with key splits + LSE merge (workgroups per query block x splits)"
+    return rep
+
+
 def append_report(torch, np, workloads, atlas):
     """K/V append: the long-context decode step's write of one new token per
     sequence (B=8, Hkv=8, D=64, fp32, into pages of 512), and a bulk append of
@@ -605,6 +633,7 @@ def main():
             result["next"]["prefill_variants"] = prefill_variants_report(torch, np, p, atlas)
             result["next"]["prefill_f32"] = prefill_f32_report(torch, np, workloads, atlas)
             result["next"]["mods"] = mods_report(torch, np, p, atlas)
+            result["next"]["chunked_prefill"] = chunked_prefill_report(torch, np, workloads, atlas)
         print("bench: fused regeneration timed", file=sys.stderr, flush=True)
     if not args.no_workloads:
         # Every synthetic workload's throughput (the long-context decode and

@@ -9,6 +9,7 @@
 // "kernel_registry": a missing kernel is loud, not silently slow).
 #include <hip/hip_runtime.h>
 
+#include <algorithm>
 #include <cmath>
 #include <cstdarg>
 #include <cstdio>
@@ -91,6 +92,8 @@ struct Plan {
     int split_tokens = 0;
     int max_splits = 0;
     int64_t rows_total = 0;
+    int tiled_npos = 0;       // tiled paths: query positions per workgroup
+    int split_blocks = 0;     // tiled paths: key blocks per split (0: no key splits)
     size_t workspace = 0;
     Path path = Path::SplitValu;
 };
@@ -189,7 +192,32 @@ int32_t check_shapes(const atlas_attn_args *a, bool decode, Plan *p)
         p->path = Path::SplitValu;
 
     if (p->path == Path::TiledPrefill || p->path == Path::TiledSplit) {
+        // Key splits when the grid would not fill the chip once (fewer
+        // workgroups than CUs, e.g. a short prefill chunk behind a long
+        // history): aim at about four per CU, at least 8 key blocks (512
+        // keys) per split, partial states within 1 GiB.  A full round (one
+        // 512-thread workgroup per CU) runs unsplit: measured, splitting it
+        // only adds the partial-state traffic.
         p->workspace = kWorkspaceHeader;
+        p->tiled_npos = 256 / gmax;
+        const int64_t n_qblocks = (a->q_len + p->tiled_npos - 1) / p->tiled_npos;
+        const int64_t wgs = n_qblocks * a->batch * hkv;
+        const int64_t max_blocks = (max_ctx + 63) / 64;
+        p->split_blocks = 0;
+        p->max_splits = 1;
+        if (wgs < 256 && max_blocks > 16) {
+            const int64_t want = (1024 + wgs - 1) / wgs;
+            int64_t sb = std::max<int64_t>(8, (max_blocks + want - 1) / want);
+            const int64_t per_split = rows * (int64_t)(a->head_dim + 2) * 4;
+            while ((max_blocks + sb - 1) / sb > 1 && per_split * ((max_blocks + sb - 1) / sb) > (INT64_C(1) << 30))
+                sb *= 2;
+            const int64_t ms = (max_blocks + sb - 1) / sb;
+            if (ms > 1) {
+                p->split_blocks = (int)sb;
+                p->max_splits = (int)ms;
+                p->workspace += (size_t)(per_split * ms);
+            }
+        }
         return ok();
     }
 
@@ -409,8 +437,41 @@ int32_t attend(const atlas_attn_args *a, void *stream_ptr, bool decode, const Re
         k.scale = a->scale;
         k.mods = mods;
         k.groups = p.groups;
+        k.split_blocks = p.split_blocks;
+        k.max_splits = p.max_splits;
+        if (p.split_blocks > 0) {
+            char *ws = static_cast<char *>(a->workspace) + kWorkspaceHeader;
+            k.ws_acc = reinterpret_cast<float *>(ws);
+            k.ws_ml = reinterpret_cast<float *>(ws + (size_t)p.rows_total * p.max_splits * a->head_dim * sizeof(float));
+        }
         hipError_t e = p.path == Path::TiledPrefill ? atlas::launch_prefill_mfma(k, stream)
                                                      : atlas::launch_prefill_split(k, stream);
+        if (e == hipSuccess && p.split_blocks > 0) {
+            // LSE merge of the key splits.
+            atlas::SplitArgs m{};
+            m.context_lens = a->context_lens;
+            m.window = a->window;
+            m.sinks = a->sink_tokens;
+            m.ws_acc = k.ws_acc;
+            m.ws_ml = k.ws_ml;
+            m.out = a->out;
+            m.lse = a->lse;
+            m.batch = a->batch;
+            m.q_len = a->q_len;
+            m.hq = a->num_q_heads;
+            m.hkv = a->num_kv_heads;
+            m.head_dim = a->head_dim;
+            m.max_context = p.max_context;
+            m.split_tokens = 1;
+            m.max_splits = p.max_splits;
+            m.rows_per_item = 1;
+            m.n_chunks = 1;
+            m.tiled_blocks = p.split_blocks;
+            m.tiled_npos = p.tiled_npos;
+            m.mods = mods;
+            m.groups = p.groups;
+            e = atlas::launch_merge(m, stream);
+        }
         if (e == hipErrorNotSupported)
             return fail(ATLAS_ERR_UNSUPPORTED, "no tiled prefill kernel for this shape");
         if (e != hipSuccess)

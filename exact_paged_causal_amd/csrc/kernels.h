@@ -61,6 +61,11 @@ struct SplitArgs {
     uint64_t regen_seed;
     int32_t regen_layer;
     int32_t regen;              // 0: every page is read from the arenas
+    // Merge of the tiled prefill's key splits (tiled_blocks > 0): the splits
+    // of query i are ceil(n / tiled_blocks) for the n key blocks its query
+    // block of tiled_npos positions visits (plan.h tiled_blocks).
+    int32_t tiled_blocks;
+    int32_t tiled_npos;
     Mods mods;
     HeadGroups groups;
 };
@@ -109,6 +114,13 @@ struct PrefillArgs {
     int32_t batch, q_len, hq, hkv, head_dim, page_shift, num_phys, max_pages, max_context;
     int32_t n_qblocks;          // query blocks per (sequence, K/V head)
     float scale;
+    // Key splits (split_blocks > 0): workgroup (query block, split s) visits
+    // blocks [s * split_blocks, (s + 1) * split_blocks) of the block list and
+    // writes unnormalised partial states for the merge (SplitArgs layout).
+    int32_t split_blocks;
+    int32_t max_splits;
+    float *ws_acc;              // [rows][max_splits][D]
+    float *ws_ml;               // [rows][max_splits][2]
     Mods mods;
     HeadGroups groups;
 };

@@ -37,10 +37,23 @@ __global__ __launch_bounds__(64) void merge_kernel(SplitArgs a)
     const ChunkRows cr = chunk_rows(rr / a.rows_per_item, a.rows_per_item, gsize, a.q_len, ctx);
     const int W = a.window ? a.window[b] : 0;
     const int S = a.sinks ? a.sinks[b] : 0;
-    // Non-causal rows (atlas_attend_mods) were planned over [0, ctx).
-    const SplitPlan plan = (a.mods.any && !a.mods.causal) ? plan_splits(ctx - 1, ctx - 1, 0, 0, a.split_tokens)
-                                                          : plan_splits(cr.pos_min, cr.pos_max, W, S, a.split_tokens);
-    const int n = plan.n_splits;
+    int n;
+    if (a.tiled_blocks > 0) {
+        // Key splits of the tiled prefill: this query's block of positions.
+        const int i0 = (i / a.tiled_npos) * a.tiled_npos;
+        const int i1 = i0 + a.tiled_npos < a.q_len ? i0 + a.tiled_npos : a.q_len;
+        const int pos_lo = ctx - a.q_len + i0;
+        const int pos_hi = ctx - a.q_len + i1 - 1;
+        const int key_hi = (a.mods.any && !a.mods.causal) ? (pos_hi >= 0 ? ctx - 1 : -1) : pos_hi;
+        const TiledBlocks tb = tiled_blocks(pos_lo, key_hi, W, W > 0 ? S : 0, 64);
+        n = (tb.n + a.tiled_blocks - 1) / a.tiled_blocks;
+    } else {
+        // Non-causal rows (atlas_attend_mods) were planned over [0, ctx).
+        const SplitPlan plan = (a.mods.any && !a.mods.causal) ? plan_splits(ctx - 1, ctx - 1, 0, 0, a.split_tokens)
+                                                              : plan_splits(cr.pos_min, cr.pos_max, W, S,
+                                                                            a.split_tokens);
+        n = plan.n_splits;
+    }
 
     const float *ml = a.ws_ml + row_id * a.max_splits * 2;
     const float *acc = a.ws_acc + row_id * a.max_splits * D;

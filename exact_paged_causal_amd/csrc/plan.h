@@ -114,4 +114,37 @@ ATLAS_HD ChunkRows chunk_rows(int32_t chunk, int32_t rows_per_item, int32_t grou
     return c;
 }
 
+// Key blocks of `block` keys a tiled query block visits (rows at positions
+// [pos_lo, pos_hi], last key any of them can see key_hi): with a window W the
+// blocks holding sink keys below the first window block, then the blocks from
+// the one holding pos_lo - W + 1 up to key_hi's; without one every block up
+// to key_hi's.  Visit index c maps to block c (c < n_sink) or
+// first_win + c - n_sink.
+struct TiledBlocks {
+    int32_t n;          // blocks visited (0: none)
+    int32_t n_sink;
+    int32_t first_win;
+};
+
+ATLAS_HD TiledBlocks tiled_blocks(int32_t pos_lo, int32_t key_hi, int32_t window, int32_t sinks, int32_t block)
+{
+    TiledBlocks t{0, 0, 0};
+    const int32_t kb_last = key_hi >= 0 ? key_hi / block : -1;
+    if (kb_last < 0)
+        return t;
+    if (window > 0) {
+        const int32_t lo_key = pos_lo - window + 1;
+        t.first_win = lo_key > 0 ? lo_key / block : 0;
+        const int32_t sb = (sinks + block - 1) / block;
+        t.n_sink = sinks > 0 ? (sb < t.first_win ? sb : t.first_win) : 0;
+    }
+    t.n = t.n_sink + (kb_last - t.first_win + 1);
+    return t;
+}
+
+ATLAS_HD int32_t tiled_block_at(const TiledBlocks &t, int32_t c)
+{
+    return c < t.n_sink ? c : t.first_win + (c - t.n_sink);
+}
+
 }  // namespace atlas

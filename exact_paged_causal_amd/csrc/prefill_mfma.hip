@@ -101,9 +101,14 @@ __global__ __launch_bounds__(512) void prefill_kernel(PrefillArgs a)
     const int half = lane >> 5;
 
     // Heavy-first workgroup order; consecutive ids cycle over (b, K/V head).
+    // Key splits (split_blocks > 0): consecutive workgroups of a query block
+    // take consecutive runs of its key-block list.
     const int per_q = a.batch * a.hkv;
-    const int qb_rev = blockIdx.x / per_q;
-    const int rem = blockIdx.x - qb_rev * per_q;
+    const int qs = blockIdx.x / per_q;
+    const int rem = blockIdx.x - qs * per_q;
+    const int nspl = a.split_blocks > 0 ? a.max_splits : 1;
+    const int qb_rev = qs / nspl;
+    const int split = qs - qb_rev * nspl;
     const int b = rem / a.hkv;
     const int g = rem - b * a.hkv;
     const int qblock = a.n_qblocks - 1 - qb_rev;
@@ -232,15 +237,17 @@ __global__ __launch_bounds__(512) void prefill_kernel(PrefillArgs a)
     // Key blocks the rows can see: with a window, the sink blocks and then
     // the blocks from the lowest row's window start to the diagonal (blocks
     // in between are skipped); otherwise every block up to the diagonal.
-    const int kb_last = key_hi >= 0 ? key_hi / kBN : -1;
-    int first_win = 0, n_sink_blk = 0;
-    if (W > 0 && kb_last >= 0) {
-        const int lo_key = pos_lo - W + 1;
-        first_win = lo_key > 0 ? lo_key / kBN : 0;
-        n_sink_blk = S > 0 ? min((S + kBN - 1) / kBN, first_win) : 0;
+    const TiledBlocks tbk = tiled_blocks(pos_lo, key_hi, W, S, kBN);
+    int c_lo = 0, n_iter = tbk.n;
+    if (a.split_blocks > 0) {
+        // This workgroup's run of the list; past the query block's last run
+        // there is nothing to do (uniform, before any barrier).
+        c_lo = split * a.split_blocks;
+        if (c_lo >= tbk.n)
+            return;
+        n_iter = c_lo + a.split_blocks < tbk.n ? a.split_blocks : tbk.n - c_lo;
     }
-    const int n_iter = kb_last < 0 ? 0 : n_sink_blk + (kb_last - first_win + 1);
-    auto block_at = [&](int it) { return it < n_sink_blk ? it : first_win + (it - n_sink_blk); };
+    auto block_at = [&](int it) { return tiled_block_at(tbk, c_lo + it); };
 
     // MODS with mask bits: the candidate blocks whose mask words are zero for
     // every row of this workgroup are dropped; the rest are listed in order
@@ -504,22 +511,62 @@ __global__ __launch_bounds__(512) void prefill_kernel(PrefillArgs a)
 
     // Epilogue: O = O^T / l, lse = (m + log2 l) ln 2.
     const float l_row = l_part + __shfl_xor(l_part, 32);
-    if (!row_ok)
+    if (a.split_blocks > 0) {
+        if (!row_ok)
+            return;
+        // Partial state of this split (log2-unit reference max, sum,
+        // unnormalised accumulator), merged by the LSE merge pass.
+        const int64_t slot = (((int64_t)b * a.q_len + qi) * a.hq + h) * a.max_splits + split;
+        float *pacc = a.ws_acc + slot * D;
+#pragma unroll
+        for (int dt = 0; dt < DT; ++dt)
+#pragma unroll
+            for (int e4 = 0; e4 < 4; ++e4)
+                *reinterpret_cast<f32x4 *>(pacc + 32 * dt + 8 * e4 + 4 * half) =
+                    f32x4{acc[dt][4 * e4 + 0], acc[dt][4 * e4 + 1], acc[dt][4 * e4 + 2], acc[dt][4 * e4 + 3]};
+        if (half == 0) {
+            a.ws_ml[slot * 2 + 0] = m_ref;
+            a.ws_ml[slot * 2 + 1] = l_row;
+        }
         return;
-    float *orow = a.out + (((int64_t)b * a.q_len + qi) * a.hq + h) * D;
+    }
+    // The output goes through LDS (the tile buffers are free after the loop's
+    // last barrier): each wave stages its 32 rows one 32-dim tile at a time
+    // and writes whole 128-byte row pieces (full cache lines) instead of
+    // 32-byte pieces of 32 rows.  Non-temporal: the output goes to HBM while
+    // this compute-bound kernel runs instead of lingering dirty in the cache.
     const bool any = l_row > 0.0f;
     const float inv = any ? 1.0f / l_row : __builtin_nanf("");
+    constexpr int kSt = 36;  // staged row stride (floats): 144 bytes, conflict-free 16-byte writes
+    static_assert(sizeof(sm) >= sizeof(float) * kWaves * 32 * kSt, "output staging fits the tile buffers");
+    float *stage = reinterpret_cast<float *>(&sm) + wave * (32 * kSt);
+    const int sr = lane >> 3;        // first staged row this lane stores (then + 8, + 16, + 24)
+    const int sc = (lane & 7) * 4;   // its 4 dims of the tile
 #pragma unroll
-    for (int dt = 0; dt < DT; ++dt)
+    for (int dt = 0; dt < DT; ++dt) {
 #pragma unroll
-        for (int e4 = 0; e4 < 4; ++e4) {
-            // Non-temporal: the output goes to HBM while this compute-bound
-            // kernel runs instead of lingering dirty in the last-level cache.
-            const f32x4 o = {acc[dt][4 * e4 + 0] * inv, acc[dt][4 * e4 + 1] * inv,
-                             acc[dt][4 * e4 + 2] * inv, acc[dt][4 * e4 + 3] * inv};
-            __builtin_nontemporal_store(o, reinterpret_cast<f32x4 *>(orow + 32 * dt + 8 * e4 + 4 * half));
+        for (int e4 = 0; e4 < 4; ++e4)
+            *reinterpret_cast<f32x4 *>(stage + (lane & 31) * kSt + 8 * e4 + 4 * half) =
+                f32x4{acc[dt][4 * e4 + 0] * inv, acc[dt][4 * e4 + 1] * inv, acc[dt][4 * e4 + 2] * inv,
+                       acc[dt][4 * e4 + 3] * inv};
+        __syncthreads();
+#pragma unroll
+        for (int k4 = 0; k4 < 4; ++k4) {
+            const int rr = sr + 8 * k4;
+            const int r2 = wave * 32 + rr;
+            const int ri2 = r2 / G;
+            const int rj2 = r2 - ri2 * G;
+            const int qi2 = i0 + ri2;
+            if (ri2 < npos && qi2 < i1 && rj2 < gsize) {
+                const int h2 = a.groups.list[gstart + rj2];
+                const f32x4 o = *reinterpret_cast<const f32x4 *>(stage + rr * kSt + sc);
+                __builtin_nontemporal_store(
+                    o, reinterpret_cast<f32x4 *>(a.out + (((int64_t)b * a.q_len + qi2) * a.hq + h2) * D + 32 * dt + sc));
+            }
         }
-    if (a.lse && half == 0)
+        __syncthreads();
+    }
+    if (a.lse && row_ok && half == 0)
         __builtin_nontemporal_store(any ? (m_ref + log2f(l_row)) * kLn2 : -INFINITY,
                                     a.lse + ((int64_t)b * a.q_len + qi) * a.hq + h);
 }
@@ -535,7 +582,7 @@ hipError_t launch_prefill_mfma(const PrefillArgs &a, hipStream_t stream)
     const int npos = kRows / a.groups.max_group;
     PrefillArgs k = a;
     k.n_qblocks = (a.q_len + npos - 1) / npos;
-    const int64_t blocks = (int64_t)k.n_qblocks * a.batch * a.hkv;
+    const int64_t blocks = (int64_t)k.n_qblocks * (a.split_blocks > 0 ? a.max_splits : 1) * a.batch * a.hkv;
     if (blocks > 0x7FFFFFFF)
         return hipErrorInvalidValue;
     void (*kernel)(PrefillArgs);

@@ -37,4 +37,13 @@ void probe_chunk(int chunk, int rows_per_item, int group_size, int q_len, int co
     out4[2] = c.pos_min;
     out4[3] = c.pos_max;
 }
+
+void probe_tiled(int pos_lo, int key_hi, int window, int sinks, int block, int *blocks, int cap, int *n_out)
+{
+    atlas::TiledBlocks t = atlas::tiled_blocks(pos_lo, key_hi, window, sinks, block);
+    int n = t.n < cap ? t.n : cap;
+    for (int c = 0; c < n; ++c)
+        blocks[c] = atlas::tiled_block_at(t, c);
+    *n_out = t.n;
+}
 }

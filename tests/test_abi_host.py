@@ -241,6 +241,7 @@ def planner(tmp_path_factory):
     lib.probe_ranges.argtypes = [ctypes.c_int] * 5 + [ip, ctypes.c_int, ip]
     lib.probe_bound.argtypes = [ctypes.c_int] * 3
     lib.probe_chunk.argtypes = [ctypes.c_int] * 5 + [ip]
+    lib.probe_tiled.argtypes = [ctypes.c_int] * 5 + [ip, ctypes.c_int, ip]
     return lib
 
 
@@ -306,3 +307,20 @@ def test_chunk_rows(planner):
     assert out[0] >= out[1]
     planner.probe_chunk(0, 4, 3, 1, 10, out)     # decode, group of 3 in a chunk of 4
     assert list(out) == [0, 3, 9, 9]
+
+
+@pytest.mark.parametrize("pos_lo,pos_hi,w,s", [
+    (0, 0, 0, 0), (0, 63, 0, 0), (100, 163, 0, 0), (5000, 5063, 0, 0), (5000, 5063, 128, 0),
+    (5000, 5063, 128, 4), (5000, 5063, 1, 70), (300, 363, 4096, 4), (1000, 1003, 64, 64), (200, 263, 100, 200),
+])
+def test_tiled_block_list_is_the_visible_blocks(planner, pos_lo, pos_hi, w, s):
+    """The key blocks a tiled query block visits (also the merge's split
+    count of the tiled key splits) are exactly, in increasing order, the
+    64-key blocks holding a key some row at positions [pos_lo, pos_hi] sees."""
+    buf = (ctypes.c_int * 4096)()
+    n = ctypes.c_int()
+    planner.probe_tiled(pos_lo, pos_hi, w, s if w > 0 else 0, 64, buf, 4096, ctypes.byref(n))
+    got = list(buf[:n.value])
+    want = sorted({k // 64 for k in _union_visible(pos_lo, pos_hi, w, s if w > 0 else 0)})
+    assert got == want
+
