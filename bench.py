@@ -10,8 +10,9 @@ One step = one pass of the whole hot path over the synthetic inputs:
 Inputs are resident in HBM before timing starts.  `value` is the decode
 attention pass's K/V-read throughput (algorithmic bytes / time of the
 attention call, split + merge); the prefill throughput and the regenerator
-are reported beside it.  Per-kernel times come from HIP events recorded on
-the stream the kernels run on.  After the timed steps, the three smaller
+are reported beside it.  Per-kernel times are medians over the timed steps
+of HIP events recorded on the stream the kernels run on (--step-times prints
+every step's).  After the timed steps, the three smaller
 synthetic workloads (single-head decode, GQA short-query suffix attention,
 mixed-length decode with window / sinks / softcap) are timed per call and
 reported under "workloads" with the two step workloads, and the long-context
@@ -64,6 +65,8 @@ def parse():
     ap.add_argument("--warmup", type=int, default=50)
     ap.add_argument("--split-tokens", type=int, default=0)
     ap.add_argument("--no-prefill", action="store_true")
+    ap.add_argument("--step-times", action="store_true",
+                    help="print every timed step's kernel durations (us) to stderr")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-workloads", action="store_true",
                     help="skip the per-call timing of the three smaller workloads")
@@ -567,9 +570,13 @@ def main():
     torch.cuda.synchronize()
     wall = time.perf_counter() - wall0
     step_ms = s0.elapsed_time(s1) / args.steps
-    dec_ms = float(np.mean(t_dec.ms()))
-    regen_ms = float(np.mean(t_regen.ms()))
+    dec_ms = float(np.median(t_dec.ms()))
+    regen_ms = float(np.median(t_regen.ms()))
     print(f"bench: timed {args.steps} steps in {wall:.2f} s", file=sys.stderr, flush=True)
+    if args.step_times:
+        for name, t in (("regen", t_regen), ("prefill", t_pre), ("decode", t_dec)):
+            if t.pairs:
+                print(f"bench: {name} us per step: {[round(x * 1000) for x in t.ms()]}", file=sys.stderr, flush=True)
 
     kv_bytes = int(w.context_lens.astype(np.int64).sum()) * w.hkv * w.head_dim * 4 * 2
     dec_gbs = kv_bytes / (dec_ms * 1e-3) / 1e9
@@ -612,7 +619,7 @@ def main():
         },
     }
     if p is not None:
-        pre_ms = float(np.mean(t_pre.ms()))
+        pre_ms = float(np.median(t_pre.ms()))
         S, hq, dd = pw.q_len, pw.hq, pw.head_dim
         flops = 4.0 * dd * hq * S * (S + 1) / 2.0
         tf = flops / (pre_ms * 1e-3) / 1e12
