@@ -61,7 +61,7 @@ METRIC = "decode attn KV-read GB/s (% HBM peak); prefill TFLOP/s (% MFMA peak)"
 def parse():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=50)
     ap.add_argument("--split-tokens", type=int, default=0)
     ap.add_argument("--no-prefill", action="store_true")
@@ -554,7 +554,11 @@ def main():
             (t_pre or (lambda f: f()))(prefill)
         (t_dec or (lambda f: f()))(decode)
 
-    for _ in range(args.warmup):
+    # The first (cold) step is timed on its own: first-call figures.
+    f_regen, f_dec, f_pre = Timer(torch), Timer(torch), Timer(torch)
+    step(f_regen, f_dec, f_pre)
+    torch.cuda.synchronize()
+    for _ in range(max(args.warmup - 1, 0)):
         step()
     torch.cuda.synchronize()
     print(f"bench: warmup done ({args.warmup} steps)", file=sys.stderr, flush=True)
@@ -606,6 +610,11 @@ def main():
             "regen_pages": n_cold,
             "regen_write_GBs": round(regen_bytes / (regen_ms * 1e-3) / 1e9, 1),
             "decode_end_to_end_ms": round(dec_ms + regen_ms, 4),
+            "timing": "medians over the timed steps; min and the cold first step beside them",
+            "decode_attention_ms_min": round(float(np.min(t_dec.ms())), 4),
+            "regen_ms_min": round(float(np.min(t_regen.ms())), 4),
+            "first_step_ms": {"decode_attention": round(f_dec.ms()[0], 4), "regen": round(f_regen.ms()[0], 4),
+                              **({} if p is None else {"prefill": round(f_pre.ms()[0], 4)})},
         },
         "roofline": {
             "bound": "hbm",
@@ -624,7 +633,8 @@ def main():
         flops = 4.0 * dd * hq * S * (S + 1) / 2.0
         tf = flops / (pre_ms * 1e-3) / 1e12
         result["prefill"] = {
-            "value": round(tf, 1), "unit": "TFLOP/s", "ms": round(pre_ms, 4), "flop": flops,
+            "value": round(tf, 1), "unit": "TFLOP/s", "ms": round(pre_ms, 4),
+            "ms_min": round(float(np.min(t_pre.ms())), 4), "flop": flops,
             "dtype": "bf16",
             "roofline": {"bound": "mfma", "kernel": "tiled causal prefill", "achieved": round(tf, 1),
                          "peak": BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
