@@ -40,10 +40,11 @@ def wl(dtype, hq, hkv, d, page, q_len, lens, seed=51, window=None, sinks=None, s
     return w
 
 
-def split_count(inp):
+def split_count(inp, head_map=None):
     """Workspace beyond the 256-byte header: the partial states of the splits."""
     import exact_paged_causal_amd as atlas
-    args, _ = atlas.make_attn_args(inp.q, inp.k, inp.v, inp.page_table, inp.context_lens, inp.w.scale)
+    args, _ = atlas.make_attn_args(inp.q, inp.k, inp.v, inp.page_table, inp.context_lens, inp.w.scale,
+                                   head_map=head_map)
     return atlas.atlas_prefill_workspace_bytes(args) - 256
 
 
@@ -93,3 +94,31 @@ def test_key_splits_are_deterministic():
     o2, l2 = H.run(inp, entry="prefill")
     torch.cuda.synchronize()
     assert torch.equal(o1, o2) and torch.equal(l1, l2)
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+def test_key_splits_one_token_pages_and_uneven_head_map(dtype):
+    """Key splits over one-token pages, with an uneven q-head -> K/V-head map
+    (groups of 3 and 2: padded rows in every query block)."""
+    hm = [0, 1, 1, 0, 1]
+    w = wl(dtype, 5, 2, 64, 1, 96, (3000, 1200))
+    say(f"[splits] one-token pages, head map {hm}, {dtype}")
+    inp = H.build(w)
+    assert split_count(inp, hm) > 0
+    out, lse = H.run(inp, entry="prefill", head_map=hm)
+    torch.cuda.synchronize()
+    H.check_against_oracle(inp, out, lse, head_map=hm, what=f"one-token pages {dtype}")
+
+
+def test_key_splits_with_a_long_page_table():
+    """max_pages_per_seq far beyond the contexts: the split count comes from
+    the largest possible context, most runs find no block and return."""
+    w = wl("bf16", 8, 2, 128, 16, 80, (2000, 100))
+    say("[splits] long page table")
+    inp = H.build(w, extra_phys=8)
+    pt = torch.full((w.batch, 4096), 0, dtype=torch.int32, device="cuda")
+    pt[:, :inp.page_table.shape[1]] = inp.page_table
+    import exact_paged_causal_amd as atlas
+    out, lse = atlas.atlas_attend_prefill(inp.q, inp.k, inp.v, pt, inp.context_lens, w.scale)
+    torch.cuda.synchronize()
+    H.check_against_oracle(inp, out, lse, what="long page table")
