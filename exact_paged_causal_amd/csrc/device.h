@@ -50,6 +50,16 @@ __device__ __forceinline__ float group_max(float x)
 // Hardware 2^x (v_exp_f32): exact 0 for -inf.
 __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
 
+// 16-byte load marked non-temporal: K/V rows a decode pass reads once stream
+// past the caches instead of displacing lines other work reuses (measured on
+// the long-context decode: the fold runs about 4 % faster).
+__device__ __forceinline__ uint4 stream_load16(const void *p)
+{
+    typedef uint32_t u32x4_nt __attribute__((ext_vector_type(4)));
+    const u32x4_nt v = __builtin_nontemporal_load(reinterpret_cast<const u32x4_nt *>(p));
+    return make_uint4(v.x, v.y, v.z, v.w);
+}
+
 // c * tanh(x * k) from one hardware exponential and one reciprocal, through
 // tanh(y) = 1 - 2 / (e^(2y) + 1) with the constants folded:
 // c - 2c / (2^(x * 2k log2 e) + 1).  Saturates to +-c (2^+big = inf, rcp(inf)

@@ -16,7 +16,10 @@
 // are reduced across the R lanes with DPP row operations; exp2 runs on the
 // hardware v_exp_f32 with the scale folded by log2(e).  Page ids of the
 // split are staged once in LDS, so the per-key address math is scalar-free
-// shifts and masks (page sizes are powers of two).
+// shifts and masks (page sizes are powers of two).  K/V loads are
+// non-temporal (each row is read once per pass), and iterations whose keys
+// every row of the item sees (no window, all at or before the rows'
+// positions) skip the per-key visibility test.
 //
 // In-kernel regeneration (REGEN instances): page-table entries of -1 mark
 // pages that are not stored; their keys' K and V values are produced at fold
@@ -30,6 +33,8 @@
 // every key of the context (the split plan then spans [0, L)); an ALiBi slope
 // per q-head adds -slope |pos - j| to the logit after the softcap; mask bits
 // hide keys per (row, key).
+#include <type_traits>
+
 #include "device.h"
 #include "kernels.h"
 #include "philox.h"
@@ -190,12 +195,19 @@ __global__ __launch_bounds__(256) void split_valu_kernel(SplitArgs a)
             const E *vr = vbase + row * D;
 #pragma unroll
             for (int n = 0; n < NL; ++n) {
-                bf.k[u][n] = *reinterpret_cast<const uint4 *>(kr + n * R * EPC + li * EPC);
-                bf.v[u][n] = *reinterpret_cast<const uint4 *>(vr + n * R * EPC + li * EPC);
+                bf.k[u][n] = stream_load16(kr + n * R * EPC + li * EPC);
+                bf.v[u][n] = stream_load16(vr + n * R * EPC + li * EPC);
             }
         }
     };
-    auto fold = [&](const Buf &bf, int base) {
+    // FULL: every key of the iteration is inside the span and at or before
+    // every row's position, with no window: no per-key visibility test.
+    // No floating-point contraction here: the FULL copy must round exactly
+    // as the masked one (and as the generator instances) do, so that a key
+    // folds to the same bits whichever copy or instance folds it.
+    auto fold = [&](const Buf &bf, int base, auto full_tag) {
+#pragma clang fp contract(off)
+        constexpr bool FULL = decltype(full_tag)::value;
         float kv[KU][DPL], vv[KU][DPL];
         int key[KU];
 #pragma unroll
@@ -240,7 +252,9 @@ __global__ __launch_bounds__(256) void split_valu_kernel(SplitArgs a)
                     s = cap * tanhf(s / cap);
                 const int j = key[u];
                 bool vis;
-                if constexpr (MODS) {
+                if constexpr (FULL) {
+                    vis = true;
+                } else if constexpr (MODS) {
                     s -= slope[r] * fabsf((float)(pos[r] - j));
                     vis = j < kb && j <= posv[r] && (W <= 0 || j > pos[r] - W || j < S);
                     if (mrow[r]) {
@@ -279,17 +293,30 @@ __global__ __launch_bounds__(256) void split_valu_kernel(SplitArgs a)
         }
     };
 
+    // Iterations ending at or before full_end see every key for every row
+    // (plain instances with 2 to 32 / DPL rows only: elsewhere a second copy
+    // of the loop body costs registers, i.e. occupancy or spills).
+    const int full_end = W <= 0 ? (kb < cr.pos_min + 1 ? kb : cr.pos_min + 1) : -1;
+    auto fold_any = [&](const Buf &bf, int base) {
+        if constexpr (!REGEN && !MODS && MC >= 2 && MC * DPL <= 32) {
+            if (base + KPI <= full_end) {
+                fold(bf, base, std::true_type{});
+                return;
+            }
+        }
+        fold(bf, base, std::false_type{});
+    };
     Buf ba, bb;
     int base = ka;
     load(ba, base);
     while (base < kb) {
         load(bb, base + KPI);
-        fold(ba, base);
+        fold_any(ba, base);
         base += KPI;
         if (base >= kb)
             break;
         load(ba, base + KPI);
-        fold(bb, base);
+        fold_any(bb, base);
         base += KPI;
     }
 
