@@ -17,7 +17,8 @@
 // hardware v_exp_f32 with the scale folded by log2(e).  Page ids of the
 // split are staged once in LDS, so the per-key address math is scalar-free
 // shifts and masks (page sizes are powers of two).  K/V loads are
-// non-temporal (each row is read once per pass), and iterations whose keys
+// non-temporal (each row is read once per pass; not in the REGEN instances,
+// whose cold keys re-read page 0), and iterations whose keys
 // every row of the item sees (no window, all at or before the rows'
 // positions) skip the per-key visibility test.
 //
@@ -195,8 +196,14 @@ __global__ __launch_bounds__(256) void split_valu_kernel(SplitArgs a)
             const E *vr = vbase + row * D;
 #pragma unroll
             for (int n = 0; n < NL; ++n) {
-                bf.k[u][n] = stream_load16(kr + n * R * EPC + li * EPC);
-                bf.v[u][n] = stream_load16(vr + n * R * EPC + li * EPC);
+                if constexpr (REGEN) {
+                    // Cold keys load page 0 again and again: keep it cached.
+                    bf.k[u][n] = *reinterpret_cast<const uint4 *>(kr + n * R * EPC + li * EPC);
+                    bf.v[u][n] = *reinterpret_cast<const uint4 *>(vr + n * R * EPC + li * EPC);
+                } else {
+                    bf.k[u][n] = stream_load16(kr + n * R * EPC + li * EPC);
+                    bf.v[u][n] = stream_load16(vr + n * R * EPC + li * EPC);
+                }
             }
         }
     };
