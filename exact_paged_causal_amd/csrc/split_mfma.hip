@@ -24,8 +24,11 @@
 //                   read).
 // The next chunk's K and V are loaded into registers as soon as the current
 // chunk's have been consumed, so they are in flight during its softmax and
-// P.V products.  At the end the 4 waves' states are combined in LDS and one
-// (m, l, acc) partial per row is written; merge.hip finishes.
+// P.V products.  V loads (1 KiB contiguous per wave instruction) are
+// non-temporal; K loads are not: each of their instructions reads half of
+// 16 cache lines, whose other halves the next instruction wants from cache.
+// At the end the 4 waves' states are combined in LDS and one (m, l, acc)
+// partial per row is written; merge.hip finishes.
 #include "device.h"
 #include "kernels.h"
 
@@ -163,7 +166,7 @@ __global__ __launch_bounds__(256) void split_mfma_kernel(SplitArgs a)
             const int c = lane + 64 * u;
             const int key = c / CPR;
             const int col = c - key * CPR;
-            r.v[u] = *reinterpret_cast<const uint4 *>(row_ptr(vpages, cb + key) + col * 8);
+            r.v[u] = stream_load16(row_ptr(vpages, cb + key) + col * 8);
         }
     };
 
