@@ -6,8 +6,8 @@
 // group of 8 q-heads costs 4 flop per K/V byte.
 //
 // Per wave, 32 keys at a time (the 4 waves interleave 32-key chunks):
-//   S^T = K Q^T     v_mfma_f32_16x16x32_bf16, A = 16 keys x 32 dims loaded
-//                   straight from the page into the A-operand layout (each
+//   S^T = K Q^T     v_mfma_f32_16x16x32_bf16, A = 16 keys x 32 dims read
+//                   from the wave's LDS K tile in the A-operand layout (each
 //                   lane 16 contiguous bytes of one key row), B = Q^T for the
 //                   item's <= 16 rows (q-heads of the group x queries) kept in
 //                   registers; each lane ends up with 8 scores of one row.
@@ -24,9 +24,11 @@
 //                   read).
 // The next chunk's K and V are loaded into registers as soon as the current
 // chunk's have been consumed, so they are in flight during its softmax and
-// P.V products.  V loads (1 KiB contiguous per wave instruction) are
-// non-temporal; K loads are not: each of their instructions reads half of
-// 16 cache lines, whose other halves the next instruction wants from cache.
+// P.V products.  K and V are both loaded as whole rows (1 KiB contiguous per
+// wave instruction), non-temporally, and staged through the wave's LDS
+// tiles: loaded straight into the A-operand layout, each K instruction read
+// half of 16 cache lines (whose other halves the next instruction wanted
+// from cache), which ruled out non-temporal loads for K.
 // At the end the 4 waves' states are combined in LDS and one (m, l, acc)
 // partial per row is written; merge.hip finishes.
 #include "device.h"
@@ -50,10 +52,12 @@ constexpr float kRescaleSlack = 8.0f;
 template <int D>
 struct alignas(16) SplitSmem {
     static constexpr int RS = D + 16; // padded LDS row (elements): 32-byte skew between rows
+    static constexpr int RSK = D + 8; // K rows: 16-byte skew (conflict-free operand reads)
     union alignas(16) {
         uint16_t v[4][kChunk][RS];    // per-wave V tile (bf16 bits)
         float acc[4][kRowsMax][D];    // end-of-span wave states
     } u;
+    alignas(16) uint16_t k[4][kChunk][RSK];  // per-wave K tile (bf16 bits)
     float m[4][kRowsMax];
     float l[4][kRowsMax];
     int32_t pid[kMaxSplitPages];
@@ -142,31 +146,28 @@ __global__ __launch_bounds__(256) void split_mfma_kernel(SplitArgs a)
     const uint16_t *kpages = reinterpret_cast<const uint16_t *>(a.k_pages);
     const uint16_t *vpages = reinterpret_cast<const uint16_t *>(a.v_pages);
     const int64_t head_rows = (int64_t)g << ps;
-    auto row_ptr = [&](const uint16_t *base, int j) {
+    // Element offset of key j's row (clamped to the span's last key).
+    auto row_off = [&](int j) {
         const int jj = j < kb ? j : kb - 1;
         const int pid = sm.pid[(jj >> ps) - p0];
-        return base + ((((int64_t)pid * a.hkv) << ps) + head_rows + (jj & pmask)) * D;
+        return ((((int64_t)pid * a.hkv) << ps) + head_rows + (jj & pmask)) * D;
     };
 
-    // Register buffer for one chunk's K (operand layout) and V (staging).
+    // Register buffer for one chunk's K and V, both staged through LDS: each
+    // wave instruction reads whole rows (1 KiB runs), non-temporally.
     struct Regs {
-        bf16x8 k[2][KS];
+        uint4 k[VCH];
         uint4 v[VCH];
     };
     auto load_chunk = [&](Regs &r, int cb) {
-#pragma unroll
-        for (int t = 0; t < 2; ++t) {
-            const uint16_t *kr = row_ptr(kpages, cb + 16 * t + l16);
-#pragma unroll
-            for (int s = 0; s < KS; ++s)
-                r.k[t][s] = *reinterpret_cast<const bf16x8 *>(kr + 32 * s + 8 * g4);
-        }
 #pragma unroll
         for (int u = 0; u < VCH; ++u) {
             const int c = lane + 64 * u;
             const int key = c / CPR;
             const int col = c - key * CPR;
-            r.v[u] = stream_load16(row_ptr(vpages, cb + key) + col * 8);
+            const int64_t off = row_off(cb + key) + col * 8;
+            r.k[u] = stream_load16(kpages + off);
+            r.v[u] = stream_load16(vpages + off);
         }
     };
 
@@ -182,14 +183,21 @@ __global__ __launch_bounds__(256) void split_mfma_kernel(SplitArgs a)
     // (once both are consumed) the next chunk's loads into the same
     // registers, then softmax and O^T += V^T P^T from LDS.
     auto fold_chunk = [&](Regs &r, int cb, int cb_next) {
-        // Stage this chunk's V in the wave's LDS tile.
+        // Stage this chunk's K and V in the wave's LDS tiles, then refill
+        // the registers with the next chunk.
 #pragma unroll
         for (int u = 0; u < VCH; ++u) {
             const int c = lane + 64 * u;
             const int key = c / CPR;
             const int col = c - key * CPR;
+            *reinterpret_cast<uint4 *>(&sm.k[wave][key][col * 8]) = r.k[u];
             *reinterpret_cast<uint4 *>(&sm.u.v[wave][key][col * 8]) = r.v[u];
         }
+        load_chunk(r, cb_next);
+        // The tiles' reads must follow their writes in this wave.
+        __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+        __builtin_amdgcn_wave_barrier();
+        __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
 
         // S^T tiles: lane holds row l16, keys 16t + 4*g4 + j.  The two tiles'
         // chains alternate.
@@ -197,9 +205,10 @@ __global__ __launch_bounds__(256) void split_mfma_kernel(SplitArgs a)
 #pragma unroll
         for (int s = 0; s < KS; ++s)
 #pragma unroll
-            for (int t = 0; t < 2; ++t)
-                st[t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(r.k[t][s], qf[s], st[t], 0, 0, 0);
-        load_chunk(r, cb_next);
+            for (int t = 0; t < 2; ++t) {
+                const bf16x8 kf = *reinterpret_cast<const bf16x8 *>(&sm.k[wave][16 * t + l16][32 * s + 8 * g4]);
+                st[t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kf, qf[s], st[t], 0, 0, 0);
+            }
 
         // Scale, softcap, mask (log2 units).
         float x[8];
@@ -252,11 +261,6 @@ __global__ __launch_bounds__(256) void split_mfma_kernel(SplitArgs a)
         }
         const bf16x8 pbh = __builtin_bit_cast(bf16x8, phi);
         const bf16x8 pbl = __builtin_bit_cast(bf16x8, plo);
-
-        // The tile's transposed reads must follow its writes in this wave.
-        __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
-        __builtin_amdgcn_wave_barrier();
-        __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
 
         // O^T += V^T P^T: slots 0..3 = keys 4*g4 + k, slots 4..7 = 16 + 4*g4 + k.
 #pragma unroll
