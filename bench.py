@@ -502,7 +502,7 @@ def cpu_baseline(d, out, np, oracle, min_seconds=3.0):
 def main():
     args = parse()
     if args.gpus != 1:
-        print(json.dumps({"error": "this build runs on one GPU; --gpus must be 1 (no multi-GPU path)"}))
+        print(json.dumps({"error": "this library runs on one GPU; --gpus must be 1 (no multi-GPU path)"}))
         sys.exit(2)
     import numpy as np
     import torch
