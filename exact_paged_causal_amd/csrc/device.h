@@ -50,6 +50,15 @@ __device__ __forceinline__ float group_max(float x)
 // Hardware 2^x (v_exp_f32): exact 0 for -inf.
 __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
 
+// Ordinary 16-byte load through a native vector type (a uint4 dereference
+// can keep a kernel's register buffers from being promoted to registers).
+__device__ __forceinline__ uint4 load16(const void *p)
+{
+    typedef uint32_t u32x4_ld __attribute__((ext_vector_type(4)));
+    const u32x4_ld v = *reinterpret_cast<const u32x4_ld *>(p);
+    return make_uint4(v.x, v.y, v.z, v.w);
+}
+
 // 16-byte load marked non-temporal: K/V rows a decode pass reads once stream
 // past the caches instead of displacing lines other work reuses (measured on
 // the long-context decode: the fold runs about 4 % faster).

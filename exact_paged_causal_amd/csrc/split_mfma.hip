@@ -25,10 +25,13 @@
 // The next chunk's K and V are loaded into registers as soon as the current
 // chunk's have been consumed, so they are in flight during its softmax and
 // P.V products.  K and V are both loaded as whole rows (1 KiB contiguous per
-// wave instruction), non-temporally, and staged through the wave's LDS
-// tiles: loaded straight into the A-operand layout, each K instruction read
-// half of 16 cache lines (whose other halves the next instruction wanted
-// from cache), which ruled out non-temporal loads for K.
+// wave instruction) and staged through the wave's LDS tiles; the loads are
+// non-temporal (NT instances) when one row chunk holds every row of a K/V
+// head, so that each row is read once per pass (several chunks re-read the
+// same rows, which ordinary loads keep in cache).  Loaded straight into the
+// A-operand layout, each K instruction read half of 16 cache lines (whose
+// other halves the next instruction wanted from cache), which ruled out
+// non-temporal loads for K there.
 // At the end the 4 waves' states are combined in LDS and one (m, l, acc)
 // partial per row is written; merge.hip finishes.
 #include "device.h"
@@ -75,7 +78,7 @@ __device__ __forceinline__ void split_hi_lo(float p0, float p1, uint32_t &hi, ui
 
 // MODS instances (atlas_attend_mods): non-causal rows plan and mask over
 // [0, ctx); ALiBi slopes and mask bits per (row, key).
-template <int D, bool MODS>
+template <int D, bool MODS, bool NT>
 __global__ __launch_bounds__(256) void split_mfma_kernel(SplitArgs a)
 {
     constexpr int KS = D / 32;                 // QK k-steps
@@ -166,8 +169,13 @@ __global__ __launch_bounds__(256) void split_mfma_kernel(SplitArgs a)
             const int key = c / CPR;
             const int col = c - key * CPR;
             const int64_t off = row_off(cb + key) + col * 8;
-            r.k[u] = stream_load16(kpages + off);
-            r.v[u] = stream_load16(vpages + off);
+            if constexpr (NT) {
+                r.k[u] = stream_load16(kpages + off);
+                r.v[u] = stream_load16(vpages + off);
+            } else {
+                r.k[u] = load16(kpages + off);
+                r.v[u] = load16(vpages + off);
+            }
         }
     };
 
@@ -348,9 +356,11 @@ hipError_t launch_split_mfma(const SplitArgs &a, hipStream_t stream)
     dim3 grid(a.max_splits, a.hkv * a.n_chunks, a.batch);
     void (*kernel)(SplitArgs);
     if (a.head_dim == 64)
-        kernel = a.mods.any ? split_mfma_kernel<64, true> : split_mfma_kernel<64, false>;
+        kernel = a.mods.any ? split_mfma_kernel<64, true, false>
+                 : (a.n_chunks == 1 ? split_mfma_kernel<64, false, true> : split_mfma_kernel<64, false, false>);
     else
-        kernel = a.mods.any ? split_mfma_kernel<128, true> : split_mfma_kernel<128, false>;
+        kernel = a.mods.any ? split_mfma_kernel<128, true, false>
+                 : (a.n_chunks == 1 ? split_mfma_kernel<128, false, true> : split_mfma_kernel<128, false, false>);
     hipLaunchKernelGGL(kernel, grid, dim3(256), 0, stream, a);
     return hipGetLastError();
 }

@@ -17,8 +17,11 @@
 // hardware v_exp_f32 with the scale folded by log2(e).  Page ids of the
 // split are staged once in LDS, so the per-key address math is scalar-free
 // shifts and masks (page sizes are powers of two).  K/V loads are
-// non-temporal (each row is read once per pass; not in the REGEN instances,
-// whose cold keys re-read page 0), and iterations whose keys
+// non-temporal (NT instances) when one row chunk covers every row of a K/V
+// head, so each row is read once per pass; with several chunks the chunks
+// re-read the same rows and ordinary loads keep them in cache, as do the
+// REGEN and MODS instances (REGEN's cold keys re-read page 0).  Iterations
+// whose keys
 // every row of the item sees (no window, all at or before the rows'
 // positions) skip the per-key visibility test.
 //
@@ -58,7 +61,7 @@ struct Elem<float> {
     }
 };
 
-template <typename E, int D, int MC, int KU, bool REGEN, bool MODS>
+template <typename E, int D, int MC, int KU, bool REGEN, bool MODS, bool NT>
 __global__ __launch_bounds__(256) void split_valu_kernel(SplitArgs a)
 {
     constexpr int EPC = Elem<E>::kPer16;                 // elements per 16-byte piece
@@ -196,13 +199,12 @@ __global__ __launch_bounds__(256) void split_valu_kernel(SplitArgs a)
             const E *vr = vbase + row * D;
 #pragma unroll
             for (int n = 0; n < NL; ++n) {
-                if constexpr (REGEN) {
-                    // Cold keys load page 0 again and again: keep it cached.
-                    bf.k[u][n] = *reinterpret_cast<const uint4 *>(kr + n * R * EPC + li * EPC);
-                    bf.v[u][n] = *reinterpret_cast<const uint4 *>(vr + n * R * EPC + li * EPC);
-                } else {
+                if constexpr (NT) {
                     bf.k[u][n] = stream_load16(kr + n * R * EPC + li * EPC);
                     bf.v[u][n] = stream_load16(vr + n * R * EPC + li * EPC);
+                } else {
+                    bf.k[u][n] = *reinterpret_cast<const uint4 *>(kr + n * R * EPC + li * EPC);
+                    bf.v[u][n] = *reinterpret_cast<const uint4 *>(vr + n * R * EPC + li * EPC);
                 }
             }
         }
@@ -403,11 +405,13 @@ hipError_t launch_one(const SplitArgs &a, hipStream_t stream)
     constexpr int KU = (D == 64) ? ((MC <= 2) ? 8 : (MC * DPL <= 16 ? 4 : 2)) : ((MC <= 2) ? 4 : 2);
     dim3 grid(a.max_splits, a.hkv * a.n_chunks, a.batch);
     if (a.regen)
-        hipLaunchKernelGGL((split_valu_kernel<E, D, MC, KU, true, false>), grid, dim3(256), 0, stream, a);
+        hipLaunchKernelGGL((split_valu_kernel<E, D, MC, KU, true, false, false>), grid, dim3(256), 0, stream, a);
     else if (a.mods.any)
-        hipLaunchKernelGGL((split_valu_kernel<E, D, MC, KU, false, true>), grid, dim3(256), 0, stream, a);
+        hipLaunchKernelGGL((split_valu_kernel<E, D, MC, KU, false, true, false>), grid, dim3(256), 0, stream, a);
+    else if (a.n_chunks == 1)
+        hipLaunchKernelGGL((split_valu_kernel<E, D, MC, KU, false, false, true>), grid, dim3(256), 0, stream, a);
     else
-        hipLaunchKernelGGL((split_valu_kernel<E, D, MC, KU, false, false>), grid, dim3(256), 0, stream, a);
+        hipLaunchKernelGGL((split_valu_kernel<E, D, MC, KU, false, false, false>), grid, dim3(256), 0, stream, a);
     return hipGetLastError();
 }
 
