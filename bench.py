@@ -158,6 +158,23 @@ def _median_call_us(torch, np, fn, calls=30, warm=5):
     return float(np.median(t.ms())) * 1000.0
 
 
+def _c_abi_call_us(torch, np, entry, args, calls=30):
+    """Median time of one C-ABI call with prepared arguments (outputs and
+    workspace already set): what a native caller pays per call, without the
+    Python binding's argument marshalling."""
+    import ctypes
+    from exact_paged_causal_amd.atlas import lib
+    fn = getattr(lib, entry)
+    sh = ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
+    ref = ctypes.byref(args)
+
+    def call():
+        st = fn(ref, sh)
+        if st != 0:
+            raise RuntimeError(f"{entry} returned {st}")
+    return _median_call_us(torch, np, call, calls=calls)
+
+
 def _arena(torch, workloads, np, w, lay):
     """Device K/V arenas of a non-regenerated workload: seeded logical pages
     scattered to their physical ids."""
@@ -407,19 +424,28 @@ def workload_report(torch, np, workloads, atlas):
         pt = torch.from_numpy(lay.page_table).cuda()
         ctx = torch.from_numpy(w.context_lens).cuda()
 
+        # Outputs and workspace allocated once, outside the timed calls.
+        out = torch.empty(workloads.query_shape(w), dtype=torch.float32, device="cuda")
+        lse = torch.empty(w.batch, 1, w.hq, dtype=torch.float32, device="cuda")
+        dargs, _ = atlas.make_attn_args(q, k, v, pt, ctx, w.scale)
+        ws = torch.empty(max(1, atlas.atlas_decode_workspace_bytes(dargs)), dtype=torch.uint8, device="cuda")
+
         def call():
             if cold is not None:
                 atlas.atlas_regenerate_pages(k, v, cold, seed=w.seed, layer=w.layer)
-            return atlas.atlas_attend_decode(q, k, v, pt, ctx, w.scale)[0]
+            return atlas.atlas_attend_decode(q, k, v, pt, ctx, w.scale, out=out, lse=lse, workspace=ws)[0]
         r = rep.setdefault("single_head_decode", {})
         r[f"{mode}_us"] = round(_median_call_us(torch, np, call), 2)
+        if mode == "resident":
+            r["c_abi_us"] = round(_c_abi_call_us(torch, np, "atlas_attend_decode", atlas.make_attn_args(
+                q, k, v, pt, ctx, w.scale, out=out, lse=lse, workspace=ws)[0]), 2)
     kvb = int(w.context_lens.sum()) * w.hkv * w.head_dim * 4 * 2
     us = rep["single_head_decode"]["resident_us"]
     rep["single_head_decode"].update({"kv_bytes": kvb, "GBs": round(kvb / us / 1e3, 1),
                                       "frac_hbm": round(kvb / us / 1e3 / HBM_PEAK_GBS, 4),
-                                      "note": "launch-latency bound (2 MiB of K/V); times are per Python "
-                                              "call, host overhead included; cold regenerates all 8 pages "
-                                              "in the call"})
+                                      "note": "launch-latency bound (2 MiB of K/V); *_us are per Python "
+                                              "call, host overhead included (c_abi_us: one C-ABI call with "
+                                              "prepared arguments); cold regenerates all 8 pages in the call"})
     # GQA short-query suffix attention (16 queries at positions 240..255).
     w = workloads.make("gqa_short_query")
     lay = workloads.page_layout(w)
@@ -427,13 +453,20 @@ def workload_report(torch, np, workloads, atlas):
     q = workloads.randn(workloads.query_shape(w), seed=w.seed * 100 + 1, device="cuda")
     pt = torch.from_numpy(lay.page_table).cuda()
     ctx = torch.from_numpy(w.context_lens).cuda()
-    call = lambda: atlas.atlas_attend_prefill(q, k, v, pt, ctx, w.scale)[0]
+    out = torch.empty(workloads.query_shape(w), dtype=torch.float32, device="cuda")
+    lse = torch.empty(w.batch, w.q_len, w.hq, dtype=torch.float32, device="cuda")
+    pargs, _ = atlas.make_attn_args(q, k, v, pt, ctx, w.scale)
+    ws = torch.empty(max(1, atlas.atlas_prefill_workspace_bytes(pargs)), dtype=torch.uint8, device="cuda")
+    call = lambda: atlas.atlas_attend_prefill(q, k, v, pt, ctx, w.scale, out=out, lse=lse, workspace=ws)[0]
     us = _median_call_us(torch, np, call)
+    c_us = _c_abi_call_us(torch, np, "atlas_attend_prefill", atlas.make_attn_args(
+        q, k, v, pt, ctx, w.scale, out=out, lse=lse, workspace=ws)[0])
     L = int(w.context_lens[0])
     pairs = w.hq * sum(L - w.q_len + i + 1 for i in range(w.q_len))
-    rep["gqa_short_query"] = {"us": round(us, 2), "kv_bytes": L * w.hkv * w.head_dim * 4 * 2,
+    rep["gqa_short_query"] = {"us": round(us, 2), "c_abi_us": round(c_us, 2),
+                              "kv_bytes": L * w.hkv * w.head_dim * 4 * 2,
                               "flop": 4 * w.head_dim * pairs,
-                              "note": "latency bound (256 KiB of K/V); per Python call, host overhead included"}
+                              "note": "latency bound (256 KiB of K/V); us per Python call, host overhead included; c_abi_us: one C-ABI call with prepared arguments"}
     del k, v
     # Mixed-length decode with window / sinks / softcap on even sequences.
     w = workloads.make("mixed_decode")
