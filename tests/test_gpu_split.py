@@ -85,6 +85,30 @@ def test_regen_is_placement_free_and_deterministic():
     assert torch.equal(k, k1)
 
 
+def test_regen_more_jobs_than_one_grid_column():
+    """More jobs than the grid's y dimension holds (65535): the jobs past it
+    are taken by the grid stride; an invalid job in between is skipped and the
+    ones after it still written."""
+    import exact_paged_causal_amd as atlas
+    n_jobs, seed, layer = 70001, 77, 2
+    say(f"[regen] {n_jobs} one-token jobs (grid-strided)")
+    k = torch.full((n_jobs, 1, 1, 64), 123.0, dtype=torch.float32, device="cuda")
+    v = torch.full_like(k, 123.0)
+    j = np.arange(n_jobs, dtype=np.int32)
+    jobs_np = np.stack([j % 7, j, j], axis=1).astype(np.int32)
+    bad = 65540
+    jobs_np[bad, 2] = n_jobs + 5            # out-of-range physical page: skipped
+    atlas.atlas_regenerate_pages(k, v, torch.from_numpy(jobs_np).cuda(), seed=seed, layer=layer)
+    kh, vh = k.cpu().numpy(), v.cpu().numpy()
+    for idx in (0, 1, 65534, 65535, 65536, bad + 1, n_jobs - 1):
+        seq, lp, phys = (int(x) for x in jobs_np[idx])
+        for tensor, arena in ((oracle.TENSOR_K, kh), (oracle.TENSOR_V, vh)):
+            z = oracle.regen_rows(seed, layer, seq, tensor, 0, lp, 1, 64, "f64")
+            err = np.abs(arena[phys, 0].astype(np.float64) - z)
+            assert np.all(err <= 1e-6 * (1 + np.abs(z))), (idx, tensor, float(err.max()))
+    assert np.all(kh[bad] == 123.0) and np.all(vh[bad] == 123.0)
+
+
 # ------------------------------------------------------ decode, small cases
 
 DECODE_CASES = [
