@@ -157,7 +157,7 @@ __global__ __launch_bounds__(256) void split_mfma_kernel(SplitArgs a)
     };
 
     // Register buffer for one chunk's K and V, both staged through LDS: each
-    // wave instruction reads whole rows (1 KiB runs), non-temporally.
+    // wave instruction reads whole rows (1 KiB runs).
     struct Regs {
         uint4 k[VCH];
         uint4 v[VCH];

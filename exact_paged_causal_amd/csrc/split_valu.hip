@@ -203,8 +203,8 @@ __global__ __launch_bounds__(256) void split_valu_kernel(SplitArgs a)
                     bf.k[u][n] = stream_load16(kr + n * R * EPC + li * EPC);
                     bf.v[u][n] = stream_load16(vr + n * R * EPC + li * EPC);
                 } else {
-                    bf.k[u][n] = *reinterpret_cast<const uint4 *>(kr + n * R * EPC + li * EPC);
-                    bf.v[u][n] = *reinterpret_cast<const uint4 *>(vr + n * R * EPC + li * EPC);
+                    bf.k[u][n] = load16(kr + n * R * EPC + li * EPC);
+                    bf.v[u][n] = load16(vr + n * R * EPC + li * EPC);
                 }
             }
         }
