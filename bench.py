@@ -29,6 +29,9 @@ the long-context decode through the hot-page cache (atlas_cache_plan ->
 regenerate admitted pages -> decode with the rest generated in the kernel)
 under "next": "hot_cache"; short prefill chunks behind a 32768-token history
 (the tiled kernels with key splits) under "next": "chunked_prefill".
+A plain 256 MiB device-to-device copy is timed last as context for the HBM
+figures ("hbm_context"); the small workloads also report one C-ABI call
+with prepared arguments ("c_abi_us") beside the Python-call time.
 
 Prints one JSON line.  `--gpus N` with N > 1 exits: this path runs on one GPU.
 """
