@@ -37,8 +37,10 @@ __device__ __forceinline__ PhiloxWords philox10(PhiloxWords c, uint32_t k0, uint
     for (int round = 0; round < 10; ++round) {
         const uint64_t p0 = (uint64_t)0xD2511F53u * c.w0;
         const uint64_t p2 = (uint64_t)0xCD9E8D57u * c.w2;
-        const PhiloxWords n{(uint32_t)(p2 >> 32) ^ c.w1 ^ k0, (uint32_t)p2,
-                            (uint32_t)(p0 >> 32) ^ c.w3 ^ k1, (uint32_t)p0};
+        // Three-input XORs as one gfx950 bitop3 each (truth table 0x96).
+        const uint32_t x0 = (uint32_t)__builtin_amdgcn_bitop3_b32((uint32_t)(p2 >> 32), c.w1, k0, 0x96);
+        const uint32_t x2 = (uint32_t)__builtin_amdgcn_bitop3_b32((uint32_t)(p0 >> 32), c.w3, k1, 0x96);
+        const PhiloxWords n{x0, (uint32_t)p2, x2, (uint32_t)p0};
         c = n;
         k0 += 0x9E3779B9u;
         k1 += 0xBB67AE85u;
