@@ -57,8 +57,11 @@ __device__ __forceinline__ float philox_unit_open(uint32_t x)
 __device__ __forceinline__ void box_muller(uint32_t wr, uint32_t wa, float &zc, float &zs)
 {
     const float r = sqrtf(-2.0f * logf(philox_unit_open(wr)));
-    float sn, cs;
-    sincospif(2.0f * philox_unit_open(wa), &sn, &cs);
+    // sin / cos of 2 pi u on the hardware units, whose argument is in
+    // revolutions (u itself, no range reduction needed in (0, 1)).
+    const float ua = philox_unit_open(wa);
+    const float sn = __builtin_amdgcn_sinf(ua);
+    const float cs = __builtin_amdgcn_cosf(ua);
     zc = r * cs;
     zs = r * sn;
 }
