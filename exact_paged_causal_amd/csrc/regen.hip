@@ -5,7 +5,7 @@
 // philox.h.  One thread produces four consecutive dims of one token for both
 // K and V, so stores are 16-byte (fp32) or 8-byte (bf16) and contiguous
 // across a wave.  The work is ALU-bound (20 32x32->64-bit multiplies plus
-// log/sqrt/sin/cos per four values); the grid's x dimension covers the items
+// log2/sqrt/sin/cos per four values); the grid's x dimension covers the items
 // of one job and y the jobs, so no thread divides by the job size (a 64-bit
 // division per thread cost about 7 % of the kernel).
 #include "device.h"
