@@ -56,8 +56,9 @@ __device__ __forceinline__ float philox_unit_open(uint32_t x)
 
 __device__ __forceinline__ void box_muller(uint32_t wr, uint32_t wa, float &zc, float &zs)
 {
-    // -2 ln u = -2 ln 2 * log2 u, with log2 on the hardware unit.
-    const float r = sqrtf(-1.3862943611198906f * __builtin_amdgcn_logf(philox_unit_open(wr)));
+    // -2 ln u = -2 ln 2 * log2 u, with log2 and the square root on the
+    // hardware units.
+    const float r = __builtin_amdgcn_sqrtf(-1.3862943611198906f * __builtin_amdgcn_logf(philox_unit_open(wr)));
     // sin / cos of 2 pi u on the hardware units, whose argument is in
     // revolutions (u itself, no range reduction needed in (0, 1)).
     const float ua = philox_unit_open(wa);
