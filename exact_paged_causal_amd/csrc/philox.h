@@ -51,7 +51,11 @@ __device__ __forceinline__ PhiloxWords philox10(PhiloxWords c, uint32_t k0, uint
 __device__ __forceinline__ float philox_unit_open(uint32_t x)
 {
     // (floor(x / 512) + 1/2) * 2^-23 = (2 floor(x/512) + 1) * 2^-24: 24 bits, exact.
-    return fmaf((float)(x >> 9), 0x1p-23f, 0x1p-24f);
+    // The top 23 bits of x become the mantissa of a float in [1, 2) (one
+    // funnel shift: 0x7F above x, shifted right by 9), and subtracting
+    // 1 - 2^-24 leaves exactly (x>>9) 2^-23 + 2^-24 (the difference is
+    // representable, so the subtraction is exact).
+    return __uint_as_float(__builtin_amdgcn_alignbit(0x7Fu, x, 9u)) - 0x1.fffffep-1f;
 }
 
 __device__ __forceinline__ void box_muller(uint32_t wr, uint32_t wa, float &zc, float &zs)
