@@ -311,6 +311,8 @@ def cache_report(torch, np, workloads, atlas, calls=10):
     q = workloads.randn(workloads.query_shape(w), seed=w.seed * 100 + 1, device="cuda")
     ctx = torch.from_numpy(w.context_lens).cuda()
     lens = w.context_lens.astype(np.int32)
+    seq_ids = list(range(B))                # each sequence's id is its generator key
+    keys = torch.tensor(seq_ids, dtype=torch.int32, device="cuda")
     rep = {}
     for name, budget in (("budget_256MiB", 256 << 20), ("budget_2GiB", 2 << 30)):
         cache = atlas.HotCache(budget, page_bytes, P, recent_tokens=2048, admit_regenerated=True)
@@ -321,12 +323,12 @@ def cache_report(torch, np, workloads, atlas, calls=10):
 
         def call():
             t0 = time.perf_counter()
-            pt, jobs = cache.plan(w.layer, list(range(B)), lens, maxp)
+            pt, jobs = cache.plan(w.layer, seq_ids, lens, maxp)
             plan_us.append((time.perf_counter() - t0) * 1e6)
             if len(jobs):
                 atlas.atlas_regenerate_pages(k, v, torch.from_numpy(jobs).cuda(), seed=w.seed, layer=w.layer)
             atlas.atlas_attend_decode_regen(q, k, v, torch.from_numpy(pt).cuda(), ctx, w.scale, seed=w.seed,
-                                            layer=w.layer)
+                                            layer=w.layer, seq_keys=keys)
 
         torch.cuda.synchronize()
         t0 = time.perf_counter()

@@ -31,14 +31,15 @@ ATLAS_DTYPE_BF16 = 1
 
 ATLAS_PAGE_REGENERATE = -1   # page-table value of a page regenerated inside atlas_attend_decode_regen
 
-ABI_VERSION = 1
+ABI_VERSION = 2
 
 _DTYPES = {torch.float32: ATLAS_DTYPE_F32, torch.bfloat16: ATLAS_DTYPE_BF16}
 
 
 class AttnArgs(ctypes.Structure):
     _fields_ = [
-        ("dtype", ctypes.c_int32),
+        ("q_dtype", ctypes.c_int32),
+        ("kv_dtype", ctypes.c_int32),
         ("batch", ctypes.c_int32),
         ("q_len", ctypes.c_int32),
         ("num_q_heads", ctypes.c_int32),
@@ -49,7 +50,6 @@ class AttnArgs(ctypes.Structure):
         ("max_pages_per_seq", ctypes.c_int32),
         ("split_tokens", ctypes.c_int32),
         ("scale", ctypes.c_float),
-        ("reserved0", ctypes.c_int32),
         ("head_map", ctypes.POINTER(ctypes.c_int32)),
         ("q", ctypes.c_void_p),
         ("k_pages", ctypes.c_void_p),
@@ -169,7 +169,7 @@ def _load():
     lib.atlas_regenerate_pages.argtypes = [ctypes.POINTER(RegenArgs), ctypes.c_void_p]
     lib.atlas_attend_decode_regen.restype = ctypes.c_int32
     lib.atlas_attend_decode_regen.argtypes = [ctypes.POINTER(AttnArgs), ctypes.c_uint64, ctypes.c_int32,
-                                              ctypes.c_void_p]
+                                              ctypes.c_void_p, ctypes.c_void_p]
     lib.atlas_append_kv.restype = ctypes.c_int32
     lib.atlas_append_kv.argtypes = [ctypes.POINTER(AppendArgs), ctypes.c_void_p]
     lib.atlas_pool_create.restype = ctypes.c_int32
@@ -253,13 +253,16 @@ def make_attn_args(q, k_pages, v_pages, page_table, context_lens, scale, *, head
                    workspace=None, split_tokens=0):
     """Fill an AttnArgs from tensors (q [B][q_len][Hq][D], arenas
     [num_phys][Hkv][P][D], page_table [B][max_pages] int32, context_lens [B]
-    int32).  Returns (args, keepalive)."""
+    int32).  q and the arenas may differ in dtype (the library accepts an
+    fp32 query over a bf16 cache).  Returns (args, keepalive)."""
     if q.dtype not in _DTYPES:
         raise ValueError(f"q dtype {q.dtype} unsupported (float32 or bfloat16)")
+    if k_pages.dtype not in _DTYPES:
+        raise ValueError(f"k_pages dtype {k_pages.dtype} unsupported (float32 or bfloat16)")
     dev = q.device
     _check(q, "q", ndim=4)
-    _check(k_pages, "k_pages", q.dtype, dev, 4)
-    _check(v_pages, "v_pages", q.dtype, dev, 4)
+    _check(k_pages, "k_pages", None, dev, 4)
+    _check(v_pages, "v_pages", k_pages.dtype, dev, 4)
     _check(page_table, "page_table", torch.int32, dev, 2)
     _check(context_lens, "context_lens", torch.int32, dev, 1)
     B, q_len, hq, d = q.shape
@@ -291,7 +294,8 @@ def make_attn_args(q, k_pages, v_pages, page_table, context_lens, scale, *, head
         keep.append(hm)
         hm_ptr = ctypes.cast(hm, ctypes.POINTER(ctypes.c_int32))
     a = AttnArgs()
-    a.dtype = _DTYPES[q.dtype]
+    a.q_dtype = _DTYPES[q.dtype]
+    a.kv_dtype = _DTYPES[k_pages.dtype]
     a.batch, a.q_len, a.num_q_heads, a.num_kv_heads, a.head_dim = B, q_len, hq, hkv, d
     a.page_size, a.num_phys_pages, a.max_pages_per_seq = P, num_phys, page_table.shape[1]
     a.split_tokens = int(split_tokens)
@@ -332,22 +336,29 @@ def _attend(entry, ws_fn, q, k_pages, v_pages, page_table, context_lens, scale, 
             workspace, stream, extra=(), **kw):
     B, q_len, hq, d = q.shape
     want_lse = kw.pop("want_lse", True)
-    if out is None:
-        out = torch.empty((B, q_len, hq, d), dtype=torch.float32, device=q.device)
-    if lse is None and want_lse:
-        lse = torch.empty((B, q_len, hq), dtype=torch.float32, device=q.device)
+    # Buffers the binding allocates belong to the stream the call runs on:
+    # torch's caching allocator may hand a freed block to the next allocation
+    # of the stream it was allocated on, so a workspace allocated on another
+    # stream could be reused while the kernels still use it.
+    run_stream = torch.cuda.current_stream(q.device) if stream is None else stream
+    with torch.cuda.stream(run_stream):
+        if out is None:
+            out = torch.empty((B, q_len, hq, d), dtype=torch.float32, device=q.device)
+        if lse is None and want_lse:
+            lse = torch.empty((B, q_len, hq), dtype=torch.float32, device=q.device)
     args, keep = make_attn_args(q, k_pages, v_pages, page_table, context_lens, scale, out=out,
                                 lse=lse, **kw)
     if workspace is None:
         need = ws_fn(args)
-        workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=q.device)
+        with torch.cuda.stream(run_stream):
+            workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=q.device)
         args.workspace = _ptr(workspace)
         args.workspace_bytes = workspace.numel()
     else:
         _check(workspace, "workspace", None, q.device)
         args.workspace = _ptr(workspace)
         args.workspace_bytes = workspace.numel() * workspace.element_size()
-    st = getattr(lib, entry)(ctypes.byref(args), *extra, _stream(stream))
+    st = getattr(lib, entry)(ctypes.byref(args), *extra, _stream(run_stream))
     if st != ATLAS_OK:
         raise AtlasError(st, entry)
     return out, lse
@@ -364,15 +375,21 @@ def atlas_attend_decode(q, k_pages, v_pages, page_table, context_lens, scale, *,
 
 
 def atlas_attend_decode_regen(q, k_pages, v_pages, page_table, context_lens, scale, seed: int, layer: int = 0,
-                              *, head_map=None, window=None, sink_tokens=None, softcap=None, out=None,
-                              lse=None, workspace=None, split_tokens=0, stream=None, want_lse=True):
+                              *, seq_keys=None, head_map=None, window=None, sink_tokens=None, softcap=None,
+                              out=None, lse=None, workspace=None, split_tokens=0, stream=None, want_lse=True):
     """Decode attention in which page_table entries equal to ATLAS_PAGE_REGENERATE (-1) are
-    regenerated inside the kernel from (seed, layer, sequence, logical page) -- the rows
-    atlas_regenerate_pages would write -- instead of read from the arenas.  fp32 only.
+    regenerated inside the kernel from (seed, layer, sequence key, logical page) -- the rows
+    atlas_regenerate_pages would write for that key -- instead of read from the arenas.
+    seq_keys: int32 [B] device tensor of generator keys in [0, 65536) (None: the batch row).
     Returns (out [B][1][Hq][D] f32, lse [B][1][Hq] f32)."""
+    if seq_keys is not None:
+        _check(seq_keys, "seq_keys", torch.int32, q.device, 1)
+        if seq_keys.shape[0] != q.shape[0]:
+            raise ValueError("seq_keys needs one entry per sequence")
     return _attend("atlas_attend_decode_regen", atlas_decode_workspace_bytes, q, k_pages, v_pages,
                    page_table, context_lens, scale, out, lse, workspace, stream,
-                   extra=(ctypes.c_uint64(int(seed) & 0xFFFFFFFFFFFFFFFF), ctypes.c_int32(int(layer))),
+                   extra=(ctypes.c_uint64(int(seed) & 0xFFFFFFFFFFFFFFFF), ctypes.c_int32(int(layer)),
+                          _ptr(seq_keys)),
                    head_map=head_map, window=window, sink_tokens=sink_tokens, softcap=softcap,
                    split_tokens=split_tokens, want_lse=want_lse)
 
@@ -555,7 +572,9 @@ class HotCache:
         self.close()
 
     def plan(self, layer: int, seq_ids, context_lens, max_pages_per_seq: int):
-        """Returns (page_table int32 [B][max_pages_per_seq], jobs int32 [n][3]) as numpy arrays."""
+        """Returns (page_table int32 [B][max_pages_per_seq], jobs int32 [n][3]) as numpy arrays.
+        seq_ids (distinct, in [0, 65536)) are also the sequences' generator keys: pass them as
+        seq_keys to atlas_attend_decode_regen and the jobs to atlas_regenerate_pages."""
         import numpy as np
         ids = np.ascontiguousarray(seq_ids, dtype=np.int64)
         ctx = np.ascontiguousarray(context_lens, dtype=np.int32)

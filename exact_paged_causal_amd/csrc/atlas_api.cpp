@@ -106,8 +106,12 @@ int32_t check_shapes(const atlas_attn_args *a, bool decode, Plan *p)
 {
     if (!a)
         return fail(ATLAS_ERR_NULL, "args is NULL");
-    if (a->dtype != ATLAS_DTYPE_F32 && a->dtype != ATLAS_DTYPE_BF16)
-        return fail(ATLAS_ERR_UNSUPPORTED, "dtype %d has no kernel (f32=0, bf16=1)", a->dtype);
+    const bool qf = a->q_dtype == ATLAS_DTYPE_F32, qb = a->q_dtype == ATLAS_DTYPE_BF16;
+    const bool kvf = a->kv_dtype == ATLAS_DTYPE_F32, kvb = a->kv_dtype == ATLAS_DTYPE_BF16;
+    if (!(qf && kvf) && !(qb && kvb) && !(qf && kvb))
+        return fail(ATLAS_ERR_UNSUPPORTED,
+                    "(q_dtype, kv_dtype) = (%d, %d) has no kernel: (f32, f32), (bf16, bf16) or (f32, bf16) "
+                    "(f32=0, bf16=1)", a->q_dtype, a->kv_dtype);
     if (a->batch < 1 || a->q_len < 1 || a->num_q_heads < 1 || a->num_kv_heads < 1)
         return fail(ATLAS_ERR_SHAPE, "batch, q_len, num_q_heads, num_kv_heads must be >= 1");
     if (decode && a->q_len != 1)
@@ -179,14 +183,15 @@ int32_t check_shapes(const atlas_attn_args *a, bool decode, Plan *p)
     p->max_context = (int)max_ctx;
     p->rows_total = rows;
 
-    // Path: the tiled kernels for long prefills (window / sinks / softcap
-    // included; fp32 on split fp16 operands); else the split-KV kernels
-    // (matrix cores for bf16, vector ALUs for fp32).
-    if (!decode && a->dtype == ATLAS_DTYPE_BF16 && a->q_len >= 64)
+    // Path: the tiled kernels for long prefills with one dtype throughout
+    // (window / sinks / softcap included; fp32 on split fp16 operands); else
+    // the split-KV kernels (matrix cores for a bf16 cache, an fp32 query
+    // included; vector ALUs for fp32).
+    if (!decode && qb && kvb && a->q_len >= 64)
         p->path = Path::TiledPrefill;
-    else if (!decode && a->dtype == ATLAS_DTYPE_F32 && a->q_len >= 64)
+    else if (!decode && qf && kvf && a->q_len >= 64)
         p->path = Path::TiledSplit;
-    else if (a->dtype == ATLAS_DTYPE_BF16)
+    else if (kvb)
         p->path = Path::SplitMfma;
     else
         p->path = Path::SplitValu;
@@ -332,7 +337,7 @@ int32_t validate_device(const atlas_attn_args *a, const Plan &p, hipStream_t str
     int flag = 0;
     e = hipMemsetAsync(s.flag, 0, sizeof(int), stream);
     if (e == hipSuccess)
-        e = atlas::launch_scan(s, a->dtype, stream);
+        e = atlas::launch_scan(s, a->q_dtype, a->kv_dtype, stream);
     if (e == hipSuccess)
         e = hipMemcpyAsync(&flag, s.flag, sizeof(int), hipMemcpyDeviceToHost, stream);
     if (e == hipSuccess)
@@ -354,6 +359,7 @@ int32_t validate_device(const atlas_attn_args *a, const Plan &p, hipStream_t str
 struct RegenSpec {
     uint64_t seed;
     int32_t layer;
+    const int32_t *seq_keys;  // device [B] or null
 };
 
 // Host checks of atlas_attn_mods (NULL: none) and their kernel form.
@@ -396,12 +402,8 @@ int32_t attend(const atlas_attn_args *a, void *stream_ptr, bool decode, const Re
     if (st != ATLAS_OK)
         return st;
     if (regen) {
-        if (a->dtype != ATLAS_DTYPE_F32)
-            return fail(ATLAS_ERR_UNSUPPORTED, "in-kernel regeneration runs on fp32 K/V only");
         if (regen->layer < 0 || regen->layer >= (1 << 16))
             return fail(ATLAS_ERR_RANGE, "layer must be in [0, 65536)");
-        if (a->batch >= (1 << 16))
-            return fail(ATLAS_ERR_RANGE, "in-kernel regeneration takes fewer than 65536 sequences");
     }
     st = check_pointers(a, p);
     if (st != ATLAS_OK)
@@ -411,6 +413,18 @@ int32_t attend(const atlas_attn_args *a, void *stream_ptr, bool decode, const Re
         st = validate_device(a, p, stream, regen != nullptr);
         if (st != ATLAS_OK)
             return st;
+        if (regen && regen->seq_keys) {
+            std::vector<int32_t> keys(a->batch);
+            hipError_t e = hipMemcpyAsync(keys.data(), regen->seq_keys, sizeof(int32_t) * a->batch,
+                                          hipMemcpyDeviceToHost, stream);
+            if (e == hipSuccess)
+                e = hipStreamSynchronize(stream);
+            if (e != hipSuccess)
+                return fail(ATLAS_ERR_DEVICE, "validation copy failed: %s", hipGetErrorString(e));
+            for (int b = 0; b < a->batch; ++b)
+                if (keys[b] < 0 || keys[b] >= (1 << 16))
+                    return fail(ATLAS_ERR_RANGE, "seq_keys[%d] = %d outside [0, 65536)", b, keys[b]);
+        }
     }
 
     if (p.path == Path::TiledPrefill || p.path == Path::TiledSplit) {
@@ -510,9 +524,11 @@ int32_t attend(const atlas_attn_args *a, void *stream_ptr, bool decode, const Re
     k.scale = a->scale;
     k.mods = mods;
     k.groups = p.groups;
+    k.q_f32 = a->q_dtype == ATLAS_DTYPE_F32 ? 1 : 0;
     if (regen) {
         k.regen_seed = regen->seed;
         k.regen_layer = regen->layer;
+        k.seq_keys = regen->seq_keys;
         k.regen = 1;
     }
 
@@ -579,9 +595,10 @@ int32_t atlas_attend_mods(const atlas_attn_args *args, const atlas_attn_mods *mo
     return attend(args, stream, false, nullptr, mods);
 }
 
-int32_t atlas_attend_decode_regen(const atlas_attn_args *args, uint64_t seed, int32_t layer, void *stream)
+int32_t atlas_attend_decode_regen(const atlas_attn_args *args, uint64_t seed, int32_t layer,
+                                  const int32_t *seq_keys, void *stream)
 {
-    const RegenSpec r{seed, layer};
+    const RegenSpec r{seed, layer, seq_keys};
     return attend(args, stream, true, &r);
 }
 

@@ -22,8 +22,12 @@
 //      free, in (sequence, page) order, without evicting;
 //   4. the page table maps every page to its slot or to
 //      ATLAS_PAGE_REGENERATE; every admission is a regeneration job
-//      (batch row, logical page, slot) for atlas_regenerate_pages, to run
+//      (sequence id, logical page, slot) for atlas_regenerate_pages, to run
 //      before the attention call.
+// A sequence id is also the sequence's generator key (the regenerator and
+// the in-kernel regeneration take the same key), so a resident page holds
+// the same values whichever batch row the sequence occupies in a later call;
+// ids are therefore limited to the generator's 16-bit key range.
 // All checks run before any state changes (transactional accounting).
 #include <algorithm>
 #include <cstdint>
@@ -118,6 +122,9 @@ int32_t atlas_cache_plan(atlas_cache *c, int32_t layer, int32_t batch, const int
         if (context_lens[b] < 1 || context_lens[b] > max_ctx)
             return fail(ATLAS_ERR_RANGE, "context_lens[%d] = %d outside [1, %lld]", b, context_lens[b],
                         (long long)max_ctx);
+        if (seq_ids[b] < 0 || seq_ids[b] >= 65536)
+            return fail(ATLAS_ERR_RANGE, "seq_ids[%d] = %lld: sequence ids key the generator and must lie in "
+                                         "[0, 65536)", b, (long long)seq_ids[b]);
         for (int b2 = 0; b2 < b; ++b2)
             if (seq_ids[b2] == seq_ids[b])
                 return fail(ATLAS_ERR_SHAPE, "sequence id %lld appears twice in one call", (long long)seq_ids[b]);
@@ -179,7 +186,7 @@ int32_t atlas_cache_plan(atlas_cache *c, int32_t layer, int32_t batch, const int
         const Key k{seq_ids[b], layer, lp};
         c->slot_key[slot] = k;
         c->map[k] = Entry{slot, pinned, now};
-        admit_jobs[3 * jobs + 0] = b;
+        admit_jobs[3 * jobs + 0] = (int32_t)seq_ids[b];
         admit_jobs[3 * jobs + 1] = lp;
         admit_jobs[3 * jobs + 2] = slot;
         ++jobs;

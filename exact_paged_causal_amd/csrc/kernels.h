@@ -56,11 +56,16 @@ struct SplitArgs {
     int32_t rows_per_item;      // rows of one work item (a chunk of a K/V head's rows)
     int32_t n_chunks;           // chunks per K/V head
     float scale;
-    // In-kernel regeneration (fp32 fold only): page-table entries of -1 are
-    // regenerated from (regen_seed, regen_layer, sequence, logical page).
+    // In-kernel regeneration: page-table entries of -1 are regenerated from
+    // (regen_seed, regen_layer, sequence key, logical page); the key of
+    // sequence b is seq_keys[b] (clamped into [0, 65536)), or b without them.
     uint64_t regen_seed;
+    const int32_t *seq_keys;    // may be null
     int32_t regen_layer;
     int32_t regen;              // 0: every page is read from the arenas
+    // bf16 K/V fold only: q is fp32 (split into bf16 high and low parts).
+    int32_t q_f32;
+    int32_t pad0;
     // Merge of the tiled prefill's key splits (tiled_blocks > 0): the splits
     // of query i are ceil(n / tiled_blocks) for the n key blocks its query
     // block of tiled_npos positions visits (plan.h tiled_blocks).
@@ -141,6 +146,6 @@ struct ScanArgs {
                                 // product), 2 = Q, K and V (the fp32 tiled prefill's split operands)
 };
 
-hipError_t launch_scan(const ScanArgs &a, int dtype, hipStream_t stream);
+hipError_t launch_scan(const ScanArgs &a, int q_dtype, int kv_dtype, hipStream_t stream);
 
 }  // namespace atlas

@@ -32,7 +32,9 @@ __global__ __launch_bounds__(256) void regen_kernel(RegenArgs a, int items_per_j
         const int32_t seq = a.jobs[job * 3 + 0];
         const int32_t lp = a.jobs[job * 3 + 1];
         const int32_t phys = a.jobs[job * 3 + 2];
-        if (seq < 0 || lp < 0 || (unsigned)phys >= (unsigned)a.num_phys)
+        // The generator's counter holds 16 bits of the sequence key: keys
+        // outside [0, 65536) would alias another sequence's values.
+        if ((unsigned)seq >= 65536u || lp < 0 || (unsigned)phys >= (unsigned)a.num_phys)
             continue;
         const uint32_t token = ((uint32_t)lp << a.page_shift) + (uint32_t)t;
         const int64_t elem = ((((int64_t)phys * a.hkv + h) << a.page_shift) + t) * D + quad * 4;

@@ -34,8 +34,21 @@
 // non-temporal loads for K there.
 // At the end the 4 waves' states are combined in LDS and one (m, l, acc)
 // partial per row is written; merge.hip finishes.
+//
+// fp32 queries over the bf16 cache (QF32 instances): each query element is
+// carried as a bf16 high part and a bf16 remainder (~16 significant bits
+// together), and S^T takes one product per part; K stays exact bf16.
+//
+// In-kernel regeneration (REGEN instances, atlas_attend_decode_regen):
+// page-table entries of -1 mark pages that are not stored; a lane whose
+// 16-byte piece (8 dims of one key row) falls in such a page builds it from
+// the page regenerator's generator (philox.h: two calls of 4 dims each for K
+// and for V, rounded to bf16 as the regenerator stores them) while the chunk
+// is staged, so the fold sees the bits a regenerated page would hold.  Its
+// placeholder load reads row 0 of page 0 of the K/V head, which stays cached.
 #include "device.h"
 #include "kernels.h"
+#include "philox.h"
 
 namespace atlas {
 namespace {
@@ -76,9 +89,24 @@ __device__ __forceinline__ void split_hi_lo(float p0, float p1, uint32_t &hi, ui
     lo = __builtin_bit_cast(uint32_t, __builtin_convertvector(f32x2{r0, r1}, bf16x2));
 }
 
+// bf16 high parts and bf16 remainders of 8 fp32 values.
+__device__ __forceinline__ void split_hi_lo8(const float *x, bf16x8 &hi, bf16x8 &lo)
+{
+    u32x4 h, l;
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+        uint32_t hh, ll;
+        split_hi_lo(x[2 * e], x[2 * e + 1], hh, ll);
+        h[e] = hh;
+        l[e] = ll;
+    }
+    hi = __builtin_bit_cast(bf16x8, h);
+    lo = __builtin_bit_cast(bf16x8, l);
+}
+
 // MODS instances (atlas_attend_mods): non-causal rows plan and mask over
 // [0, ctx); ALiBi slopes and mask bits per (row, key).
-template <int D, bool MODS, bool NT>
+template <int D, bool MODS, bool NT, bool QF32, bool REGEN>
 __global__ __launch_bounds__(256) void split_mfma_kernel(SplitArgs a)
 {
     constexpr int KS = D / 32;                 // QK k-steps
@@ -122,7 +150,15 @@ __global__ __launch_bounds__(256) void split_mfma_kernel(SplitArgs a)
     const int np = ((kb - 1) >> ps) - p0 + 1;
     for (int t = tid; t < np; t += 256) {
         int pid = a.page_table[(int64_t)b * a.max_pages + p0 + t];
-        sm.pid[t] = ((unsigned)pid < (unsigned)a.num_phys) ? pid : 0;
+        sm.pid[t] = (REGEN && pid == -1) ? -1 : (((unsigned)pid < (unsigned)a.num_phys) ? pid : 0);
+    }
+    // REGEN: this sequence's generator key.
+    uint32_t seq_key = (uint32_t)b;
+    if constexpr (REGEN) {
+        if (a.seq_keys) {
+            const int sk = a.seq_keys[b];
+            seq_key = (uint32_t)(sk < 0 ? 0 : (sk > 65535 ? 65535 : sk));
+        }
     }
 
     // This lane's row (column of the S^T / O^T tiles) and its query operand.
@@ -137,38 +173,60 @@ __global__ __launch_bounds__(256) void split_mfma_kernel(SplitArgs a)
     const uint32_t *mrow =
         (MODS && row_ok && a.mods.mask) ? a.mods.mask + ((int64_t)b * a.q_len + qi) * a.mods.mask_words : nullptr;
     bf16x8 qf[KS];
+    bf16x8 qlo[QF32 ? KS : 1];  // QF32: the remainders of the query
     {
-        const uint16_t *qrow = reinterpret_cast<const uint16_t *>(a.q) +
-                               (((int64_t)b * a.q_len + qi) * a.hq + h) * D;
+        const int64_t qoff = (((int64_t)b * a.q_len + qi) * a.hq + h) * D;
 #pragma unroll
-        for (int s = 0; s < KS; ++s)
-            qf[s] = row_ok ? *reinterpret_cast<const bf16x8 *>(qrow + 32 * s + 8 * g4) : bf16x8{};
+        for (int s = 0; s < KS; ++s) {
+            if constexpr (QF32) {
+                float x[8] = {0.0f, 0.0f, 0.0f, 0.0f, 0.0f, 0.0f, 0.0f, 0.0f};
+                if (row_ok) {
+                    const float *qrow = reinterpret_cast<const float *>(a.q) + qoff + 32 * s + 8 * g4;
+                    const f32x4 x0 = *reinterpret_cast<const f32x4 *>(qrow);
+                    const f32x4 x1 = *reinterpret_cast<const f32x4 *>(qrow + 4);
+#pragma unroll
+                    for (int e = 0; e < 4; ++e) {
+                        x[e] = x0[e];
+                        x[4 + e] = x1[e];
+                    }
+                }
+                split_hi_lo8(x, qf[s], qlo[s]);
+            } else {
+                const uint16_t *qrow = reinterpret_cast<const uint16_t *>(a.q) + qoff;
+                qf[s] = row_ok ? *reinterpret_cast<const bf16x8 *>(qrow + 32 * s + 8 * g4) : bf16x8{};
+            }
+        }
     }
     __syncthreads();
 
     const uint16_t *kpages = reinterpret_cast<const uint16_t *>(a.k_pages);
     const uint16_t *vpages = reinterpret_cast<const uint16_t *>(a.v_pages);
     const int64_t head_rows = (int64_t)g << ps;
-    // Element offset of key j's row (clamped to the span's last key).
-    auto row_off = [&](int j) {
-        const int jj = j < kb ? j : kb - 1;
-        const int pid = sm.pid[(jj >> ps) - p0];
-        return ((((int64_t)pid * a.hkv) << ps) + head_rows + (jj & pmask)) * D;
-    };
-
     // Register buffer for one chunk's K and V, both staged through LDS: each
     // wave instruction reads whole rows (1 KiB runs).
     struct Regs {
         uint4 k[VCH];
         uint4 v[VCH];
+        uint32_t cold;  // REGEN: bit u set when piece u's page is regenerated here
     };
     auto load_chunk = [&](Regs &r, int cb) {
+        r.cold = 0;
 #pragma unroll
         for (int u = 0; u < VCH; ++u) {
             const int c = lane + 64 * u;
             const int key = c / CPR;
             const int col = c - key * CPR;
-            const int64_t off = row_off(cb + key) + col * 8;
+            // Key row (clamped to the span's last key).
+            const int j = cb + key;
+            const int jj = j < kb ? j : kb - 1;
+            const int pid = sm.pid[(jj >> ps) - p0];
+            int64_t row = (((int64_t)pid * a.hkv) << ps) + head_rows + (jj & pmask);
+            if constexpr (REGEN) {
+                // A cold key's placeholder load reads row 0 of page 0.
+                r.cold |= (pid < 0 ? 1u : 0u) << u;
+                row = pid < 0 ? head_rows : row;
+            }
+            const int64_t off = row * D + col * 8;
             if constexpr (NT) {
                 r.k[u] = stream_load16(kpages + off);
                 r.v[u] = stream_load16(vpages + off);
@@ -191,6 +249,34 @@ __global__ __launch_bounds__(256) void split_mfma_kernel(SplitArgs a)
     // (once both are consumed) the next chunk's loads into the same
     // registers, then softmax and O^T += V^T P^T from LDS.
     auto fold_chunk = [&](Regs &r, int cb, int cb_next) {
+        // REGEN: the pieces of cold keys come from the generator.
+        if constexpr (REGEN) {
+            if (r.cold) {
+#pragma unroll
+                for (int u = 0; u < VCH; ++u) {
+                    if ((r.cold >> u) & 1u) {
+                        const int c = lane + 64 * u;
+                        const int key = c / CPR;
+                        const int col = c - key * CPR;
+                        const uint32_t tok = (uint32_t)(cb + key < kb ? cb + key : kb - 1);
+                        uint32_t w[2][4];
+#pragma unroll
+                        for (int t = 0; t < 2; ++t) {
+#pragma unroll
+                            for (int hq4 = 0; hq4 < 2; ++hq4) {
+                                float z[4];
+                                regen_quad(a.regen_seed, (uint32_t)a.regen_layer, seq_key, 1u + t, (uint32_t)g,
+                                           tok, (uint32_t)(2 * col + hq4), z);
+                                w[t][2 * hq4 + 0] = f32_to_bf16_bits(z[0]) | (f32_to_bf16_bits(z[1]) << 16);
+                                w[t][2 * hq4 + 1] = f32_to_bf16_bits(z[2]) | (f32_to_bf16_bits(z[3]) << 16);
+                            }
+                        }
+                        r.k[u] = make_uint4(w[0][0], w[0][1], w[0][2], w[0][3]);
+                        r.v[u] = make_uint4(w[1][0], w[1][1], w[1][2], w[1][3]);
+                    }
+                }
+            }
+        }
         // Stage this chunk's K and V in the wave's LDS tiles, then refill
         // the registers with the next chunk.
 #pragma unroll
@@ -216,6 +302,8 @@ __global__ __launch_bounds__(256) void split_mfma_kernel(SplitArgs a)
             for (int t = 0; t < 2; ++t) {
                 const bf16x8 kf = *reinterpret_cast<const bf16x8 *>(&sm.k[wave][16 * t + l16][32 * s + 8 * g4]);
                 st[t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kf, qf[s], st[t], 0, 0, 0);
+                if constexpr (QF32)
+                    st[t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kf, qlo[s], st[t], 0, 0, 0);
             }
 
         // Scale, softcap, mask (log2 units).
@@ -347,20 +435,28 @@ __global__ __launch_bounds__(256) void split_mfma_kernel(SplitArgs a)
     }
 }
 
+template <int D, bool QF32>
+void (*pick_split_mfma(const SplitArgs &a))(SplitArgs)
+{
+    if (a.regen)
+        return split_mfma_kernel<D, false, false, QF32, true>;
+    if (a.mods.any)
+        return split_mfma_kernel<D, true, false, QF32, false>;
+    return a.n_chunks == 1 ? split_mfma_kernel<D, false, true, QF32, false> : split_mfma_kernel<D, false, false, QF32, false>;
+}
+
 }  // namespace
 
 hipError_t launch_split_mfma(const SplitArgs &a, hipStream_t stream)
 {
-    if (a.rows_per_item != kRowsMax)
+    if (a.rows_per_item != kRowsMax || (a.regen && a.mods.any))
         return hipErrorInvalidValue;
     dim3 grid(a.max_splits, a.hkv * a.n_chunks, a.batch);
     void (*kernel)(SplitArgs);
     if (a.head_dim == 64)
-        kernel = a.mods.any ? split_mfma_kernel<64, true, false>
-                 : (a.n_chunks == 1 ? split_mfma_kernel<64, false, true> : split_mfma_kernel<64, false, false>);
+        kernel = a.q_f32 ? pick_split_mfma<64, true>(a) : pick_split_mfma<64, false>(a);
     else
-        kernel = a.mods.any ? split_mfma_kernel<128, true, false>
-                 : (a.n_chunks == 1 ? split_mfma_kernel<128, false, true> : split_mfma_kernel<128, false, false>);
+        kernel = a.q_f32 ? pick_split_mfma<128, true>(a) : pick_split_mfma<128, false>(a);
     hipLaunchKernelGGL(kernel, grid, dim3(256), 0, stream, a);
     return hipGetLastError();
 }

@@ -30,8 +30,9 @@
 // time by the page regenerator's generator (philox.h) for exactly this
 // lane's dims -- a lane's 16-byte piece is one generator call of 4 dims --
 // so the fold sees the same bits a regenerated scratch page would hold.
-// Their loads still go out (to page 0, cached) so that the prefetch stays
-// unconditional.
+// Their loads still go out so that the prefetch stays unconditional, but all
+// to one row (row 0 of page 0 for the item's K/V head), which stays in cache
+// however many resident rows stream past it.
 //
 // Modifications (MODS instances, atlas_attend_mods): non-causal rows see
 // every key of the context (the split plan then spans [0, L)); an ALiBi slope
@@ -169,6 +170,14 @@ __global__ __launch_bounds__(256) void split_valu_kernel(SplitArgs a)
     }
 
     const float qk_scale = a.scale;
+    // REGEN: this sequence's generator key.
+    uint32_t seq_key = (uint32_t)b;
+    if constexpr (REGEN) {
+        if (a.seq_keys) {
+            const int sk = a.seq_keys[b];
+            seq_key = (uint32_t)(sk < 0 ? 0 : (sk > 65535 ? 65535 : sk));
+        }
+    }
     const E *kbase = reinterpret_cast<const E *>(a.k_pages);
     const E *vbase = reinterpret_cast<const E *>(a.v_pages);
     const int64_t head_off = (int64_t)g << ps;  // rows before head g inside a page
@@ -189,12 +198,13 @@ __global__ __launch_bounds__(256) void split_valu_kernel(SplitArgs a)
         for (int u = 0; u < KU; ++u) {
             const int key = base + u * (4 * GPW) + wave * GPW + grp;
             const int jj = key < kb ? key : kb - 1;
-            int pid = s_pid[(jj >> ps) - p0];
+            const int pid = s_pid[(jj >> ps) - p0];
+            int64_t row = ((int64_t)pid * a.hkv << ps) + head_off + (jj & pmask);
             if constexpr (REGEN) {
+                // A cold key's placeholder load reads row 0 of page 0.
                 bf.cold |= (pid < 0 ? 1u : 0u) << u;
-                pid = pid < 0 ? 0 : pid;
+                row = pid < 0 ? head_off : row;
             }
-            const int64_t row = ((int64_t)pid * a.hkv << ps) + head_off + (jj & pmask);
             const E *kr = kbase + row * D;
             const E *vr = vbase + row * D;
 #pragma unroll
@@ -238,9 +248,9 @@ __global__ __launch_bounds__(256) void split_valu_kernel(SplitArgs a)
 #pragma unroll
                         for (int n = 0; n < NL; ++n) {
                             const uint32_t quad = (uint32_t)(n * R + li);
-                            regen_quad(a.regen_seed, (uint32_t)a.regen_layer, (uint32_t)b, 1u, (uint32_t)g, tok,
+                            regen_quad(a.regen_seed, (uint32_t)a.regen_layer, seq_key, 1u, (uint32_t)g, tok,
                                        quad, &kv[u][n * EPC]);
-                            regen_quad(a.regen_seed, (uint32_t)a.regen_layer, (uint32_t)b, 2u, (uint32_t)g, tok,
+                            regen_quad(a.regen_seed, (uint32_t)a.regen_layer, seq_key, 2u, (uint32_t)g, tok,
                                        quad, &vv[u][n * EPC]);
                         }
                     }

@@ -44,7 +44,7 @@ __device__ __forceinline__ bool finite_elem<uint16_t>(uint16_t x)
     return (x & 0x7F80u) != 0x7F80u;
 }
 
-template <typename E>
+template <typename EQ, typename E>
 __global__ __launch_bounds__(256) void scan_kernel(ScanArgs a)
 {
     // blockIdx.x: logical page index (last one: the queries), blockIdx.y: sequence
@@ -56,10 +56,10 @@ __global__ __launch_bounds__(256) void scan_kernel(ScanArgs a)
     bool wide = false;
     if (lp == a.max_pages) {
         const int64_t n = (int64_t)a.q_len * a.hq * a.head_dim;
-        const E *q = reinterpret_cast<const E *>(a.q) + (int64_t)b * n;
+        const EQ *q = reinterpret_cast<const EQ *>(a.q) + (int64_t)b * n;
         for (int64_t i = threadIdx.x; i < n; i += 256) {
-            bad |= !finite_elem<E>(q[i]);
-            wide |= a.check_f16 == 2 && beyond_f16<E>(q[i]);
+            bad |= !finite_elem<EQ>(q[i]);
+            wide |= a.check_f16 == 2 && beyond_f16<EQ>(q[i]);
         }
     } else {
         const int P = 1 << a.page_shift;
@@ -91,13 +91,15 @@ __global__ __launch_bounds__(256) void scan_kernel(ScanArgs a)
 
 }  // namespace
 
-hipError_t launch_scan(const ScanArgs &a, int dtype, hipStream_t stream)
+hipError_t launch_scan(const ScanArgs &a, int q_dtype, int kv_dtype, hipStream_t stream)
 {
     dim3 grid(a.max_pages + 1, a.batch);
-    if (dtype == 0)
-        hipLaunchKernelGGL(scan_kernel<float>, grid, dim3(256), 0, stream, a);
+    if (kv_dtype == 0)
+        hipLaunchKernelGGL((scan_kernel<float, float>), grid, dim3(256), 0, stream, a);
+    else if (q_dtype == 0)
+        hipLaunchKernelGGL((scan_kernel<float, uint16_t>), grid, dim3(256), 0, stream, a);
     else
-        hipLaunchKernelGGL(scan_kernel<uint16_t>, grid, dim3(256), 0, stream, a);
+        hipLaunchKernelGGL((scan_kernel<uint16_t, uint16_t>), grid, dim3(256), 0, stream, a);
     return hipGetLastError();
 }
 

@@ -27,8 +27,8 @@
  *
  * Memory layout (all row-major, all caller-owned; the library never
  * allocates device memory):
- *   q           [B][q_len][Hq][D]                 (dtype)
- *   k_pages     [num_phys_pages][Hkv][P][D]       (dtype) one (page, head)
+ *   q           [B][q_len][Hq][D]                 (q_dtype)
+ *   k_pages     [num_phys_pages][Hkv][P][D]       (kv_dtype) one (page, head)
  *   v_pages     [num_phys_pages][Hkv][P][D]       slab is K[token][dim],
  *                                                 CFR-Atlas "Minimal integration"
  *   page_table  [B][max_pages_per_seq] int32      logical page -> physical id
@@ -66,9 +66,13 @@
 extern "C" {
 #endif
 
-#define ATLAS_ABI_VERSION 1
+#define ATLAS_ABI_VERSION 2
 
-/* Status codes returned by every entry point. */
+/* Status codes returned by every entry point.  The CFR-Atlas README
+ * ("Validation and hardening") rejects invalid configuration and non-finite
+ * inputs with an error instead of a partial result; the ferrox-core crate
+ * index ("kernel_registry") makes a missing kernel a loud error.  These codes
+ * are how this library reports both. */
 enum {
     ATLAS_OK = 0,
     ATLAS_ERR_NULL = 1,        /* a required pointer is NULL */
@@ -81,7 +85,7 @@ enum {
     ATLAS_ERR_DEVICE = 8       /* a HIP runtime error */
 };
 
-/* Element types of q, k_pages and v_pages (all three share one type). */
+/* Element types of q (q_dtype) and of k_pages / v_pages (kv_dtype). */
 enum {
     ATLAS_DTYPE_F32 = 0,
     ATLAS_DTYPE_BF16 = 1
@@ -89,10 +93,14 @@ enum {
 
 /*
  * Arguments of one attention call.  Supported: head_dim 64 or 128; page_size
- * a power of two in [1, 4096]; Hq, Hkv <= 256; dtype f32 or bf16.
+ * a power of two in [1, 4096]; Hq, Hkv <= 256; (q_dtype, kv_dtype) one of
+ * (f32, f32), (bf16, bf16) or (f32, bf16) -- an fp32 query over a bf16 cache
+ * -- else ATLAS_ERR_UNSUPPORTED.  The CPUAttn README ("Parallel example")
+ * passes Q, K and V as separate caller-owned tensors, K/V read-only.
  */
 typedef struct atlas_attn_args {
-    int32_t dtype;              /* ATLAS_DTYPE_* of q, k_pages, v_pages */
+    int32_t q_dtype;            /* ATLAS_DTYPE_* of q */
+    int32_t kv_dtype;           /* ATLAS_DTYPE_* of k_pages and v_pages */
     int32_t batch;              /* B >= 1 */
     int32_t q_len;              /* queries per sequence (1 for decode) */
     int32_t num_q_heads;        /* Hq */
@@ -104,7 +112,6 @@ typedef struct atlas_attn_args {
     int32_t split_tokens;       /* keys per split-KV work item; 0 = library's choice
                                    (results depend on it only through rounding order) */
     float scale;                /* score scale, finite and > 0, e.g. 1/sqrt(D) */
-    int32_t reserved0;
     const int32_t *head_map;    /* HOST [Hq] -> K/V head, or NULL for h / (Hq / Hkv) */
     const void *q;              /* device, see layout above */
     const void *k_pages;        /* device */
@@ -120,7 +127,8 @@ typedef struct atlas_attn_args {
     size_t workspace_bytes;
 } atlas_attn_args;
 
-/* One page to regenerate: page `logical_page` of sequence `seq` is written
+/* One page to regenerate: page `logical_page` of the sequence whose generator
+ * key is `seq` (in [0, 65536); other values make the job a no-op) is written
  * into physical page `phys_page` of both arenas (all Hkv heads). */
 typedef struct atlas_regen_job {
     int32_t seq;
@@ -139,7 +147,8 @@ typedef struct atlas_regen_job {
  * as r cos(2 pi u1), r sin(2 pi u1) with r = sqrt(-2 ln u0), words 2,3 give
  * dims 4k+2, 4k+3, and word x maps to u = (floor(x / 512) + 1/2) * 2^-23.
  * Computed in fp32; bf16 arenas store it rounded to nearest-even.
- * Requires layer < 2^16, seq < 2^16, Hkv < 2^30.
+ * Requires layer < 2^16 and Hkv < 2^30 (ATLAS_ERR_RANGE); jobs with seq
+ * outside [0, 2^16) are skipped.
  */
 typedef struct atlas_regen_args {
     uint64_t seed;
@@ -152,31 +161,51 @@ typedef struct atlas_regen_args {
     int32_t num_jobs;           /* >= 0 */
     int32_t reserved0;
     const atlas_regen_job *jobs;/* device [num_jobs]; jobs with phys_page outside
-                                   [0, num_phys_pages) or seq/logical_page < 0 are skipped */
+                                   [0, num_phys_pages), seq outside [0, 65536) or
+                                   logical_page < 0 are skipped */
     void *k_pages;              /* device arena */
     void *v_pages;              /* device arena */
 } atlas_regen_args;
 
-/* ABI version of the loaded library (ATLAS_ABI_VERSION at build time). */
+/* ABI version of the loaded library (ATLAS_ABI_VERSION at build time).  The
+ * CPUAttn README ("Runtime ownership") keys its compiled artifacts by ABI so
+ * that a caller never runs code built against another argument layout; a
+ * binding compares this value with the version it was written for. */
 int32_t atlas_abi_version(void);
 
-/* Static description of a status code. */
+/* Static description of a status code (never NULL; "unknown status" for a
+ * value outside the enum).  CFR-Atlas README, "Validation and hardening":
+ * rejected configuration is reported, not silently repaired. */
 const char *atlas_status_str(int32_t status);
 
-/* Detail of the last non-OK status returned on this thread ("" if none). */
+/* Detail of the last non-OK status returned on the calling thread ("" after
+ * a successful call or if none); the string is owned by the library and valid
+ * until the thread's next call.  Same passage as atlas_status_str. */
 const char *atlas_last_error(void);
 
-/* Workspace bytes atlas_attend_decode / atlas_attend_prefill need for these
- * arguments (pointers are not inspected).  Returns SIZE_MAX when the sizes
- * are invalid (the reason is in atlas_last_error()). */
+/* Workspace bytes atlas_attend_decode / atlas_attend_prefill (and
+ * atlas_attend_mods, atlas_attend_decode_regen) need for these arguments; only
+ * the sizes are read, pointers are not inspected.  The CPUAttn README
+ * ("Runtime ownership") keeps workspace and output allocation outside the
+ * timed native call; here the caller allocates the workspace once (device
+ * memory, any alignment of 256 bytes or more) and may reuse it for every call
+ * with the same or smaller sizes.  Returns SIZE_MAX when the sizes are
+ * invalid (the reason is in atlas_last_error()). */
 size_t atlas_decode_workspace_bytes(const atlas_attn_args *args);
 size_t atlas_prefill_workspace_bytes(const atlas_attn_args *args);
 
 /*
- * Decode: one query per sequence (q_len must be 1) at position L_b - 1.
- * Split-KV: each (sequence, K/V head, span of keys) work item folds its keys
- * into an online-softmax state for all q-heads of that K/V head, then a merge
- * pass combines the states of each (sequence, q-head) by log-sum-exp.
+ * Decode: one query per sequence (q_len must be 1) at position L_b - 1 (the
+ * CFR-Atlas README, "Minimal integration", passes the context length
+ * including the current token).  The CFR-Atlas README ("Core contract") folds
+ * each page into an online-softmax state and requires the folded result to
+ * equal full-K/V attention; the CPUAttn README ("Operator model") allows a
+ * split over keys only with a structured merge.  Here each (sequence, K/V
+ * head, span of keys) work item folds its keys into an online-softmax state
+ * for all q-heads of that K/V head, and a log-sum-exp merge combines the
+ * states of each (sequence, q-head) in a fixed span order (deterministic:
+ * the same arguments give the same bits, whatever the physical page order).
+ * Arguments as described above; workspace >= atlas_decode_workspace_bytes().
  */
 int32_t atlas_attend_decode(const atlas_attn_args *args, void *stream);
 
@@ -251,14 +280,20 @@ int32_t atlas_regenerate_pages(const atlas_regen_args *args, void *stream);
  * traffic.  Same as atlas_attend_decode (same arguments, workspace and
  * output), except that page_table entries equal to ATLAS_PAGE_REGENERATE
  * stand for the rows atlas_regenerate_pages would write for
- * (seed, layer, sequence b, that logical page): the result equals
+ * (seed, layer, key seq_keys[b], that logical page): the result equals
  * regenerating those pages into the pool and calling atlas_attend_decode, to
- * the bit.  Nothing of such a page is read from the arenas.  fp32 only
- * (ATLAS_ERR_UNSUPPORTED otherwise); requires layer in [0, 65536) and
- * batch < 65536 (ATLAS_ERR_RANGE).  Validation mode accepts
+ * the bit.  Nothing of such a page is read from the arenas.
+ *   seq_keys  device [B] int32, each sequence's generator key in [0, 65536)
+ *             (a persistent sequence id, so that a sequence keeps its K/V when
+ *             it moves to another batch row between calls), or NULL: the key
+ *             is the batch row b.  Keys outside [0, 65536) are clamped into it
+ *             outside validation mode (ATLAS_ERR_RANGE in validation mode).
+ * kv_dtype f32 or bf16 (any q_dtype pairing atlas_attend_decode takes);
+ * requires layer in [0, 65536) (ATLAS_ERR_RANGE).  Validation mode accepts
  * ATLAS_PAGE_REGENERATE entries.
  */
-int32_t atlas_attend_decode_regen(const atlas_attn_args *args, uint64_t seed, int32_t layer, void *stream);
+int32_t atlas_attend_decode_regen(const atlas_attn_args *args, uint64_t seed, int32_t layer,
+                                  const int32_t *seq_keys, void *stream);
 
 /*
  * Appending K/V rows: the decode step's write of each sequence's new tokens
@@ -369,8 +404,10 @@ void atlas_cache_destroy(atlas_cache *cache);
 
 /*
  * Plan one attention call of `layer` over `batch` sequences (host arrays):
- * seq_ids [batch] (distinct), context_lens [batch] in [1, max_pages_per_seq *
- * page_size].  In order: the call's resident pages are hits; with
+ * seq_ids [batch] (distinct, each in [0, 65536): a sequence id is also its
+ * generator key, the seq_keys entry atlas_attend_decode_regen must be given
+ * for that sequence's batch row), context_lens [batch] in [1,
+ * max_pages_per_seq * page_size].  In order: the call's resident pages are hits; with
  * recent_tokens, each sequence's recent pages that are not resident are
  * admitted, newest first, into a free slot or in place of the least recently
  * used page this call does not read (pages outside every recent window
@@ -379,8 +416,10 @@ void atlas_cache_destroy(atlas_cache *cache);
  * still free, in (sequence, page) order.  Writes page_table [batch]
  * [max_pages_per_seq] (host): each page's slot, or ATLAS_PAGE_REGENERATE for
  * pages left cold and for entries past the context; and admit_jobs
- * [*n_jobs][3] = (batch row, logical page, slot) for atlas_regenerate_pages,
- * which must run before the attention call reads the admitted slots.
+ * [*n_jobs][3] = (sequence id, logical page, slot) for atlas_regenerate_pages,
+ * which must run before the attention call reads the admitted slots.  A
+ * sequence may occupy a different batch row in every call: its resident pages
+ * and its regenerated ones come from the same key.
  * max_jobs must be >= min(pages in the call, capacity) (ATLAS_ERR_SHAPE).
  */
 int32_t atlas_cache_plan(atlas_cache *cache, int32_t layer, int32_t batch, const int64_t *seq_ids,

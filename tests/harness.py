@@ -24,6 +24,11 @@ def tdtype(w):
     return torch.float32 if w.dtype == "f32" else torch.bfloat16
 
 
+def seq_keys_tensor(w, device="cuda"):
+    """The workload's generator keys as a device tensor (None: batch rows)."""
+    return None if w.seq_keys is None else torch.from_numpy(np.asarray(w.seq_keys, np.int32)).to(device)
+
+
 def assert_close(got, want, dtype: str, what: str = ""):
     got = np.asarray(got, np.float64)
     want = np.asarray(want, np.float64)
@@ -68,7 +73,7 @@ def build(w, device="cuda", hot_fraction=None, layout_seed=0, extra_phys=0, pois
     import exact_paged_causal_amd as atlas
     lay = workloads.page_layout(w, hot_fraction, layout_seed, extra_phys)
     dt = tdtype(w)
-    q = workloads.randn(workloads.query_shape(w), seed=w.seed * 100 + 1, dtype=w.dtype, device=device)
+    q = workloads.randn(workloads.query_shape(w), seed=w.seed * 100 + 1, dtype=w.qdt, device=device)
     shape = workloads.arena_shape(w, lay.num_phys)
     fill = float("nan") if poison else 0.0
     pt = torch.from_numpy(lay.page_table).to(device)
@@ -76,8 +81,8 @@ def build(w, device="cuda", hot_fraction=None, layout_seed=0, extra_phys=0, pois
     if w.regenerated:
         k = torch.full(shape, fill, dtype=dt, device=device)
         v = torch.full(shape, fill, dtype=dt, device=device)
-        hot = torch.from_numpy(lay.hot_jobs).to(device) if len(lay.hot_jobs) else None
-        cold = torch.from_numpy(lay.cold_jobs).to(device) if len(lay.cold_jobs) else None
+        hot = torch.from_numpy(workloads.key_jobs(w, lay.hot_jobs)).to(device) if len(lay.hot_jobs) else None
+        cold = torch.from_numpy(workloads.key_jobs(w, lay.cold_jobs)).to(device) if len(lay.cold_jobs) else None
         if regen_hot and hot is not None:
             atlas.atlas_regenerate_pages(k, v, hot, seed=w.seed, layer=w.layer)
     else:
@@ -142,9 +147,10 @@ class OracleSource:
         if w.regenerated:
             kind = "f32" if w.dtype == "f32" else "bf16"
             ks, vs = [], []
+            key = w.seq_key(b)
             for h in range(w.hkv):
-                kr = oracle.regen_rows(w.seed, w.layer, b, oracle.TENSOR_K, h, 0, L, w.head_dim, kind)
-                vr = oracle.regen_rows(w.seed, w.layer, b, oracle.TENSOR_V, h, 0, L, w.head_dim, kind)
+                kr = oracle.regen_rows(w.seed, w.layer, key, oracle.TENSOR_K, h, 0, L, w.head_dim, kind)
+                vr = oracle.regen_rows(w.seed, w.layer, key, oracle.TENSOR_V, h, 0, L, w.head_dim, kind)
                 if kind == "bf16":
                     kr, vr = oracle.bf16_bits_to_f32(kr), oracle.bf16_bits_to_f32(vr)
                 ks.append(kr)
@@ -155,8 +161,10 @@ class OracleSource:
                 oracle.gather_pages(self.v_host, pt, L, w.page_size))
 
 
-def oracle_answer(inp: DeviceInputs, b: int, rows=None, head_map=None, src: OracleSource | None = None):
-    """Oracle output for sequence b (all query rows, or the listed ones)."""
+def oracle_answer(inp: DeviceInputs, b: int, rows=None, head_map=None, src: OracleSource | None = None,
+                  heads=None):
+    """Oracle output for sequence b (all query rows, or the listed ones; all
+    q-heads, or the listed ones)."""
     w = inp.w
     src = src or OracleSource(inp)
     k, v = src.kv(b)
@@ -166,21 +174,37 @@ def oracle_answer(inp: DeviceInputs, b: int, rows=None, head_map=None, src: Orac
     if rows is not None:
         q, pos = q[rows], pos[rows]
     hm = oracle.default_head_map(w.hq, w.hkv) if head_map is None else np.asarray(head_map, np.int32)
+    if heads is not None:
+        q, hm = np.ascontiguousarray(q[:, heads]), hm[heads]
     win = int(w.window[b]) if w.window is not None else 0
     snk = int(w.sinks[b]) if (w.sinks is not None and win > 0) else 0
     cap = float(w.softcap[b]) if w.softcap is not None else 0.0
     return oracle.attend(q, k, v, pos, hm, w.scale, win, snk, cap)
 
 
-def check_against_oracle(inp, out, lse, seqs=None, rows=None, head_map=None, what=""):
+def check_against_oracle(inp, out, lse, seqs=None, rows=None, head_map=None, what="", heads=None):
     w = inp.w
     src = OracleSource(inp)
     out_h = to_f32_numpy(out)
     lse_h = to_f32_numpy(lse) if lse is not None else None
     for b in (range(w.batch) if seqs is None else seqs):
-        ref_o, ref_l = oracle_answer(inp, b, rows, head_map, src)
+        ref_o, ref_l = oracle_answer(inp, b, rows, head_map, src, heads)
         got_o = out_h[b] if rows is None else out_h[b][rows]
+        got_o = got_o if heads is None else got_o[:, heads]
         assert_close(got_o, ref_o, w.dtype, f"{what} out[b={b}]")
         if lse_h is not None:
             got_l = lse_h[b] if rows is None else lse_h[b][rows]
+            got_l = got_l if heads is None else got_l[:, heads]
             assert_close(got_l, ref_l, w.dtype, f"{what} lse[b={b}]")
+
+
+def full_size_blocks(w, seed: int, edge: int = 512):
+    """(rows, heads) blocks the oracle checks on a full-size prefill it cannot
+    afford whole: every row of one seeded q-head per K/V head, and the first
+    and last `edge` rows of every q-head."""
+    rng = np.random.default_rng(seed)
+    hm = oracle.default_head_map(w.hq, w.hkv)
+    heads = np.array(sorted(int(rng.choice(np.flatnonzero(hm == g))) for g in range(w.hkv)))
+    n = w.q_len
+    ends = np.array(sorted(set(range(min(edge, n))) | set(range(max(0, n - edge), n))))
+    return [(np.arange(n), heads), (ends, np.arange(w.hq))]

@@ -40,7 +40,7 @@ def test_library_exports_every_declared_symbol():
                         check=True).stdout
     exported = set(re.findall(r" T (atlas_\w+)", nm))
     assert exported == set(_declared_functions())
-    assert A.atlas_abi_version() == 1
+    assert A.atlas_abi_version() == 2
     assert A.atlas_status_str(A.ATLAS_ERR_POOL) == "page id outside the physical pool"
 
 
@@ -58,6 +58,7 @@ def test_binding_structs_mirror_the_header():
     assert [f[0] for f in A.RegenArgs._fields_] == _struct_offsets_from_header("atlas_regen_args")
     assert [f[0] for f in A.RegenJob._fields_] == _struct_offsets_from_header("atlas_regen_job")
     assert ctypes.sizeof(A.AttnArgs) == 4 * 12 + 8 * 13
+    assert A.AttnArgs.head_map.offset == 48
     assert ctypes.sizeof(A.RegenArgs) == 8 + 4 * 8 + 8 * 3
     assert [f[0] for f in A.AttnMods._fields_] == _struct_offsets_from_header("atlas_attn_mods")
     assert ctypes.sizeof(A.AttnMods) == 4 * 2 + 8 * 2
@@ -72,7 +73,8 @@ FAKE = 0x10000  # never dereferenced: every case below fails host validation fir
 def _valid_args(**over):
     from exact_paged_causal_amd import atlas as A
     a = A.AttnArgs()
-    a.dtype, a.batch, a.q_len, a.num_q_heads, a.num_kv_heads, a.head_dim = 0, 2, 1, 8, 2, 64
+    a.q_dtype, a.kv_dtype = 0, 0
+    a.batch, a.q_len, a.num_q_heads, a.num_kv_heads, a.head_dim = 2, 1, 8, 2, 64
     a.page_size, a.num_phys_pages, a.max_pages_per_seq, a.split_tokens, a.scale = 16, 10, 4, 0, 0.125
     for f in ("q", "k_pages", "v_pages", "page_table", "context_lens", "out", "workspace"):
         setattr(a, f, FAKE)
@@ -83,7 +85,7 @@ def _valid_args(**over):
 
 
 @pytest.mark.parametrize("field,value,status", [
-    ("dtype", 5, 4), ("batch", 0, 2), ("q_len", 0, 2), ("q_len", 2, 2),      # decode needs q_len 1
+    ("q_dtype", 5, 4), ("kv_dtype", 5, 4), ("q_dtype", -1, 4), ("batch", 0, 2), ("q_len", 0, 2), ("q_len", 2, 2),      # decode needs q_len 1
     ("num_q_heads", 7, 2), ("num_kv_heads", 0, 2), ("num_q_heads", 512, 4),
     ("head_dim", 96, 4), ("page_size", 0, 2), ("page_size", 24, 4), ("page_size", 8192, 4),
     ("num_phys_pages", 0, 2), ("max_pages_per_seq", 0, 2), ("split_tokens", -1, 3),
@@ -97,6 +99,30 @@ def test_decode_rejects_bad_arguments_before_launch(field, value, status):
     st = A.lib.atlas_attend_decode(ctypes.byref(a), None)
     assert st == status, (st, A.atlas_last_error())
     assert A.atlas_last_error() != ""
+
+
+def test_dtype_pairs():
+    """(q_dtype, kv_dtype): (f32, f32), (bf16, bf16) and an fp32 query over a
+    bf16 cache have kernels; a bf16 query over an fp32 cache does not."""
+    from exact_paged_causal_amd import atlas as A
+    for qd, kd, want in ((0, 0, A.ATLAS_ERR_NULL), (1, 1, A.ATLAS_ERR_NULL), (0, 1, A.ATLAS_ERR_NULL),
+                         (1, 0, A.ATLAS_ERR_UNSUPPORTED)):
+        # q = NULL: a supported pair gets past the dtype check to the pointer check
+        a = _valid_args(q_dtype=qd, kv_dtype=kd, q=None)
+        for fn in (A.lib.atlas_attend_decode, A.lib.atlas_attend_prefill):
+            st = fn(ctypes.byref(a), None)
+            assert st == want, (qd, kd, st, A.atlas_last_error())
+        if want == A.ATLAS_ERR_UNSUPPORTED:
+            assert "kv_dtype" in A.atlas_last_error()
+            assert A.lib.atlas_decode_workspace_bytes(ctypes.byref(a)) == ctypes.c_size_t(-1).value
+        else:
+            assert A.lib.atlas_decode_workspace_bytes(ctypes.byref(a)) not in (0, ctypes.c_size_t(-1).value)
+    # the mixed pair always plans the split-KV path, for prefills too: its
+    # workspace holds partial states, unlike the tiled bf16 prefill's header
+    mixed = _valid_args(q_dtype=0, kv_dtype=1, q_len=64, max_pages_per_seq=8, num_q_heads=8)
+    same = _valid_args(q_dtype=1, kv_dtype=1, q_len=64, max_pages_per_seq=8, num_q_heads=8)
+    assert A.lib.atlas_prefill_workspace_bytes(ctypes.byref(same)) == 256
+    assert A.lib.atlas_prefill_workspace_bytes(ctypes.byref(mixed)) > 256
 
 
 def test_prefill_limits_and_head_map():
@@ -127,13 +153,16 @@ def test_workspace_sizing():
 def test_decode_regen_rejects_bad_arguments_before_launch():
     from exact_paged_causal_amd import atlas as A
     fn = A.lib.atlas_attend_decode_regen
-    a = _valid_args(dtype=1)                      # in-kernel regeneration is fp32 only
-    assert fn(ctypes.byref(a), 7, 0, None) == A.ATLAS_ERR_UNSUPPORTED
+    a = _valid_args(q_dtype=1, kv_dtype=0)        # no kernel for a bf16 query over fp32 pages
+    assert fn(ctypes.byref(a), 7, 0, None, None) == A.ATLAS_ERR_UNSUPPORTED
+    for qd, kd in ((0, 0), (1, 1), (0, 1)):      # every supported pair gets past the dtype check
+        a = _valid_args(q_dtype=qd, kv_dtype=kd, q=None)
+        assert fn(ctypes.byref(a), 7, 0, None, None) == A.ATLAS_ERR_NULL, (qd, kd)
     for layer in (-1, 1 << 16):
-        assert fn(ctypes.byref(_valid_args()), 7, layer, None) == A.ATLAS_ERR_RANGE, layer
-    assert fn(ctypes.byref(_valid_args(q_len=2)), 7, 0, None) == A.ATLAS_ERR_SHAPE   # decode only
-    assert fn(ctypes.byref(_valid_args(q=None)), 7, 0, None) == A.ATLAS_ERR_NULL
-    assert fn(ctypes.byref(_valid_args(workspace_bytes=16)), 7, 0, None) == A.ATLAS_ERR_WORKSPACE
+        assert fn(ctypes.byref(_valid_args()), 7, layer, None, None) == A.ATLAS_ERR_RANGE, layer
+    assert fn(ctypes.byref(_valid_args(q_len=2)), 7, 0, None, None) == A.ATLAS_ERR_SHAPE   # decode only
+    assert fn(ctypes.byref(_valid_args(q=None)), 7, 0, None, None) == A.ATLAS_ERR_NULL
+    assert fn(ctypes.byref(_valid_args(workspace_bytes=16)), 7, 0, FAKE, None) == A.ATLAS_ERR_WORKSPACE
     assert A.ATLAS_PAGE_REGENERATE == -1
     assert "#define ATLAS_PAGE_REGENERATE (-1)" in open(HEADER).read()
 

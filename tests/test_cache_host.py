@@ -18,31 +18,36 @@ def resident(pt):
     return {(b, lp): int(s) for b in range(pt.shape[0]) for lp, s in enumerate(pt[b]) if s >= 0}
 
 
-def check_contract(pt, jobs, ctx, slots):
+def check_contract(pt, jobs, ctx, slots, ids):
     """Slots are distinct, inside the pool; entries past the context are
-    REGENERATE; every job admits a page the table now maps to its slot."""
+    REGENERATE; every job (sequence id, logical page, slot) admits a page the
+    table now maps to its slot in that sequence's batch row."""
     res = resident(pt)
     assert len(set(res.values())) == len(res) and all(0 <= s < slots for s in res.values())
     for b, L in enumerate(ctx):
         np_ = (L + P - 1) // P
         assert (pt[b, np_:] == atlas.ATLAS_PAGE_REGENERATE).all()
-    for b, lp, s in jobs:
-        assert pt[b, lp] == s
+    for sid, lp, s in jobs:
+        assert pt[list(ids).index(sid), lp] == s
 
 
 def test_budget_and_admission_order():
     c = cache(6, recent=32)
     ctx = [50, 20]                      # 4 + 2 pages
     pt, jobs = c.plan(0, [7, 9], ctx, 4)
-    check_contract(pt, jobs, ctx, 6)
-    # recent pages first (newest first per sequence), then the rest while slots last
-    assert [tuple(j[:2]) for j in jobs] == [(0, 3), (0, 2), (0, 1), (1, 1), (1, 0), (0, 0)]
+    check_contract(pt, jobs, ctx, 6, [7, 9])
+    # recent pages first (newest first per sequence), then the rest while slots
+    # last; jobs name the sequence by its id (its generator key)
+    assert [tuple(j[:2]) for j in jobs] == [(7, 3), (7, 2), (7, 1), (9, 1), (9, 0), (7, 0)]
     st = c.stats()
     assert st["resident_pages"] == 6 and st["resident_bytes"] == 6000 and st["admitted"] == 6
     # the same call again: all hits, nothing admitted
     pt2, jobs2 = c.plan(0, [7, 9], ctx, 4)
     assert len(jobs2) == 0 and np.array_equal(pt, pt2)
     assert c.stats()["hits"] == 6 and c.stats()["misses"] == 0
+    # the sequences swap batch rows: the same pages hit, in the other rows
+    pt3, jobs3 = c.plan(0, [9, 7], ctx[::-1], 4)
+    assert len(jobs3) == 0 and np.array_equal(pt3, pt[::-1])
 
 
 def test_no_admission_without_policy_leaves_pages_cold():
@@ -55,7 +60,7 @@ def test_no_admission_without_policy_leaves_pages_cold():
 def test_admit_regenerated_never_evicts():
     c = cache(2, recent=0, admit=True)
     pt, jobs = c.plan(0, [1], [64], 4)            # 4 pages, 2 slots: pages 0 and 1 admitted
-    assert [tuple(j[:2]) for j in jobs] == [(0, 0), (0, 1)]
+    assert [tuple(j[:2]) for j in jobs] == [(1, 0), (1, 1)]
     pt, jobs = c.plan(0, [2], [64], 4)            # another sequence: no free slot, no eviction
     assert len(jobs) == 0 and (pt == atlas.ATLAS_PAGE_REGENERATE).all()
     assert c.stats()["evicted"] == 0
@@ -101,6 +106,10 @@ def test_errors_change_nothing():
     with pytest.raises(atlas.AtlasError) as ei:
         c.plan(0, [1], [0], 2)
     assert ei.value.status == atlas.ATLAS_ERR_RANGE
+    for bad_id in (-1, 65536):                     # ids key the generator: 16 bits
+        with pytest.raises(atlas.AtlasError) as ei:
+            c.plan(0, [2, bad_id], [10, 10], 2)
+        assert ei.value.status == atlas.ATLAS_ERR_RANGE
     assert c.stats() == {"capacity_pages": 4, "resident_pages": 0, "resident_bytes": 0, "hits": 0, "misses": 0,
                          "admitted": 0, "evicted": 0}
     with pytest.raises(atlas.AtlasError) as ei:
@@ -119,7 +128,7 @@ def test_random_traffic_respects_the_budget():
             lens[s] += int(rng.integers(0, 3))
         ctx = [lens[s] for s in ids]
         pt, jobs = c.plan(int(rng.integers(0, 2)), ids, ctx, 16)
-        check_contract(pt, jobs, ctx, slots)
+        check_contract(pt, jobs, ctx, slots, ids)
         assert c.stats()["resident_pages"] <= slots
         if step % 17 == 16:
             c.drop_sequence(int(rng.integers(0, 6)))

@@ -35,12 +35,12 @@ PAGE_BYTES = HKV * P * D * 4 * 2
 SEED, LAYER = 11, 3
 
 
-def decode_all_cold(q, ctx):
+def decode_all_cold(q, ctx, keys):
     import exact_paged_causal_amd as atlas
     k = torch.zeros((1, HKV, P, D), device="cuda")
     pt = torch.full((B, MAXP), atlas.ATLAS_PAGE_REGENERATE, dtype=torch.int32, device="cuda")
     return atlas.atlas_attend_decode_regen(q, k, torch.zeros_like(k), pt, ctx, 1.0 / math.sqrt(D), seed=SEED,
-                                           layer=LAYER)
+                                           layer=LAYER, seq_keys=keys)
 
 
 @pytest.mark.parametrize("slots,recent,admit", [
@@ -52,19 +52,24 @@ def test_cached_decode_is_bit_identical(slots, recent, admit):
     cache = atlas.HotCache(slots * PAGE_BYTES, PAGE_BYTES, P, recent_tokens=recent, admit_regenerated=admit)
     k = torch.full((max(slots, 1), HKV, P, D), float("nan"), device="cuda")   # unwritten slots are never read
     v = torch.full_like(k, float("nan"))
-    lens = np.array([3000, 1500, 800], np.int32)
-    seq_ids = [101, 202, 303]
+    lens_of = {101: 3000, 202: 1500, 303: 800}
+    # the sequences change batch rows from step to step (a serving loop
+    # reorders its batch); a sequence's id is its generator key
+    orders = [[101, 202, 303], [303, 101, 202], [202, 303, 101], [101, 303, 202]]
     for step in range(4):
         if step == 2:
-            lens = lens + 70                      # the contexts grow into new pages
+            lens_of = {s: L + 70 for s, L in lens_of.items()}   # the contexts grow into new pages
+        seq_ids = orders[step]
+        lens = np.array([lens_of[s] for s in seq_ids], np.int32)
         ctx = torch.from_numpy(lens).cuda()
+        keys = torch.tensor(seq_ids, dtype=torch.int32, device="cuda")
         q = workloads.randn((B, 1, HQ, D), seed=500 + step, device="cuda")
-        ref_o, ref_l = decode_all_cold(q, ctx)
+        ref_o, ref_l = decode_all_cold(q, ctx, keys)
         pt, jobs = cache.plan(LAYER, seq_ids, lens, MAXP)
         if len(jobs):
             atlas.atlas_regenerate_pages(k, v, torch.from_numpy(jobs).cuda(), seed=SEED, layer=LAYER)
         out, lse = atlas.atlas_attend_decode_regen(q, k, v, torch.from_numpy(pt).cuda(), ctx, 1.0 / math.sqrt(D),
-                                                   seed=SEED, layer=LAYER)
+                                                   seed=SEED, layer=LAYER, seq_keys=keys)
         torch.cuda.synchronize()
         st = cache.stats()
         say(f"[cache] step {step}: {len(jobs)} admitted, stats {st}")
@@ -80,10 +85,11 @@ def test_reference_matches_oracle():
     workload's rows come from the oracle's own generator)."""
     w = workloads.Workload("cache_ref", seed=SEED, batch=B, hq=HQ, hkv=HKV, head_dim=D, page_size=P, dtype="f32",
                            q_len=1, context_lens=np.array([3000, 1500, 800], np.int32), scale=1.0 / math.sqrt(D),
-                           regenerated=True, hot_fraction=0.0, shuffle_pages=True)
+                           regenerated=True, hot_fraction=0.0, shuffle_pages=True,
+                           seq_keys=np.array([303, 101, 202], np.int32))
     w.layer = LAYER
     say("[cache] reference vs oracle")
     inp = H.build(w)
-    out, lse = decode_all_cold(inp.q, inp.context_lens)
+    out, lse = decode_all_cold(inp.q, inp.context_lens, H.seq_keys_tensor(w))
     torch.cuda.synchronize()
     H.check_against_oracle(inp, out, lse, what="all-cold reference")

@@ -1,8 +1,9 @@
 """GPU parity of atlas_attend_decode_regen: decode with the cold pages
 regenerated inside the attention kernel (page-table entries -1) instead of
-into scratch pages.  Checked against the fp64 oracle and, bit for bit,
-against regenerating the same pages into scratch and running
-atlas_attend_decode.
+into scratch pages, for fp32 and bf16 caches (the latter with bf16 or fp32
+queries) and for explicit per-sequence generator keys.  Checked against the
+fp64 oracle and, bit for bit, against regenerating the same pages into
+scratch and running atlas_attend_decode.
 
 Each test prints the case it runs before touching the GPU."""
 import math
@@ -42,15 +43,17 @@ def run_fused(inp, pt=None, **kw):
     w = inp.w
     return atlas.atlas_attend_decode_regen(inp.q, inp.k, inp.v, fused_table(inp) if pt is None else pt,
                                            inp.context_lens, w.scale, seed=w.seed, layer=w.layer,
+                                           seq_keys=H.seq_keys_tensor(w),
                                            window=inp.window, sink_tokens=inp.sinks, softcap=inp.softcap, **kw)
 
 
 def regen_workload(batch, lens, *, d=64, page=512, hq=32, hkv=8, hot=0.25, window=None, sinks=None,
-                   softcap=None, seed=3):
+                   softcap=None, seed=3, dtype="f32", q_dtype=None, seq_keys=None):
     return workloads.Workload(
-        "fused", seed=seed, batch=batch, hq=hq, hkv=hkv, head_dim=d, page_size=page, dtype="f32",
+        "fused", seed=seed, batch=batch, hq=hq, hkv=hkv, head_dim=d, page_size=page, dtype=dtype,
         q_len=1, context_lens=np.asarray(lens, np.int32), scale=1.0 / math.sqrt(d), regenerated=True,
-        hot_fraction=hot, shuffle_pages=True,
+        hot_fraction=hot, shuffle_pages=True, q_dtype=q_dtype,
+        seq_keys=None if seq_keys is None else np.asarray(seq_keys, np.int32),
         window=None if window is None else np.asarray(window, np.int32),
         sinks=None if sinks is None else np.asarray(sinks, np.int32),
         softcap=None if softcap is None else np.asarray(softcap, np.float32))
@@ -76,6 +79,48 @@ def test_fused_matches_oracle_and_scratch_path(case):
     H.check_against_oracle(inp, out_f, lse_f, what=f"fused {case}")
     say(f"[fused] scratch path {case}")
     out_s, lse_s = H.run(inp)          # regenerates the cold pages into scratch, then decodes
+    torch.cuda.synchronize()
+    assert torch.equal(out_f, out_s) and torch.equal(lse_f, lse_s)
+
+
+@pytest.mark.parametrize("case", [
+    # (dtype, q_dtype, batch, lens, d, page, hq, hkv, hot)
+    ("bf16", None, 3, (8192, 5000, 1), 128, 16, 16, 2, 0.25),
+    ("bf16", None, 2, (300, 77), 128, 1, 8, 2, 0.5),      # one key per page: hot and cold rows in one chunk
+    ("bf16", None, 2, (1000, 513), 64, 64, 8, 8, 0.3),
+    ("bf16", "f32", 2, (2000, 700), 128, 16, 8, 1, 0.25),  # fp32 query over a bf16 cache
+    ("bf16", None, 1, (4096,), 128, 512, 1, 1, 0.0),      # every page cold
+], ids=lambda c: f"{c[0]}-q{c[1] or c[0]}-b{c[2]}-d{c[4]}-p{c[5]}-h{c[6]}x{c[7]}-hot{c[8]}")
+def test_fused_bf16_matches_oracle_and_scratch_path(case):
+    """bf16 caches: the fold builds cold keys' rows from the generator (each
+    value rounded to bf16 as the regenerator stores it)."""
+    dtype, qdt, batch, lens, d, page, hq, hkv, hot = case
+    w = regen_workload(batch, lens, d=d, page=page, hq=hq, hkv=hkv, hot=hot, dtype=dtype, q_dtype=qdt)
+    say(f"[fused bf16] {case}")
+    inp = H.build(w, poison=True)
+    out_f, lse_f = run_fused(inp)
+    torch.cuda.synchronize()
+    assert not torch.isnan(out_f).any()
+    H.check_against_oracle(inp, out_f, lse_f, what=f"fused bf16 {case}")
+    say(f"[fused bf16] scratch path {case}")
+    out_s, lse_s = H.run(inp)
+    torch.cuda.synchronize()
+    assert torch.equal(out_f, out_s) and torch.equal(lse_f, lse_s)
+
+
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+def test_fused_with_sequence_keys(dtype):
+    """Explicit generator keys (one above 2^15, one 0): the cold pages come
+    from each sequence's key, not its batch row, in the kernel and in the
+    regenerator alike."""
+    w = regen_workload(3, (1500, 900, 2100), d=64 if dtype == "f32" else 128, hq=8, hkv=2, page=64, hot=0.4,
+                       dtype=dtype, seq_keys=(40000, 0, 7))
+    say(f"[fused] sequence keys {dtype}")
+    inp = H.build(w, poison=True)
+    out_f, lse_f = run_fused(inp)
+    torch.cuda.synchronize()
+    H.check_against_oracle(inp, out_f, lse_f, what=f"fused keys {dtype}")
+    out_s, lse_s = H.run(inp)
     torch.cuda.synchronize()
     assert torch.equal(out_f, out_s) and torch.equal(lse_f, lse_s)
 
@@ -119,6 +164,26 @@ def test_fused_all_cold_single_head_equals_resident():
     assert torch.equal(out_r, out_f) and torch.equal(lse_r, lse_f)
 
 
+def test_fused_bf16_mixed_decode_full_size():
+    """The mixed-length bf16 decode (64 sequences, windows / sinks / softcap
+    on the even ones) with K/V regenerated and 75 % of the pages generated in
+    the kernel: bit-identical to the scratch path, and against the oracle on
+    every sequence."""
+    w = workloads.make("mixed_decode", regenerated=True, hot_fraction=0.25)
+    say("[fused] mixed_decode full size, bf16, regenerated")
+    inp = H.build(w)
+    out_f, lse_f = run_fused(inp)
+    out_f, lse_f = out_f.clone(), lse_f.clone()
+    out_s, lse_s = H.run(inp)
+    torch.cuda.synchronize()
+    assert torch.equal(out_f, out_s) and torch.equal(lse_f, lse_s)
+    # the oracle regenerates every row it reads on the CPU: the two shortest
+    # windowed (even) and plain (odd) sequences
+    order = np.argsort(w.context_lens, kind="stable")
+    seqs = [int(b) for b in order if b % 2 == 0][:2] + [int(b) for b in order if b % 2 == 1][:2]
+    H.check_against_oracle(inp, out_f, lse_f, seqs=seqs, what="fused mixed_decode")
+
+
 def test_fused_validation_mode(monkeypatch):
     import exact_paged_causal_amd as atlas
     monkeypatch.setenv("ATLAS_VALIDATE", "1")
@@ -134,3 +199,9 @@ def test_fused_validation_mode(monkeypatch):
     with pytest.raises(atlas.AtlasError) as ei:
         run_fused(inp, pt=pt)
     assert ei.value.status == atlas.ATLAS_ERR_POOL
+    say("[fused] validation mode rejects a sequence key of 65536")
+    keys = torch.tensor([3, 65536], dtype=torch.int32, device="cuda")
+    with pytest.raises(atlas.AtlasError) as ei:
+        atlas.atlas_attend_decode_regen(inp.q, inp.k, inp.v, fused_table(inp), inp.context_lens, w.scale,
+                                        seed=w.seed, layer=w.layer, seq_keys=keys)
+    assert ei.value.status == atlas.ATLAS_ERR_RANGE

@@ -69,16 +69,19 @@ def run_mods(inp, causal, slopes, mask):
         window=inp.window, sink_tokens=inp.sinks, softcap=inp.softcap)
 
 
-def check_mods(inp, out, lse, causal, slopes, mask, what, rows=None):
+def check_mods(inp, out, lse, causal, slopes, mask, what, rows=None, heads=None):
     w = inp.w
     src = H.OracleSource(inp)
     out_h, lse_h = H.to_f32_numpy(out), H.to_f32_numpy(lse)
-    hm = oracle.default_head_map(w.hq, w.hkv)
+    hsel = np.arange(w.hq) if heads is None else np.asarray(heads)
+    hm = oracle.default_head_map(w.hq, w.hkv)[hsel]
+    if slopes is not None:
+        slopes = slopes[hsel]
     for b in range(w.batch):
         k, v = src.kv(b)
         L = int(w.context_lens[b])
         sel = np.arange(w.q_len) if rows is None else np.asarray(rows)
-        q = H.to_f32_numpy(inp.q[b])[sel]
+        q = np.ascontiguousarray(H.to_f32_numpy(inp.q[b])[sel][:, hsel])
         pos = (L - w.q_len + np.arange(w.q_len))[sel].astype(np.int32)
         win = int(w.window[b]) if w.window is not None else 0
         snk = int(w.sinks[b]) if (w.sinks is not None and win > 0) else 0
@@ -86,7 +89,7 @@ def check_mods(inp, out, lse, causal, slopes, mask, what, rows=None):
         ro, rl = oracle.attend(q, k, v, pos, hm, w.scale, win, snk, cap, causal=causal,
                                alibi=None if slopes is None else slopes.astype(np.float64),
                                mask=None if mask is None else mask[b][sel][:, :L], allow_empty=True)
-        got_o, got_l = out_h[b][sel], lse_h[b][sel]
+        got_o, got_l = out_h[b][sel][:, hsel], lse_h[b][sel][:, hsel]
         empty = np.isneginf(rl)
         assert np.isnan(got_o[empty]).all() and np.isneginf(got_l[empty]).all(), f"{what}: empty rows"
         H.assert_close(got_o[~empty], ro[~empty], w.dtype, f"{what} out[b={b}]")
@@ -177,17 +180,19 @@ def test_no_op_mods_equal_the_plain_call(dtype, q_len):
 
 
 @pytest.mark.parametrize("causal", [True, False])
-def test_mods_causal_prefill_full_size_sampled(causal):
+def test_mods_causal_prefill_full_size(causal):
     """The causal-prefill shape (S=8192, Hq=32, Hkv=8, D=128, bf16) with ALiBi
-    slopes, causal and non-causal: every head of a sample of rows."""
+    slopes, causal and non-causal: every row of one seeded q-head per K/V
+    head, and the first and last 512 rows of every q-head."""
     w = workloads.make("causal_prefill")
     say(f"[mods] causal_prefill shape with ALiBi, causal={causal}")
     inp = H.build(w)
     slopes = alibi_slopes(w.hq)
     out, lse = run_mods(inp, causal, slopes, None)
     torch.cuda.synchronize()
-    rows = [0, 1, 63, 64, 4095, 4096, 8190, 8191]
-    check_mods(inp, out, lse, causal, slopes, None, f"full size causal={causal}", rows=rows)
+    for rows, heads in H.full_size_blocks(w, seed=2):
+        say(f"[mods] oracle on {len(rows)} rows x heads {heads.tolist()}")
+        check_mods(inp, out, lse, causal, slopes, None, f"full size causal={causal}", rows=rows, heads=heads)
     assert not torch.isnan(out).any()
 
 

@@ -97,20 +97,55 @@ def test_tiled_prefill_uneven_head_map():
     H.check_against_oracle(inp, out, lse, head_map=hm, what="uneven head map")
 
 
-def test_causal_prefill_full_size_sampled():
+def test_causal_prefill_full_size():
     """S=8192, Hq=32, Hkv=8, D=128, pages of 128 in random physical order:
-    every head of a sample of rows (block edges, the first and last rows)."""
+    every row of one seeded q-head per K/V head, and the first and last 512
+    rows of every q-head, against the oracle; no NaN anywhere."""
     w = workloads.make("causal_prefill")
     say("[causal_prefill] full size")
     inp = H.build(w)
     out, lse = H.run(inp)
     torch.cuda.synchronize()
-    rng = np.random.default_rng(0)
-    rows = sorted(set([0, 1, 2, 31, 32, 63, 64, 65, 127, 128, 255, 256, 257, 4095, 4096, 8127, 8128,
-                       8190, 8191] + rng.integers(0, 8192, size=12).tolist()))
-    say(f"[causal_prefill] oracle on {len(rows)} rows x 32 heads")
-    H.check_against_oracle(inp, out, lse, rows=rows, what="causal_prefill")
+    for rows, heads in H.full_size_blocks(w, seed=0):
+        say(f"[causal_prefill] oracle on {len(rows)} rows x heads {heads.tolist()}")
+        H.check_against_oracle(inp, out, lse, rows=rows, heads=heads, what="causal_prefill")
     assert not torch.isnan(out).any() and not torch.isnan(lse).any()
+
+
+def restage_workload(dtype, hkv=8, ctx=33000, q_len=64, window=None, sinks=None, softcap=None, seed=25):
+    """32 sequences x hkv K/V heads, pages of 16, q_len positions each: 256
+    workgroups fill the chip, so no key splits; each workgroup's key range
+    spans more pages than its page-id window holds (2048 pages for bf16,
+    1024 for fp32), so the window is restaged inside the key loop."""
+    B = 256 // hkv
+    lens = np.full(B, ctx, np.int32)
+    lens[1::2] -= 333                       # ragged last pages
+    w = workloads.Workload("restage", seed=seed, batch=B, hq=hkv, hkv=hkv, head_dim=128, page_size=16,
+                           dtype=dtype, q_len=q_len, context_lens=lens, scale=1.0 / math.sqrt(128),
+                           shuffle_pages=True)
+    if window is not None:
+        w.window, w.sinks, w.softcap = (np.asarray(x, np.int32 if i < 2 else np.float32)
+                                        for i, x in enumerate((window, sinks, softcap)))
+    return w
+
+
+def test_tiled_prefill_restages_page_ids():
+    """bf16 tiled prefill whose workgroups each read 33000 keys in pages of
+    16 (2063 pages, above the 2048-entry page-id window), and windowed rows
+    (window 100 + 4 sinks) whose first window block sits more than 2048
+    pages after the sink page: both restage the window.  Two sequences of
+    each kind against the oracle."""
+    B = 32
+    win = np.where(np.arange(B) % 4 == 0, 100, 0)
+    snk = np.where(np.arange(B) % 4 == 0, 4, 0)
+    cap = np.zeros(B, np.float32)
+    w = restage_workload("bf16", window=win, sinks=snk, softcap=cap)
+    say("[prefill-tiled] page-id window restage (33000 keys in pages of 16)")
+    inp = H.build(w)
+    out, lse = H.run(inp, entry="prefill")
+    torch.cuda.synchronize()
+    H.check_against_oracle(inp, out, lse, seqs=[0, 4, 1, 3], what="restage")
+    assert not torch.isnan(out).any()
 
 
 def test_tiled_prefill_poison_and_determinism():

@@ -132,19 +132,40 @@ def test_f32_tiled_prefill_poison_determinism_and_page_order():
     H.check_against_oracle(clean, o1, l1, what="poison reference")
 
 
-def test_f32_causal_prefill_full_size_sampled():
+def test_f32_causal_prefill_full_size():
     """The causal-prefill shape in fp32 (S=8192, Hq=32, Hkv=8, D=128, pages
-    of 128 in random physical order): every head of a sample of rows."""
+    of 128 in random physical order): every row of one seeded q-head per K/V
+    head, and the first and last 512 rows of every q-head."""
     w = workloads.make("causal_prefill", dtype="f32")
     say("[prefill-f32] causal_prefill shape, fp32")
     inp = H.build(w)
     out, lse = H.run(inp)
     torch.cuda.synchronize()
-    rng = np.random.default_rng(1)
-    rows = sorted(set([0, 1, 63, 64, 255, 256, 4095, 4096, 8191] + rng.integers(0, 8192, size=8).tolist()))
-    say(f"[prefill-f32] oracle on {len(rows)} rows x 32 heads")
-    H.check_against_oracle(inp, out, lse, rows=rows, what="causal_prefill f32")
+    for rows, heads in H.full_size_blocks(w, seed=1):
+        say(f"[prefill-f32] oracle on {len(rows)} rows x heads {heads.tolist()}")
+        H.check_against_oracle(inp, out, lse, rows=rows, heads=heads, what="causal_prefill f32")
     assert not torch.isnan(out).any() and not torch.isnan(lse).any()
+
+
+def test_f32_tiled_prefill_restages_page_ids():
+    """fp32 tiled prefill over 17000 keys in pages of 16 per workgroup (1063
+    pages, above its 1024-entry page-id window), unsplit (256 workgroups),
+    with windowed rows whose window starts past page 1024 of their sinks."""
+    B = 32
+    lens = np.full(B, 17000, np.int32)
+    lens[1::2] -= 333
+    w = workloads.Workload("restage_f32", seed=35, batch=B, hq=8, hkv=8, head_dim=128, page_size=16,
+                           dtype="f32", q_len=64, context_lens=lens, scale=1.0 / math.sqrt(128),
+                           shuffle_pages=True)
+    w.window = np.where(np.arange(B) % 4 == 0, 300, 0).astype(np.int32)
+    w.sinks = np.where(np.arange(B) % 4 == 0, 4, 0).astype(np.int32)
+    w.softcap = np.zeros(B, np.float32)
+    say("[prefill-f32] page-id window restage (17000 keys in pages of 16)")
+    inp = H.build(w)
+    out, lse = H.run(inp, entry="prefill")
+    torch.cuda.synchronize()
+    H.check_against_oracle(inp, out, lse, seqs=[0, 4, 1, 3], what="restage f32")
+    assert not torch.isnan(out).any()
 
 
 @pytest.mark.parametrize("which", ["q", "k", "v"])

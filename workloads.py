@@ -45,7 +45,7 @@ class Workload:
     hkv: int
     head_dim: int
     page_size: int
-    dtype: str                     # "f32" or "bf16" (Q and K/V)
+    dtype: str                     # "f32" or "bf16" (K/V, and Q unless q_dtype says otherwise)
     q_len: int                     # 1 for decode
     context_lens: np.ndarray       # [B] int32
     scale: float
@@ -56,7 +56,16 @@ class Workload:
     sinks: np.ndarray | None = None      # [B] int32
     softcap: np.ndarray | None = None    # [B] float32, 0 = off
     layer: int = 0
+    q_dtype: str | None = None           # Q's dtype when it differs from the K/V dtype
+    seq_keys: np.ndarray | None = None   # [B] generator keys of regenerated sequences (None: the batch row)
     extra: dict = field(default_factory=dict)
+
+    @property
+    def qdt(self) -> str:
+        return self.q_dtype or self.dtype
+
+    def seq_key(self, b: int) -> int:
+        return int(b if self.seq_keys is None else self.seq_keys[b])
 
     @property
     def group(self) -> int:
@@ -112,12 +121,22 @@ class PageLayout:
     (entries past a sequence's last page are 0 and never read).  For
     regenerated workloads ids [0, n_hot) form the resident pool and ids
     [n_hot, n_hot + n_cold) the scratch region; `cold_jobs` lists
-    (seq, logical_page, phys_page) for every cold page and `hot_jobs` the same
-    for resident pages (filled once, before any timed call)."""
+    (batch row, logical_page, phys_page) for every cold page and `hot_jobs`
+    the same for resident pages (filled once, before any timed call);
+    `key_jobs` turns such a list into regeneration jobs, whose first column is
+    the sequence's generator key."""
     page_table: np.ndarray          # [B][max_pages] int32
     num_phys: int
     hot_jobs: np.ndarray            # [n][3] int32
     cold_jobs: np.ndarray           # [n][3] int32
+
+
+def key_jobs(w: Workload, jobs: np.ndarray) -> np.ndarray:
+    """(batch row, logical page, phys page) -> (generator key, logical page, phys page)."""
+    out = np.array(jobs, np.int32).reshape(-1, 3).copy()
+    if w.seq_keys is not None and len(out):
+        out[:, 0] = np.asarray(w.seq_keys, np.int32)[out[:, 0]]
+    return out
 
 
 def page_layout(w: Workload, hot_fraction: float | None = None, seed_offset: int = 0,
