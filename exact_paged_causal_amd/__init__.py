@@ -9,7 +9,8 @@ from .atlas import (  # noqa: F401
     ATLAS_OK, ATLAS_PAGE_REGENERATE, AppendArgs, AtlasError, AttnArgs, AttnMods, CacheConfig, CacheStats, HotCache,
     PagePool, RegenArgs,
     atlas_abi_version, atlas_append_kv, atlas_attend_mods,
-    atlas_attend_decode, atlas_attend_decode_regen, atlas_attend_prefill, atlas_decode_workspace_bytes,
+    atlas_attend_decode, atlas_attend_decode_noalloc, atlas_attend_decode_regen, atlas_attend_prefill,
+    atlas_decode_workspace_bytes,
     atlas_last_error,
     atlas_prefill_workspace_bytes, atlas_regenerate_pages, atlas_status_str, make_attn_args,
 )

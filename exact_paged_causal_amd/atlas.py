@@ -138,7 +138,7 @@ class CacheStats(ctypes.Structure):
 EXPORTS = ("atlas_abi_version", "atlas_status_str", "atlas_last_error",
            "atlas_decode_workspace_bytes", "atlas_prefill_workspace_bytes",
            "atlas_attend_decode", "atlas_attend_prefill", "atlas_attend_mods", "atlas_regenerate_pages",
-           "atlas_attend_decode_regen", "atlas_append_kv", "atlas_pool_create", "atlas_pool_destroy",
+           "atlas_attend_decode_regen", "atlas_attend_decode_noalloc", "atlas_append_kv", "atlas_pool_create", "atlas_pool_destroy",
            "atlas_pool_alloc", "atlas_pool_retain", "atlas_pool_release", "atlas_pool_free_pages",
            "atlas_pool_refcount", "atlas_cache_create", "atlas_cache_destroy", "atlas_cache_plan",
            "atlas_cache_drop_sequence", "atlas_cache_get_stats")
@@ -170,6 +170,8 @@ def _load():
     lib.atlas_attend_decode_regen.restype = ctypes.c_int32
     lib.atlas_attend_decode_regen.argtypes = [ctypes.POINTER(AttnArgs), ctypes.c_uint64, ctypes.c_int32,
                                               ctypes.c_void_p, ctypes.c_void_p]
+    lib.atlas_attend_decode_noalloc.restype = ctypes.c_int32
+    lib.atlas_attend_decode_noalloc.argtypes = [ctypes.POINTER(AttnArgs), ctypes.c_void_p]
     lib.atlas_append_kv.restype = ctypes.c_int32
     lib.atlas_append_kv.argtypes = [ctypes.POINTER(AppendArgs), ctypes.c_void_p]
     lib.atlas_pool_create.restype = ctypes.c_int32
@@ -392,6 +394,24 @@ def atlas_attend_decode_regen(q, k_pages, v_pages, page_table, context_lens, sca
                           _ptr(seq_keys)),
                    head_map=head_map, window=window, sink_tokens=sink_tokens, softcap=softcap,
                    split_tokens=split_tokens, want_lse=want_lse)
+
+
+NOALLOC_SCRATCH_BYTES = 32 << 20   # ATLAS_NOALLOC_SCRATCH_BYTES
+
+
+def atlas_attend_decode_noalloc(q, k_pages, v_pages, page_table, context_lens, scale, *, out, lse=None,
+                                head_map=None, window=None, sink_tokens=None, softcap=None, split_tokens=0,
+                                stream=None):
+    """atlas_attend_decode whose partial states live in the library's own device array: the
+    caller passes the outputs (out [B][1][Hq][D] f32, optionally lse [B][1][Hq] f32) and
+    nothing is allocated.  Calls overlapping on one GPU race (one shared array per GPU)."""
+    args, keep = make_attn_args(q, k_pages, v_pages, page_table, context_lens, scale, head_map=head_map,
+                                window=window, sink_tokens=sink_tokens, softcap=softcap, out=out, lse=lse,
+                                split_tokens=split_tokens)
+    st = lib.atlas_attend_decode_noalloc(ctypes.byref(args), _stream(stream))
+    if st != ATLAS_OK:
+        raise AtlasError(st, "atlas_attend_decode_noalloc")
+    return out, lse
 
 
 def atlas_attend_prefill(q, k_pages, v_pages, page_table, context_lens, scale, *, head_map=None,

@@ -149,7 +149,7 @@ int32_t check_shapes(const atlas_attn_args *a, bool decode, Plan *p)
 
     // Head groups.
     const int hq = a->num_q_heads, hkv = a->num_kv_heads;
-    std::vector<int> map(hq);
+    int map[atlas::kMaxHeads];  // no host allocation on the call path
     if (a->head_map) {
         for (int h = 0; h < hq; ++h) {
             if (a->head_map[h] < 0 || a->head_map[h] >= hkv)

@@ -265,6 +265,27 @@ typedef struct atlas_attn_mods {
  */
 int32_t atlas_attend_mods(const atlas_attn_args *args, const atlas_attn_mods *mods, void *stream);
 
+/*
+ * For callers that cannot allocate device memory: code under HIP graph
+ * capture, tight serving loops, harnesses that forbid hipMalloc.  The same
+ * decode as atlas_attend_decode (same kernels, same results to the bit), but
+ * the split partial states live in a device array inside the library instead
+ * of a caller workspace: args->workspace and args->workspace_bytes are
+ * ignored, the caller passes only inputs and outputs, and the call allocates
+ * nothing (no hipMalloc, no host allocation).  The array holds
+ * ATLAS_NOALLOC_SCRATCH_BYTES (32 MiB) on each GPU the library runs on, from
+ * the first call on that GPU until the process ends; a decode whose partial
+ * states need more (atlas_decode_workspace_bytes() above that) returns
+ * ATLAS_ERR_WORKSPACE before anything runs.  Calls on the current device's
+ * streams only (ATLAS_ERR_DEVICE for a stream of another device).  Every
+ * call on one GPU uses the same array: calls that overlap in time on one GPU
+ * (several streams, several threads) race and must be serialised by the
+ * caller.  Validation mode (ATLAS_VALIDATE=1) is not available here
+ * (ATLAS_ERR_UNSUPPORTED): it copies device arrays to host buffers.
+ */
+#define ATLAS_NOALLOC_SCRATCH_BYTES ((size_t)32 << 20)
+int32_t atlas_attend_decode_noalloc(const atlas_attn_args *args, void *stream);
+
 /* Regenerate whole pages (all heads, all P tokens) into the arenas. */
 int32_t atlas_regenerate_pages(const atlas_regen_args *args, void *stream);
 

@@ -24,7 +24,8 @@ def test_header_declares_the_boundary():
     assert names == sorted(["atlas_abi_version", "atlas_status_str", "atlas_last_error",
                             "atlas_decode_workspace_bytes", "atlas_prefill_workspace_bytes",
                             "atlas_attend_decode", "atlas_attend_prefill", "atlas_attend_mods",
-                            "atlas_regenerate_pages", "atlas_attend_decode_regen", "atlas_append_kv",
+                            "atlas_regenerate_pages", "atlas_attend_decode_regen",
+                            "atlas_attend_decode_noalloc", "atlas_append_kv",
                             "atlas_pool_create", "atlas_pool_destroy", "atlas_pool_alloc",
                             "atlas_pool_retain", "atlas_pool_release", "atlas_pool_free_pages",
                             "atlas_pool_refcount", "atlas_cache_create", "atlas_cache_destroy",
@@ -165,6 +166,25 @@ def test_decode_regen_rejects_bad_arguments_before_launch():
     assert fn(ctypes.byref(_valid_args(workspace_bytes=16)), 7, 0, FAKE, None) == A.ATLAS_ERR_WORKSPACE
     assert A.ATLAS_PAGE_REGENERATE == -1
     assert "#define ATLAS_PAGE_REGENERATE (-1)" in open(HEADER).read()
+
+
+def test_noalloc_decode_rejects_before_touching_the_gpu():
+    """The allocation-free decode checks sizes on the host first: bad shapes
+    report the decode's own status; partial states beyond the library's
+    32 MiB array are ATLAS_ERR_WORKSPACE, whatever workspace is passed."""
+    from exact_paged_causal_amd import atlas as A
+    fn = A.lib.atlas_attend_decode_noalloc
+    assert fn(None, None) == A.ATLAS_ERR_NULL
+    assert fn(ctypes.byref(_valid_args(head_dim=96)), None) == A.ATLAS_ERR_UNSUPPORTED
+    assert fn(ctypes.byref(_valid_args(q_len=2)), None) == A.ATLAS_ERR_SHAPE
+    # 64 x 64 rows x 16 spans of 4096 keys x 130 floats = 34 MiB > 32 MiB
+    big = _valid_args(batch=64, num_q_heads=64, num_kv_heads=8, head_dim=128, page_size=4096,
+                      max_pages_per_seq=16, split_tokens=4096)
+    need = A.lib.atlas_decode_workspace_bytes(ctypes.byref(big))
+    assert need > A.NOALLOC_SCRATCH_BYTES
+    assert fn(ctypes.byref(big), None) == A.ATLAS_ERR_WORKSPACE
+    assert "32" in A.atlas_last_error() or str(A.NOALLOC_SCRATCH_BYTES) in A.atlas_last_error()
+    assert "#define ATLAS_NOALLOC_SCRATCH_BYTES ((size_t)32 << 20)" in open(HEADER).read()
 
 
 def test_mods_reject_bad_arguments_before_launch():
