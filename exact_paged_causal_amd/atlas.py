@@ -193,7 +193,7 @@ def _load():
     i32p, i64p = ctypes.POINTER(ctypes.c_int32), ctypes.POINTER(ctypes.c_int64)
     lib.atlas_cache_plan.restype = ctypes.c_int32
     lib.atlas_cache_plan.argtypes = [ctypes.c_void_p, ctypes.c_int32, ctypes.c_int32, i64p, i32p, ctypes.c_int32,
-                                     i32p, i32p, ctypes.c_int32, i32p]
+                                     i32p, i32p, ctypes.c_int32, i32p, i32p]
     lib.atlas_cache_drop_sequence.restype = ctypes.c_int32
     lib.atlas_cache_drop_sequence.argtypes = [ctypes.c_void_p, ctypes.c_int64]
     lib.atlas_cache_get_stats.restype = ctypes.c_int32
@@ -572,6 +572,7 @@ class HotCache:
     in the kernel (ATLAS_PAGE_REGENERATE)."""
 
     _h = None
+    last_cold = 0   # pages the last plan left to in-kernel regeneration (0: plain decode gives the same bits)
 
     def __init__(self, hot_cache_bytes: int, page_bytes: int, page_size: int, recent_tokens: int = 0,
                  admit_regenerated: bool = True):
@@ -603,12 +604,14 @@ class HotCache:
         max_jobs = B * int(max_pages_per_seq)  # >= the pages of the call
         jobs = np.empty((max_jobs, 3), dtype=np.int32)
         n = ctypes.c_int32()
+        n_cold = ctypes.c_int32()
         i32p, i64p = ctypes.POINTER(ctypes.c_int32), ctypes.POINTER(ctypes.c_int64)
         st = lib.atlas_cache_plan(self._h, int(layer), B, ids.ctypes.data_as(i64p), ctx.ctypes.data_as(i32p),
                                   int(max_pages_per_seq), pt.ctypes.data_as(i32p), jobs.ctypes.data_as(i32p),
-                                  max_jobs, ctypes.byref(n))
+                                  max_jobs, ctypes.byref(n), ctypes.byref(n_cold))
         if st != ATLAS_OK:
             raise AtlasError(st, "atlas_cache_plan")
+        self.last_cold = int(n_cold.value)
         return pt, jobs[:n.value].copy()
 
     def drop_sequence(self, seq_id: int):

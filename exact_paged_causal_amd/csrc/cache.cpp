@@ -108,7 +108,7 @@ void atlas_cache_destroy(atlas_cache *c) { delete c; }
 
 int32_t atlas_cache_plan(atlas_cache *c, int32_t layer, int32_t batch, const int64_t *seq_ids,
                          const int32_t *context_lens, int32_t max_pages_per_seq, int32_t *page_table,
-                         int32_t *admit_jobs, int32_t max_jobs, int32_t *n_jobs)
+                         int32_t *admit_jobs, int32_t max_jobs, int32_t *n_jobs, int32_t *n_cold)
 {
     if (!c || !seq_ids || !context_lens || !page_table || !n_jobs || (max_jobs > 0 && !admit_jobs))
         return fail(ATLAS_ERR_NULL, "cache, seq_ids, context_lens, page_table and n_jobs are required");
@@ -229,6 +229,8 @@ int32_t atlas_cache_plan(atlas_cache *c, int32_t layer, int32_t batch, const int
         }
     }
     *n_jobs = jobs;
+    if (n_cold)
+        *n_cold = (int32_t)misses;
     c->stats.hits += hits;
     c->stats.misses += misses;
     c->stats.admitted += jobs;

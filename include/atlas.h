@@ -442,10 +442,15 @@ void atlas_cache_destroy(atlas_cache *cache);
  * sequence may occupy a different batch row in every call: its resident pages
  * and its regenerated ones come from the same key.
  * max_jobs must be >= min(pages in the call, capacity) (ATLAS_ERR_SHAPE).
+ * n_cold (may be NULL) receives the number of the call's pages left to
+ * in-kernel regeneration; when it is 0 every page is resident, and
+ * atlas_attend_decode over this page table returns the same bits as
+ * atlas_attend_decode_regen without running the generator instances (their
+ * placeholder loads and ordinary caching included).
  */
 int32_t atlas_cache_plan(atlas_cache *cache, int32_t layer, int32_t batch, const int64_t *seq_ids,
                          const int32_t *context_lens, int32_t max_pages_per_seq, int32_t *page_table,
-                         int32_t *admit_jobs, int32_t max_jobs, int32_t *n_jobs);
+                         int32_t *admit_jobs, int32_t max_jobs, int32_t *n_jobs, int32_t *n_cold);
 
 /* Free every resident page of a sequence (all layers), e.g. when it ends. */
 int32_t atlas_cache_drop_sequence(atlas_cache *cache, int64_t seq_id);

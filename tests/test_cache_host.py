@@ -42,6 +42,7 @@ def test_budget_and_admission_order():
     st = c.stats()
     assert st["resident_pages"] == 6 and st["resident_bytes"] == 6000 and st["admitted"] == 6
     # the same call again: all hits, nothing admitted
+    assert c.last_cold == 0                       # every page of the call admitted
     pt2, jobs2 = c.plan(0, [7, 9], ctx, 4)
     assert len(jobs2) == 0 and np.array_equal(pt, pt2)
     assert c.stats()["hits"] == 6 and c.stats()["misses"] == 0
@@ -54,6 +55,7 @@ def test_no_admission_without_policy_leaves_pages_cold():
     c = cache(4, recent=0, admit=False)
     pt, jobs = c.plan(0, [1], [40], 3)
     assert len(jobs) == 0 and (pt == atlas.ATLAS_PAGE_REGENERATE).all()
+    assert c.last_cold == 3
     assert c.stats()["misses"] == 3 and c.stats()["resident_pages"] == 0
 
 

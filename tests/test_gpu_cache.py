@@ -75,6 +75,11 @@ def test_cached_decode_is_bit_identical(slots, recent, admit):
         say(f"[cache] step {step}: {len(jobs)} admitted, stats {st}")
         assert st["resident_pages"] <= slots
         assert torch.equal(out, ref_o) and torch.equal(lse, ref_l), f"step {step}"
+        if cache.last_cold == 0:
+            # every page resident: the plain decode over the same table gives the same bits
+            o2, l2 = atlas.atlas_attend_decode(q, k, v, torch.from_numpy(pt).cuda(), ctx, 1.0 / math.sqrt(D))
+            torch.cuda.synchronize()
+            assert torch.equal(o2, ref_o) and torch.equal(l2, ref_l), f"plain decode, step {step}"
     if slots >= 400:
         assert st["misses"] == 0 or step < 1
         assert st["hits"] > 0
