@@ -32,6 +32,12 @@ under "next": "hot_cache"; short prefill chunks behind a 32768-token history
 A plain 256 MiB device-to-device copy is timed last as context for the HBM
 figures ("hbm_context"); the small workloads also report one C-ABI call
 with prepared arguments ("c_abi_us") beside the Python-call time.
+"provenance" names the GPU, its shader clock as rocm-smi reads it right
+after the timed steps, the host CPU model and thread count, the ROCm, HIP and
+torch versions and the git commit.  The fp64 CPU oracle is timed on the
+host's cores as a baseline (not a target): on the whole decode workload in
+GB/s ("cpu_baseline") and on a bounded sample of the prefill in GFLOP/s
+("prefill": "cpu_baseline"), each also checking the GPU output it covers.
 
 Prints one JSON line.  `--gpus N` with N > 1 exits: this path runs on one GPU.
 """
@@ -41,6 +47,8 @@ import argparse
 import json
 import math
 import os
+import re
+import subprocess
 import sys
 import time
 
@@ -537,10 +545,126 @@ def cpu_baseline(d, out, np, oracle, min_seconds=3.0):
                 max_err = max(max_err, float(err.max()))
         passes += 1
     return {"value": round(passes * bytes_per_pass / secs / 1e9, 3), "unit": "GB/s",
-            "cores": oracle.num_threads(), "kind": "oracle",
+            "cores": oracle.num_threads(), "cpu_model": _cpu_model(), "kind": "oracle",
             "sample": f"whole decode workload (8 seqs x 32 q-heads x 65536 keys, "
                       f"{bytes_per_pass / 1e9:.2f} GB fp32 K/V) x {passes} passes, {secs:.2f} s timed; "
                       f"K/V generation untimed; GPU outputs agreed (max abs err {max_err:.2e})"}
+
+
+def _cpu_model():
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return None
+
+
+def _git_commit():
+    try:
+        r = subprocess.run(["git", "-C", os.path.dirname(os.path.abspath(__file__)), "rev-parse", "HEAD"],
+                           capture_output=True, text=True, timeout=10)
+        return r.stdout.strip() or None
+    except (OSError, subprocess.SubprocessError):
+        return None
+
+
+def _rocm_version():
+    for path in ("/opt/rocm/.info/version",):
+        try:
+            with open(path) as f:
+                return f.read().strip()
+        except OSError:
+            pass
+    return None
+
+
+def gpu_sclk_mhz():
+    """Current shader clock of GPU 0 as rocm-smi reports it (None if unavailable)."""
+    try:
+        r = subprocess.run(["rocm-smi", "-d", "0", "--showclocks", "--json"], capture_output=True, text=True,
+                           timeout=20)
+        data = json.loads(r.stdout)
+    except (OSError, subprocess.SubprocessError, ValueError):
+        return None
+    for card in data.values():
+        if isinstance(card, dict):
+            for key, val in card.items():
+                if "sclk" in key.lower():
+                    m = re.search(r"(\d+)\s*Mhz", str(val), re.I)
+                    if m:
+                        return int(m.group(1))
+    return None
+
+
+def _library_build():
+    """The library's build record (git commit and source hash at build time),
+    and whether the sources here still hash the same."""
+    here = os.path.dirname(os.path.abspath(__file__))
+    try:
+        with open(os.path.join(here, "exact_paged_causal_amd", "build_info.json")) as f:
+            info = json.load(f)
+    except (OSError, ValueError):
+        return None
+    import importlib.util
+    spec = importlib.util.spec_from_file_location("_atlas_build", os.path.join(here, "exact_paged_causal_amd",
+                                                                              "build.py"))
+    mod = importlib.util.module_from_spec(spec)
+    spec.loader.exec_module(mod)
+    info["sources_unchanged_since_build"] = info.get("sources_sha256") == mod.sources_sha256()
+    info.pop("hipcc_flags", None)
+    return info
+
+
+def provenance(torch):
+    """Where the numbers come from (CPUAttn README, "Benchmark suite": reports
+    carry their environment)."""
+    prop = torch.cuda.get_device_properties(0)
+    return {"gpu": getattr(prop, "gcnArchName", None) or torch.cuda.get_device_name(0),
+            "gpu_name": torch.cuda.get_device_name(0), "cu_count": prop.multi_processor_count,
+            "gpu_sclk_mhz_after_timing": gpu_sclk_mhz(), "cpu_model": _cpu_model(),
+            "host_threads": os.cpu_count(), "rocm": _rocm_version(), "hip_runtime": torch.version.hip,
+            "torch": torch.__version__, "git_commit": _git_commit(), "library_build": _library_build()}
+
+
+def prefill_cpu_baseline(p, out, np, oracle, heads_per_kv=1, edge=512):
+    """Time the oracle (fp64 two-pass, OpenMP) on a bounded sample of the
+    8192-token causal prefill: every row of one q-head per K/V head (8 of the
+    32) plus the first and last `edge` rows of every q-head, in GFLOP/s over
+    that sample's visible pairs (4 D flop per pair, as for the GPU figure).
+    The GPU output is checked against the oracle's on the same rows."""
+    w = p["w"]
+    S, D = w.q_len, w.head_dim
+    P = w.page_size
+    n_pages = S // P
+    kl = p["kl"].float().cpu().numpy()[:n_pages]       # logical pages [n][Hkv][P][D]
+    vl = p["vl"].float().cpu().numpy()[:n_pages]
+    k = np.ascontiguousarray(kl.transpose(1, 0, 2, 3).reshape(w.hkv, S, D))
+    v = np.ascontiguousarray(vl.transpose(1, 0, 2, 3).reshape(w.hkv, S, D))
+    q = p["q"][0].float().cpu().numpy()                  # [S][Hq][D]
+    o = out[0]
+    hm = oracle.default_head_map(w.hq, w.hkv)
+    heads = np.array([g * (w.hq // w.hkv) for g in range(w.hkv)])
+    ends = np.array(sorted(set(range(edge)) | set(range(S - edge, S))))
+    blocks = [(np.arange(S), heads), (ends, np.arange(w.hq))]
+    flop, secs, max_err = 0.0, 0.0, 0.0
+    for rows, hs in blocks:
+        qq = np.ascontiguousarray(q[rows][:, hs])
+        t0 = time.perf_counter()
+        ro, _ = oracle.attend(qq, k, v, rows.astype(np.int32), hm[hs], w.scale)
+        secs += time.perf_counter() - t0
+        flop += 4.0 * D * len(hs) * float((rows + 1).sum())
+        err = np.abs(o[rows][:, hs].astype(np.float64) - ro)
+        if not np.all(err <= 2e-3):
+            raise SystemExit(f"bench: GPU prefill output disagrees with the oracle (max err {err.max():.3e})")
+        max_err = max(max_err, float(err.max()))
+    return {"value": round(flop / secs / 1e9, 3), "unit": "GFLOP/s", "cores": oracle.num_threads(),
+            "cpu_model": _cpu_model(), "kind": "oracle",
+            "sample": f"every row of {len(heads)} q-heads (one per K/V head) + the first and last {edge} rows of "
+                      f"all {w.hq} q-heads of the 8192-token prefill: {flop / 1e9:.1f} GFLOP over visible pairs, "
+                      f"{secs:.2f} s timed; GPU outputs agreed (max abs err {max_err:.2e})"}
 
 
 def main():
@@ -727,9 +851,14 @@ def main():
                              "GBs_read_plus_written": round(2 * src.numel() / (cms * 1e-3) / 1e9, 1),
                              "frac_hbm": round(2 * src.numel() / (cms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4)}
     del src, dst
+    result["provenance"] = provenance(torch)
     if not args.no_cpu_baseline:
         import oracle
         result["cpu_baseline"] = cpu_baseline(d, dec_out.cpu().numpy(), np, oracle)
+        print("bench: decode oracle baseline timed", file=sys.stderr, flush=True)
+        if p is not None:
+            result["prefill"]["cpu_baseline"] = prefill_cpu_baseline(p, pre_out.cpu().numpy(), np, oracle)
+            print("bench: prefill oracle baseline timed", file=sys.stderr, flush=True)
     print(json.dumps(result), flush=True)
 
 

@@ -8,6 +8,8 @@ from __future__ import annotations
 
 import concurrent.futures as cf
 import glob
+import hashlib
+import json
 import os
 import shutil
 import subprocess
@@ -17,6 +19,7 @@ HERE = os.path.dirname(os.path.abspath(__file__))
 CSRC = os.path.join(HERE, "csrc")
 BUILD_DIR = os.path.join(HERE, "_build")
 LIB = os.path.join(HERE, "libatlas.so")
+INFO = os.path.join(HERE, "build_info.json")   # written beside the library (not committed)
 INCLUDE = os.path.join(os.path.dirname(HERE), "include")
 
 ARCH = "gfx950"
@@ -45,6 +48,25 @@ def _compile(src: str, hipcc: str, extra) -> str:
     return obj
 
 
+def sources_sha256() -> str:
+    """Hash of the library's sources (csrc and the public header)."""
+    h = hashlib.sha256()
+    files = sorted(glob.glob(os.path.join(CSRC, "*")) + [os.path.join(INCLUDE, "atlas.h")])
+    for f in files:
+        h.update(os.path.basename(f).encode())
+        with open(f, "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()
+
+
+def _git(*args):
+    try:
+        r = subprocess.run(["git", "-C", os.path.dirname(HERE), *args], capture_output=True, text=True, timeout=10)
+        return r.stdout.strip() if r.returncode == 0 else None
+    except (OSError, subprocess.SubprocessError):
+        return None
+
+
 def build(verbose: bool = False, extra=()) -> str:
     """Compile every csrc/*.hip and csrc/*.cpp and link libatlas.so; returns its path."""
     os.makedirs(BUILD_DIR, exist_ok=True)
@@ -59,6 +81,12 @@ def build(verbose: bool = False, extra=()) -> str:
     if res.returncode != 0:
         raise RuntimeError(f"link failed:\n{res.stderr}")
     os.replace(tmp, LIB)
+    status = _git("status", "--porcelain", "--", "exact_paged_causal_amd/csrc", "include")
+    info = {"git_commit": _git("rev-parse", "HEAD"),
+            "sources_modified_since_commit": None if status is None else bool(status),
+            "sources_sha256": sources_sha256(), "hipcc_flags": FLAGS + list(extra)}
+    with open(INFO, "w") as f:
+        json.dump(info, f, indent=1)
     if verbose:
         print(f"built {LIB} from {len(sources)} sources")
     return LIB
