@@ -333,7 +333,7 @@ int32_t validate_device(const atlas_attn_args *a, const Plan &p, hipStream_t str
     s.num_phys = a->num_phys_pages;
     s.max_pages = a->max_pages_per_seq;
     s.max_context = p.max_context;
-    s.check_f16 = p.path == Path::TiledPrefill ? 1 : (p.path == Path::TiledSplit ? 2 : 0);
+    s.check_f16 = (p.path == Path::TiledPrefill || p.path == Path::TiledSplit) ? 1 : 0;
     int flag = 0;
     e = hipMemsetAsync(s.flag, 0, sizeof(int), stream);
     if (e == hipSuccess)
@@ -347,11 +347,8 @@ int32_t validate_device(const atlas_attn_args *a, const Plan &p, hipStream_t str
     if (flag & 1)
         return fail(ATLAS_ERR_NONFINITE, "NaN or Inf in q or in the K/V rows the contexts cover");
     if (flag & 2)
-        return fail(ATLAS_ERR_RANGE, p.path == Path::TiledSplit
-                                         ? "a Q, K or V value exceeds 65504, the fp16 range of the fp32 tiled "
-                                           "prefill's split operands"
-                                         : "a V value exceeds 65504, the fp16 range of the tiled prefill's P.V "
-                                           "product");
+        return fail(ATLAS_ERR_RANGE, "a V value exceeds 65504, the fp16 range of the tiled prefill's P.V "
+                                     "product");
     return ok();
 }
 

@@ -142,8 +142,7 @@ struct ScanArgs {
     const int32_t *context_lens;
     int *flag;                  // bit 0: NaN/Inf; bit 1: beyond the fp16 range (cleared by the caller)
     int32_t batch, q_len, hq, hkv, head_dim, page_shift, num_phys, max_pages, max_context;
-    int32_t check_f16;          // flag values beyond 65504: 1 = V (the bf16 tiled prefill's fp16 P.V
-                                // product), 2 = Q, K and V (the fp32 tiled prefill's split operands)
+    int32_t check_f16;          // 1: flag V values beyond 65504 (the tiled prefills' fp16 P.V products)
 };
 
 hipError_t launch_scan(const ScanArgs &a, int q_dtype, int kv_dtype, hipStream_t stream);

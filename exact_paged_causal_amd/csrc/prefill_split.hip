@@ -39,8 +39,9 @@
 // non-causal rows take every key block of the context; ALiBi bias (in the
 // units the scores have after the softcap step) and mask bits per element.
 //
-// Precondition: |q|, |k|, |v| <= 65504 (fp16 range of the hi parts);
-// validation mode checks it.
+// Precondition: |v| <= 65504 (fp16 range of V's hi parts; validation mode
+// checks it).  Q and K rows take any magnitude below 2^115: the range shift
+// (clamped to +-100) brings each row's largest element into [2^14, 2^15).
 #include "device.h"
 #include "kernels.h"
 

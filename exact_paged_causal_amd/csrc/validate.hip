@@ -4,10 +4,10 @@
 // inputs before they reach the cache.  In validation mode the C ABI runs this
 // scan first: every query element, and every K/V element of the rows each
 // sequence's context covers (rows past the context are never read and are
-// not scanned).  For the tiled prefills it also flags values outside the
-// fp16 range their matrix products use: V for the bf16 kernel (its P.V
-// product), Q, K and V for the fp32 kernel (split into fp16 parts).  Hits set
-// bits of a flag word, which the host reads back.
+// not scanned).  For the tiled prefills it also flags V values outside the
+// fp16 range of their P.V products (the fp32 kernel scales Q and K rows into
+// that range itself).  Hits set bits of a flag word, which the host reads
+// back.
 #include "device.h"
 #include "kernels.h"
 
@@ -59,7 +59,6 @@ __global__ __launch_bounds__(256) void scan_kernel(ScanArgs a)
         const EQ *q = reinterpret_cast<const EQ *>(a.q) + (int64_t)b * n;
         for (int64_t i = threadIdx.x; i < n; i += 256) {
             bad |= !finite_elem<EQ>(q[i]);
-            wide |= a.check_f16 == 2 && beyond_f16<EQ>(q[i]);
         }
     } else {
         const int P = 1 << a.page_shift;
@@ -78,7 +77,6 @@ __global__ __launch_bounds__(256) void scan_kernel(ScanArgs a)
                     bad |= !finite_elem<E>(kk);
                     bad |= !finite_elem<E>(vv);
                     wide |= a.check_f16 != 0 && beyond_f16<E>(vv);
-                    wide |= a.check_f16 == 2 && beyond_f16<E>(kk);
                 }
             }
         }

@@ -189,8 +189,8 @@ const char *atlas_last_error(void);
  * ("Runtime ownership") keeps workspace and output allocation outside the
  * timed native call; here the caller allocates the workspace once (device
  * memory, any alignment of 256 bytes or more) and may reuse it for every call
- * with the same or smaller sizes.  Returns SIZE_MAX when the sizes are
- * invalid (the reason is in atlas_last_error()). */
+ * that fits in it; its contents need no initialisation.  Returns SIZE_MAX
+ * when the sizes are invalid (the reason is in atlas_last_error()). */
 size_t atlas_decode_workspace_bytes(const atlas_attn_args *args);
 size_t atlas_prefill_workspace_bytes(const atlas_attn_args *args);
 
@@ -221,8 +221,15 @@ int32_t atlas_attend_decode(const atlas_attn_args *args, void *stream);
  * tiling on the fp16 matrix cores with every operand split into two fp16
  * parts (hi = fp16(x), lo = fp16(x - hi)) and each product taken as
  * hi.hi + lo.hi + hi.lo, which keeps fp32 accuracy (CPUAttn defines the
- * method on FP32 tensors); it requires |q|, |k|, |v| <= 65504 (validation
- * mode: ATLAS_ERR_RANGE).  Every other case runs the split-KV kernels of
+ * method on FP32 tensors).  Q and K rows are first scaled by powers of two
+ * into the fp16 range, so any finite q and k elements below 2^115 in
+ * magnitude are taken (the scores scale * q.k still have to stay within the
+ * fp32 softmax's range, |score| < 2^26); V is split unscaled, so this path
+ * requires |v| <= 65504 (validation
+ * mode: ATLAS_ERR_RANGE).  On both tiled paths a V value beyond 65504 is
+ * outside the kernel's domain: validation mode rejects the call, and without
+ * validation the rows that read it come out inf or NaN (the split-KV kernels
+ * below take any finite V).  Every other case runs the split-KV kernels of
  * atlas_attend_decode with each (query, q-head) pair as a row.
  */
 int32_t atlas_attend_prefill(const atlas_attn_args *args, void *stream);
