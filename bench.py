@@ -59,7 +59,8 @@ sys.path.insert(0, ROOT)
 # counters (profiles/traffic.json) is reported only while these files still
 # hash to what was profiled; otherwise `traffic` is null.
 PROFILED_SOURCES = {
-    "decode_split_long_context": ["split_valu.hip", "merge.hip", "plan.h", "device.h", "kernels.h"],
+    "decode_split_long_context": ["split_valu.hip", "merge.hip", "merge_row.h", "philox.h", "plan.h", "device.h",
+                                  "kernels.h"],
     "prefill_tiled_causal_8192": ["prefill_mfma.hip", "device.h", "kernels.h"],
     "regen_long_context": ["regen.hip", "philox.h", "device.h", "kernels.h"],
 }
