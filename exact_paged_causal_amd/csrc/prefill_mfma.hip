@@ -147,6 +147,11 @@ __global__ __launch_bounds__(512) void prefill_kernel(PrefillArgs a)
     const float slope_raw = (MODS && row_ok && a.mods.alibi) ? a.mods.alibi[h] / a.scale : 0.0f;
     const uint32_t *mrow =
         (MODS && row_ok && a.mods.mask) ? a.mods.mask + ((int64_t)b * a.q_len + qi) * a.mods.mask_words : nullptr;
+    // ALiBi on a key block starting at k0 is slope (k0 - pos) + slope jo over
+    // its keys jo = j - k0 (both negated for a block at or right of the row):
+    // one FMA with a constant per score for the per-key part, while the
+    // per-lane part joins the row max and the exponent's offset.
+    const bool alibi_on = MODS && a.mods.alibi != nullptr;
 
     bf16x8 qf[KS];
     {
@@ -169,9 +174,12 @@ __global__ __launch_bounds__(512) void prefill_kernel(PrefillArgs a)
 
     // Page ids come from LDS, so a block's K/V loads never wait on a
     // page-table load.  Staged by windows of kPidWindow pages (one window
-    // covers every page of all but extremely long, finely paged histories).
+    // covers every page of all but extremely long, finely paged histories);
+    // a window ends at the block's last page when the blocks run backwards.
     int pid_base = 0;
     auto stage_pids = [&](int first_page) {
+        if (MODS && first_page < 0)
+            first_page = 0;
         pid_base = first_page;
         const int last_page = key_hi >= 0 ? key_hi >> ps : -1;
         for (int t = tid; t < kPidWindow && first_page + t <= last_page; t += 512) {
@@ -251,53 +259,107 @@ __global__ __launch_bounds__(512) void prefill_kernel(PrefillArgs a)
 
     // MODS with mask bits: the candidate blocks whose mask words are zero for
     // every row of this workgroup are dropped; the rest are listed in order
-    // (wave 0 compacts the flags with a ballot).  The test is conservative:
-    // a listed block may still be wholly hidden by the causal or window rule.
-    __shared__ int32_t s_blk[MODS ? kMaxListed : 1];
-    __shared__ uint8_t s_flag[MODS ? kMaxListed : 1];
+    // (wave 0 compacts the flags with a ballot), each marked full when every
+    // row's 64 bits are set (its mask bits are then not applied per score).
+    // The tests are conservative: a listed block may still be wholly hidden
+    // by the causal or window rule.  Consecutive threads read consecutive
+    // blocks of one mask row.
+    __shared__ int32_t s_blk[MODS ? kMaxListed : 1];   // block * 2 + partial
+    __shared__ uint8_t s_need[MODS ? kMaxListed : 1];
+    __shared__ uint8_t s_part[MODS ? kMaxListed : 1];
     __shared__ int32_t s_count;
+    __shared__ int32_t s_pivot;
     int n_run = n_iter;
     bool listed = false;
+    // ALiBi: listed blocks whose first key is at or left of the last row's
+    // position (the blocks run outward from the diagonal, see below).
+    const int kb_diag = pos_hi >= 0 ? pos_hi / kBN : -1;
+    int n_left = 0;
     if constexpr (MODS) {
         if (a.mods.mask && n_iter > 0 && n_iter <= kMaxListed) {
             listed = true;
-            for (int i = tid; i < n_iter; i += 512)
-                s_flag[i] = 0;
+            for (int i = tid; i < n_iter; i += 512) {
+                s_need[i] = 0;
+                s_part[i] = 0;
+            }
             __syncthreads();
             const int rows_pos = i1 - i0;
             const int wl = a.mods.mask_words - 1;
             for (int idx = tid; idx < n_iter * rows_pos; idx += 512) {
-                const int c = idx / rows_pos;
-                const int pp = idx - c * rows_pos;
+                const int pp = idx / n_iter;
+                const int c = idx - pp * n_iter;
                 const uint32_t *m = a.mods.mask + ((int64_t)b * a.q_len + i0 + pp) * a.mods.mask_words;
                 const int w = (block_at(c) * kBN) >> 5;
-                if ((m[w < wl ? w : wl] | m[w + 1 < wl ? w + 1 : wl]) != 0u)
-                    s_flag[c] = 1;
+                const uint32_t m0 = m[w < wl ? w : wl];
+                const uint32_t m1 = m[w + 1 < wl ? w + 1 : wl];
+                if ((m0 | m1) != 0u)
+                    s_need[c] = 1;
+                if ((m0 & m1) != ~0u || w + 1 > wl)
+                    s_part[c] = 1;
             }
             __syncthreads();
             if (wave == 0) {
-                int base = 0;
+                int base = 0, left = 0;
                 for (int c0 = 0; c0 < n_iter; c0 += 64) {
                     const int c = c0 + lane;
-                    const bool f = c < n_iter && s_flag[c];
+                    const bool f = c < n_iter && s_need[c];
                     const uint64_t bal = __ballot(f);
                     if (f)
-                        s_blk[base + __popcll(bal & ((1ull << lane) - 1ull))] = block_at(c);
+                        s_blk[base + __popcll(bal & ((1ull << lane) - 1ull))] = block_at(c) * 2 + s_part[c];
                     base += __popcll(bal);
+                    left += __popcll(__ballot(f && block_at(c) <= kb_diag));
                 }
-                if (lane == 0)
+                if (lane == 0) {
                     s_count = base;
+                    s_pivot = left;
+                }
             }
             __syncthreads();
             n_run = s_count;
+            n_left = s_pivot;
+        } else {
+            // Entries of this run of the ascending list at or left of kb_diag.
+            int le = kb_diag < 0 ? 0
+                     : kb_diag < tbk.n_sink ? kb_diag + 1
+                                            : tbk.n_sink + (kb_diag - tbk.first_win + 1);
+            le = le < tbk.n_sink ? (kb_diag < tbk.n_sink ? le : tbk.n_sink) : (le > tbk.n ? tbk.n : le);
+            le -= c_lo;
+            n_left = le < 0 ? 0 : (le > n_iter ? n_iter : le);
         }
     }
-    auto run_block = [&](int it) { return (MODS && listed) ? s_blk[it] : block_at(it); };
+    // Block order.  With ALiBi the bias falls with the distance from the
+    // row, so the blocks run from the diagonal leftwards and then rightwards
+    // (non-causal rows): the first block holds (nearly) the row max and the
+    // accumulator is rarely rescaled; forward otherwise.
+    const int d_last = alibi_on ? n_left - 1 : -1;
+    auto list_at = [&](int it) { return (MODS && it <= d_last) ? d_last - it : it; };
+    auto run_block = [&](int it) {
+        const int i = list_at(it);
+        return (MODS && listed) ? s_blk[i] >> 1 : block_at(i);
+    };
+    // First page to stage for block kb when the walk goes backwards from it.
+    auto back_first = [&](int kbx) { return ((kbx * kBN + kBN - 1) >> ps) - kPidWindow + 1; };
 
     if (n_run > 0)
-        stage_pids((run_block(0) * kBN) >> ps);
+        stage_pids(d_last >= 0 ? back_first(run_block(0)) : (run_block(0) * kBN) >> ps);
     __syncthreads();  // page ids staged
+    // MODS: the row's mask words for a block's two 32-key tiles (words past
+    // the row's end hold keys beyond every context and are clamped); full
+    // blocks need none.  Loaded one block ahead with the K/V, so the stash's
+    // wait covers them and the next block reads them without waiting.
+    auto is_partial = [&](int it) { return !(MODS && listed) || (s_blk[list_at(it)] & 1); };
+    auto mask_words = [&](int it, int kbx, uint32_t &m0, uint32_t &m1) {
+        if (mrow && is_partial(it)) {
+            const int w = (kbx * kBN) >> 5;
+            const int wl = a.mods.mask_words - 1;
+            m0 = mrow[w < wl ? w : wl];
+            m1 = mrow[w + 1 < wl ? w + 1 : wl];
+        }
+    };
+    uint32_t mw0 = ~0u, mw1 = ~0u;  // the current block's mask words
     if (n_run > 0) {
+        if constexpr (MODS)
+            mask_words(0, run_block(0), mw0, mw1);
         fetch(run_block(0));
         stash(0);
     }
@@ -308,29 +370,30 @@ __global__ __launch_bounds__(512) void prefill_kernel(PrefillArgs a)
         const int cur = it & 1;
         const bool more = it + 1 < n_run;
         const int kb_next = more ? run_block(it + 1) : kb;
-        if (more && (((kb_next * kBN + kBN - 1) >> ps) - pid_base) >= kPidWindow) {
-            // Uniform across the workgroup: move the page-id window forward.
+        if (more && ((((kb_next * kBN + kBN - 1) >> ps) - pid_base) >= kPidWindow ||
+                     (MODS && ((kb_next * kBN) >> ps) < pid_base))) {
+            // Uniform across the workgroup: move the page-id window.
             __syncthreads();
-            stage_pids((kb_next * kBN) >> ps);
+            stage_pids((MODS && kb_next < kb) ? back_first(kb_next) : (kb_next * kBN) >> ps);
             __syncthreads();
         }
-        if (more)
-            fetch(kb_next);
-        // MODS: the row's mask words for this block's two 32-key tiles (words
-        // past the row's end hold keys beyond every context and are clamped).
-        uint32_t mw0 = ~0u, mw1 = ~0u;
-        if (MODS && mrow) {
-            const int w = (kb * kBN) >> 5;
-            const int wl = a.mods.mask_words - 1;
-            mw0 = mrow[w < wl ? w : wl];
-            mw1 = mrow[w + 1 < wl ? w + 1 : wl];
+        const int k0 = kb * kBN;
+        const bool part = is_partial(it);
+        uint32_t nw0 = ~0u, nw1 = ~0u;
+        if constexpr (MODS) {
+            if (more) {
+                mask_words(it + 1, kb_next, nw0, nw1);
+                fetch(kb_next);
+            }
+        } else {
+            if (more)
+                fetch(kb_next);
         }
-
         // S^T for the block: two 32-key tiles.
+        f32x16 st[2] = {f32x16{}, f32x16{}};
         __builtin_amdgcn_s_setprio(1);
         // The two tiles' accumulation chains alternate: back-to-back
         // products into one accumulator would wait on each other.
-        f32x16 st[2] = {f32x16{}, f32x16{}};
 #pragma unroll
         for (int s = 0; s < KS; ++s) {
 #pragma unroll
@@ -351,55 +414,69 @@ __global__ __launch_bounds__(512) void prefill_kernel(PrefillArgs a)
 
         __builtin_amdgcn_s_setprio(0);
 
-        // Softcap (before the mask): s' = cap tanh(s scale / cap), kept in the
-        // units of the raw product so that the scale below still applies.
-        // The hardware-exponential tanh keeps the logit error under cap * 1e-6.
+        // Softcap (before the mask).  The capped logit cap tanh(s scale / cap)
+        // is, in log2 units, L - 2L / (1 + 2^(k2 s)) with L = cap log2(e) and
+        // k2 = 2 scale log2(e) / cap.  Each score becomes v = -1 / (1 + 2^(k2 s)),
+        // which orders like the capped logit, so the mask and the row max
+        // below apply unchanged and the map v -> 2L v + L replaces the scale
+        // (lg_mul, lg_add).  With ALiBi, which is added after the cap in
+        // raw-product units, the capped logit is formed in those units
+        // instead.  The hardware exponential and reciprocal keep the logit
+        // error under cap * 1e-6.
+        float lg_mul = c_log2, lg_add = 0.0f;
         if (cap > 0.0f) {
-            const float k2 = 2.0f * 1.4426950408889634f * a.scale / cap, back = cap / a.scale;
+            const float k2 = 2.0f * kLog2e * a.scale / cap;
+            if (MODS && alibi_on) {
+                const float back = cap / a.scale;
 #pragma unroll
-            for (int t = 0; t < 2; ++t)
+                for (int t = 0; t < 2; ++t)
 #pragma unroll
-                for (int e = 0; e < 16; ++e)
-                    st[t][e] = scaled_tanh_fast(st[t][e], k2, back, -2.0f * back);
+                    for (int e = 0; e < 16; ++e)
+                        st[t][e] = scaled_tanh_fast(st[t][e], k2, back, -2.0f * back);
+            } else {
+                lg_mul = 2.0f * cap * kLog2e;
+                lg_add = cap * kLog2e;
+#pragma unroll
+                for (int t = 0; t < 2; ++t)
+#pragma unroll
+                    for (int e = 0; e < 16; ++e)
+                        st[t][e] = __builtin_amdgcn_rcpf(-1.0f - __builtin_amdgcn_exp2f(st[t][e] * k2));
+            }
         }
         // Mask only blocks some row does not see whole: past the first row's
         // position (causal), or not inside every row's window or sink range.
-        const int k0 = kb * kBN;
+        float cst = 0.0f;
         if constexpr (MODS) {
-            // ALiBi: on a block wholly at or left of this row's position the
-            // bias -slope |pos - j| is linear in j, c + slope (j - k0 - 4 half)
-            // with c per lane and block, one FMA with a constant per element;
-            // wholly right of it (non-causal rows) the mirror image; only
-            // blocks crossing the position take the absolute value.
-            if (slope_raw != 0.0f) {
-                if (k0 + kBN - 1 <= pos) {
-                    const float c = slope_raw * (float)(k0 + 4 * half - pos);
+            // ALiBi (after the softcap): this lane's part of the bias, in
+            // raw-product units, and the per-key part, one FMA per score.
+            float sslope = 0.0f;
+            if (alibi_on) {
+                const bool right = k0 >= pos;
+                sslope = right ? -slope_raw : slope_raw;
+                cst = sslope * (float)(k0 + 4 * half - pos);
 #pragma unroll
-                    for (int t = 0; t < 2; ++t)
+                for (int t = 0; t < 2; ++t)
 #pragma unroll
-                        for (int e = 0; e < 16; ++e)
-                            st[t][e] += fmaf(slope_raw, (float)(32 * t + 8 * (e >> 2) + (e & 3)), c);
-                } else if (k0 >= pos) {
-                    const float c = slope_raw * (float)(pos - k0 - 4 * half);
-#pragma unroll
-                    for (int t = 0; t < 2; ++t)
-#pragma unroll
-                        for (int e = 0; e < 16; ++e)
-                            st[t][e] += fmaf(-slope_raw, (float)(32 * t + 8 * (e >> 2) + (e & 3)), c);
-                } else {
-#pragma unroll
-                    for (int t = 0; t < 2; ++t)
-#pragma unroll
-                        for (int e = 0; e < 16; ++e) {
-                            const int j = k0 + 32 * t + 8 * (e >> 2) + 4 * half + (e & 3);
-                            st[t][e] -= slope_raw * fabsf((float)(pos - j));
-                        }
-                }
+                    for (int e = 0; e < 16; ++e)
+                        st[t][e] = fmaf(sslope, (float)(32 * t + 8 * (e >> 2) + (e & 3)), st[t][e]);
             }
-            // Mask bits on every element when given; otherwise only blocks
-            // some row does not see whole (non-causal rows: keys past the
-            // context).
-            if (mrow || k0 + kBN - 1 > (causal ? pos_lo : key_hi) ||
+            // A block crossing a non-causal row's position took the left-hand
+            // form: keys right of the position are corrected to the mirror
+            // image (causal rows never see them).
+            if (alibi_on && !causal && k0 < pos && k0 + kBN - 1 > pos) {
+#pragma unroll
+                for (int t = 0; t < 2; ++t)
+#pragma unroll
+                    for (int e = 0; e < 16; ++e) {
+                        const int j = k0 + 32 * t + 8 * (e >> 2) + 4 * half + (e & 3);
+                        if (j > pos)
+                            st[t][e] -= 2.0f * slope_raw * (float)(j - pos);
+                    }
+            }
+            // Mask bits on every score of a partial block; otherwise only
+            // blocks some row does not see whole (non-causal rows: keys past
+            // the context).
+            if ((mrow && part) || k0 + kBN - 1 > (causal ? pos_lo : key_hi) ||
                 !(W <= 0 || k0 > pos_hi - W || k0 + kBN - 1 < S)) {
 #pragma unroll
                 for (int t = 0; t < 2; ++t)
@@ -436,8 +513,10 @@ __global__ __launch_bounds__(512) void prefill_kernel(PrefillArgs a)
 #pragma unroll
             for (int e = 0; e < 16; ++e)
                 mx = fmaxf(mx, st[t][e]);
+        if constexpr (MODS)
+            mx += cst;
         mx = fmaxf(mx, __shfl_xor(mx, 32));
-        const float m_blk = mx * c_log2;
+        const float m_blk = fmaf(mx, lg_mul, lg_add);
         if (m_blk > m_ref + kRescaleSlack) {
             const float alpha = fast_exp2(m_ref - m_blk);
             l_part *= alpha;
@@ -447,6 +526,7 @@ __global__ __launch_bounds__(512) void prefill_kernel(PrefillArgs a)
             m_ref = m_blk;
         }
         const float msafe = m_ref == -INFINITY ? 0.0f : m_ref;
+        const float p_off = MODS ? fmaf(cst, lg_mul, lg_add - msafe) : lg_add - msafe;
 
         // P^T as the B operand: tile t, k-step ks -> elements 8ks..8ks+7,
         // packed two fp16 values per 32-bit word.  The row sum is taken over
@@ -457,8 +537,8 @@ __global__ __launch_bounds__(512) void prefill_kernel(PrefillArgs a)
         for (int t = 0; t < 2; ++t) {
 #pragma unroll
             for (int e = 0; e < 16; e += 2) {
-                const float p0 = fast_exp2(fmaf(st[t][e], c_log2, -msafe));
-                const float p1 = fast_exp2(fmaf(st[t][e + 1], c_log2, -msafe));
+                const float p0 = fast_exp2(fmaf(st[t][e], lg_mul, p_off));
+                const float p1 = fast_exp2(fmaf(st[t][e + 1], lg_mul, p_off));
                 const f16x2 ph = __builtin_convertvector(f32x2{p0, p1}, f16x2);
                 l_part = __builtin_amdgcn_fdot2(ph, ones, l_part, false);
                 pw[t][e >> 3][(e & 7) >> 1] = __builtin_bit_cast(uint32_t, ph);
@@ -507,6 +587,10 @@ __global__ __launch_bounds__(512) void prefill_kernel(PrefillArgs a)
         if (more)
             stash(cur ^ 1);
         __syncthreads();
+        if constexpr (MODS) {
+            mw0 = nw0;
+            mw1 = nw1;
+        }
     }
 
     // Epilogue: O = O^T / l, lse = (m + log2 l) ln 2.

@@ -122,6 +122,13 @@ CASES = [
     ("f32", 8, 2, 128, 16, 100, (100, 300), False, True, 0.7),    # fp32 tiled
     ("f32", 4, 1, 64, 32, 70, (500,), True, True, None),
     ("f32", 2, 2, 128, 128, 257, (3000,), False, False, 0.4),
+    # ALiBi walks the key blocks outward from the diagonal: over 3000
+    # one-token pages the page-id window moves backwards (and forwards again
+    # for non-causal rows), with and without a listed mask
+    ("bf16", 4, 1, 64, 1, 64, (3000,), True, True, None),
+    ("bf16", 4, 1, 64, 1, 3000, (3000,), False, True, None),
+    ("bf16", 4, 1, 64, 1, 64, (3000,), True, True, 0.9),
+    ("bf16", 4, 1, 64, 1, 1000, (3000,), False, True, 0.9),
 ]
 
 
@@ -216,3 +223,24 @@ def test_block_sparse_document_mask(dtype):
     torch.cuda.synchronize()
     assert torch.isnan(out[0, :64]).all() and torch.isneginf(lse[0, :64]).all()
     check_mods(inp, out, lse, True, None, mask, f"document mask {dtype}")
+
+
+def test_document_mask_full_size():
+    """The causal-prefill shape (S=8192, Hq=32, Hkv=8, D=128, bf16) packed with
+    four documents of 2048 tokens (a causal block-diagonal mask, as the
+    benchmark runs it): key blocks inside a document are wholly visible to a
+    query block's rows and skip the per-score mask.  Every row of one seeded
+    q-head per K/V head, and the first and last 512 rows of every q-head."""
+    w = workloads.make("causal_prefill")
+    say("[mods] causal_prefill shape with a 4 x 2048 document mask")
+    inp = H.build(w)
+    L = int(inp.layout.page_table.shape[1]) * w.page_size
+    j = np.arange(L)
+    pos = np.arange(w.q_len)
+    mask = ((j[None, :] // 2048 == pos[:, None] // 2048) & (j[None, :] <= pos[:, None]))[None]
+    out, lse = run_mods(inp, True, None, mask)
+    torch.cuda.synchronize()
+    for rows, heads in H.full_size_blocks(w, seed=3):
+        say(f"[mods] oracle on {len(rows)} rows x heads {heads.tolist()}")
+        check_mods(inp, out, lse, True, None, mask, "document mask full size", rows=rows, heads=heads)
+    assert not torch.isnan(out).any()
