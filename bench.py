@@ -159,9 +159,17 @@ def prefill_setup(torch, workloads, np):
     return dict(w=w, lay=lay, k=k, v=v, q=q, pt=pt, ctx=ctx, kl=kl, vl=vl)
 
 
-def _median_call_us(torch, np, fn, calls=30, warm=5):
-    for _ in range(warm):
+def _median_call_us(torch, np, fn, calls=30, warm=5, warm_s=0.1):
+    """Median HIP-event time of `calls` back-to-back calls, after at least
+    `warm` calls and `warm_s` seconds of them (the clocks ramp back up after
+    host-only set-up phases)."""
+    t0 = time.perf_counter()
+    n = 0
+    while n < warm or time.perf_counter() - t0 < warm_s:
         fn()
+        n += 1
+        if n % 4 == 0:
+            torch.cuda.synchronize()
     torch.cuda.synchronize()
     t = Timer(torch)
     for _ in range(calls):
@@ -623,11 +631,17 @@ def provenance(torch):
     """Where the numbers come from (CPUAttn README, "Benchmark suite": reports
     carry their environment)."""
     prop = torch.cuda.get_device_properties(0)
+    lib = _library_build()
+    commit, source = _git_commit(), "git"
+    if commit is None and lib:
+        # a copy of the tree without its repository: the commit the library
+        # was built at (library_build says whether the sources changed since)
+        commit, source = lib.get("git_commit"), "library build record"
     return {"gpu": getattr(prop, "gcnArchName", None) or torch.cuda.get_device_name(0),
             "gpu_name": torch.cuda.get_device_name(0), "cu_count": prop.multi_processor_count,
             "gpu_sclk_mhz_after_timing": gpu_sclk_mhz(), "cpu_model": _cpu_model(),
             "host_threads": os.cpu_count(), "rocm": _rocm_version(), "hip_runtime": torch.version.hip,
-            "torch": torch.__version__, "git_commit": _git_commit(), "library_build": _library_build()}
+            "torch": torch.__version__, "git_commit": commit, "git_commit_from": source, "library_build": lib}
 
 
 def prefill_cpu_baseline(p, out, np, oracle, heads_per_kv=1, edge=512):
