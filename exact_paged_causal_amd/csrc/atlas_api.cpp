@@ -278,6 +278,8 @@ int32_t check_pointers(const atlas_attn_args *a, const Plan &p)
         if (a->workspace_bytes < p.workspace)
             return fail(ATLAS_ERR_WORKSPACE, "workspace of %zu bytes, %zu needed", a->workspace_bytes,
                         p.workspace);
+        if (reinterpret_cast<uintptr_t>(a->workspace) % 16 != 0)
+            return fail(ATLAS_ERR_WORKSPACE, "workspace must be 16-byte aligned");
     }
     return ok();
 }
@@ -569,7 +571,7 @@ const char *atlas_status_str(int32_t status)
     case ATLAS_ERR_SHAPE: return "invalid shape";
     case ATLAS_ERR_RANGE: return "value out of range";
     case ATLAS_ERR_UNSUPPORTED: return "unsupported (no kernel for this configuration)";
-    case ATLAS_ERR_WORKSPACE: return "workspace too small";
+    case ATLAS_ERR_WORKSPACE: return "workspace too small or misaligned";
     case ATLAS_ERR_POOL: return "page id outside the physical pool";
     case ATLAS_ERR_NONFINITE: return "non-finite input";
     case ATLAS_ERR_DEVICE: return "HIP runtime error";

@@ -9,15 +9,18 @@
 namespace atlas {
 namespace {
 
-template <int D>
+template <int D, int NF>
 __global__ __launch_bounds__(64) void merge_kernel(SplitArgs a)
 {
-    const int64_t row_id = blockIdx.x;
-    const int h = (int)(row_id % a.hq);
-    const int64_t bi = row_id / a.hq;
-    const int i = (int)(bi % a.q_len);
-    const int b = (int)(bi / a.q_len);
-    merge_row<D>(a, row_id, merge_split_count(a, b, i, h), threadIdx.x);
+    // 32-bit index arithmetic: the grid has fewer than 2^31 rows.
+    const uint32_t row = blockIdx.x;
+    const uint32_t bi = row / (uint32_t)a.hq;
+    const int h = (int)(row - bi * (uint32_t)a.hq);
+    const uint32_t b32 = bi / (uint32_t)a.q_len;
+    const int i = (int)(bi - b32 * (uint32_t)a.q_len);
+    const int b = (int)b32;
+    const int64_t row_id = row;
+    merge_row<D, NF>(a, row_id, [&] { return merge_split_count(a, b, i, h); }, threadIdx.x);
 }
 
 }  // namespace
@@ -25,10 +28,21 @@ __global__ __launch_bounds__(64) void merge_kernel(SplitArgs a)
 hipError_t launch_merge(const SplitArgs &a, hipStream_t stream)
 {
     const int64_t rows = (int64_t)a.batch * a.q_len * a.hq;
-    if (a.head_dim == 64)
-        hipLaunchKernelGGL(merge_kernel<64>, dim3((unsigned)rows), dim3(64), 0, stream, a);
-    else
-        hipLaunchKernelGGL(merge_kernel<128>, dim3((unsigned)rows), dim3(64), 0, stream, a);
+    if (rows <= 0 || rows > 0x7FFFFFFF)
+        return hipErrorInvalidValue;
+    // The first batch of accumulator rows covers max_splits (up to 64).
+    const int nf = a.max_splits <= 8 ? 0 : a.max_splits <= 16 ? 1 : a.max_splits <= 32 ? 2 : 3;
+    void (*kernel)(SplitArgs);
+    if (a.head_dim == 64) {
+        void (*const k64[4])(SplitArgs) = {merge_kernel<64, 8>, merge_kernel<64, 16>, merge_kernel<64, 32>,
+                                           merge_kernel<64, 64>};
+        kernel = k64[nf];
+    } else {
+        void (*const k128[4])(SplitArgs) = {merge_kernel<128, 8>, merge_kernel<128, 16>, merge_kernel<128, 32>,
+                                            merge_kernel<128, 64>};
+        kernel = k128[nf];
+    }
+    hipLaunchKernelGGL(kernel, dim3((unsigned)rows), dim3(64), 0, stream, a);
     return hipGetLastError();
 }
 

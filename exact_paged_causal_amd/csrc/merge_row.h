@@ -49,22 +49,59 @@ __device__ __forceinline__ int merge_split_count(const SplitArgs &a, int b, int 
 // One wave merges output row row_id = (b * q_len + i) * hq + h over its n
 // splits: lanes over splits for the maximum and the denominator, then lanes
 // over dims for the weighted sum in split order (each split's weight is the
-// same hardware exponential both times).
-template <int D>
-__device__ __forceinline__ void merge_row(const SplitArgs &a, int64_t row_id, int n, int lane)
+// same hardware exponential both times).  The chain of memory round trips is
+// kept short: the (m, l) pairs of the first 64 splits (one per lane) and
+// the accumulator rows of the first NF are loaded before the split count is
+// known (their addresses depend only on the row; entries past the count are
+// never used), the weights are broadcast from the lanes that computed them,
+// and any further splits are loaded 32 at a time.  count() gives the split
+// count; NF (8 to 64) is chosen on the host to cover max_splits.
+template <int D, int NF, class Count>
+__device__ __forceinline__ void merge_row(const SplitArgs &a, int64_t row_id, Count count, int lane)
 {
-    constexpr int DPT = D / 64;  // dims per lane
-    const float *ml = a.ws_ml + row_id * a.max_splits * 2;
-    const float *acc = a.ws_acc + row_id * a.max_splits * D;
+    static_assert(NF >= 1 && NF <= 64, "the first batch is at most one split per lane");
+    constexpr int DPT = D / 64;    // dims per lane
+    constexpr int kBatch = 32;     // further accumulator rows loaded together
+    const int ms = a.max_splits;
+    const float *ml = a.ws_ml + row_id * ms * 2;
+    const float *acc = a.ws_acc + row_id * ms * D;
 
-    float mm = -INFINITY;
-    for (int s = lane; s < n; s += 64)
+    // Loads independent of the split count: (m, l) of splits 0..63 and the
+    // accumulator rows of splits 0..NF-1 (clamped to the row's max_splits
+    // slots).
+    const int first = ms < 64 ? (ms > 0 ? ms : 0) : 64;
+    float2 mlv = make_float2(-INFINITY, 0.0f);
+    if (lane < first)
+        mlv = *reinterpret_cast<const float2 *>(ml + 2 * lane);
+    float v0[NF][DPT];
+#pragma unroll
+    for (int j = 0; j < NF; ++j)
+#pragma unroll
+        for (int e = 0; e < DPT; ++e)
+            v0[j][e] = 0.0f;
+    if (first > 0) {
+#pragma unroll
+        for (int j = 0; j < NF; ++j) {
+            const int sj = j < first ? j : first - 1;
+#pragma unroll
+            for (int e = 0; e < DPT; ++e)
+                v0[j][e] = acc[(int64_t)sj * D + e * 64 + lane];
+        }
+    }
+    int n = count();
+    n = n < ms ? n : ms;  // the workspace holds max_splits states per row
+
+    const float m0 = lane < n ? mlv.x : -INFINITY;
+    const float l0 = lane < n ? mlv.y : 0.0f;
+    float mm = m0;
+    for (int s = lane + 64; s < n; s += 64)
         mm = fmaxf(mm, ml[2 * s]);
     for (int off = 32; off > 0; off >>= 1)
         mm = fmaxf(mm, __shfl_xor(mm, off));
     const float msafe = mm == -INFINITY ? 0.0f : mm;
-    float L = 0.0f;
-    for (int s = lane; s < n; s += 64)
+    const float f0 = fast_exp2(m0 - msafe);
+    float L = lane < n ? fmaf(l0, f0, 0.0f) : 0.0f;
+    for (int s = lane + 64; s < n; s += 64)
         L = fmaf(ml[2 * s + 1], fast_exp2(ml[2 * s] - msafe), L);
     for (int off = 32; off > 0; off >>= 1)
         L += __shfl_xor(L, off);
@@ -73,12 +110,41 @@ __device__ __forceinline__ void merge_row(const SplitArgs &a, int64_t row_id, in
 #pragma unroll
     for (int e = 0; e < DPT; ++e)
         o[e] = 0.0f;
-#pragma unroll 8
-    for (int s = 0; s < n; ++s) {
-        const float f = fast_exp2(ml[2 * s] - msafe);
+    // Splits 0..NF-1 from the registers loaded above.
 #pragma unroll
-        for (int e = 0; e < DPT; ++e)
-            o[e] = fmaf(acc[(int64_t)s * D + e * 64 + lane], f, o[e]);
+    for (int j = 0; j < NF; ++j) {
+        if (j < n) {
+            const float f = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(f0), j));
+#pragma unroll
+            for (int e = 0; e < DPT; ++e)
+                o[e] = fmaf(v0[j][e], f, o[e]);
+        }
+    }
+    // Further splits, 64 weights and kBatch rows at a time (the weights of
+    // splits below 64 are the f0 computed above).
+    for (int s0 = 0; s0 < n; s0 += 64) {
+        const float fl = s0 == 0 ? f0 : (s0 + lane < n ? fast_exp2(ml[2 * (s0 + lane)] - msafe) : 0.0f);
+        const int nb = n - s0 < 64 ? n - s0 : 64;
+        for (int b0 = s0 == 0 ? NF : 0; b0 < nb; b0 += kBatch) {
+            float v[kBatch][DPT];
+#pragma unroll
+            for (int j = 0; j < kBatch; ++j) {
+                // Past the last split the load repeats it (in bounds, unused).
+                const int s = s0 + (b0 + j < nb ? b0 + j : nb - 1);
+#pragma unroll
+                for (int e = 0; e < DPT; ++e)
+                    v[j][e] = acc[(int64_t)s * D + e * 64 + lane];
+            }
+#pragma unroll
+            for (int j = 0; j < kBatch; ++j) {
+                if (b0 + j < nb) {
+                    const float f = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(fl), b0 + j));
+#pragma unroll
+                    for (int e = 0; e < DPT; ++e)
+                        o[e] = fmaf(v[j][e], f, o[e]);
+                }
+            }
+        }
     }
     float *orow = a.out + row_id * D;
     if (L > 0.0f) {

@@ -79,7 +79,7 @@ enum {
     ATLAS_ERR_SHAPE = 2,       /* bad sizes, Hq % Hkv != 0 without head_map, bad head_map entry */
     ATLAS_ERR_RANGE = 3,       /* a size or count out of range (e.g. q_len > max context) */
     ATLAS_ERR_UNSUPPORTED = 4, /* no kernel for this dtype / head_dim / page size: never a silent fallback */
-    ATLAS_ERR_WORKSPACE = 5,   /* workspace smaller than the matching *_workspace_bytes() */
+    ATLAS_ERR_WORKSPACE = 5,   /* workspace smaller than the matching *_workspace_bytes(), or not 16-byte aligned */
     ATLAS_ERR_POOL = 6,        /* validation mode: a page id outside [0, num_phys_pages) */
     ATLAS_ERR_NONFINITE = 7,   /* validation mode: a NaN or Inf in the visible inputs */
     ATLAS_ERR_DEVICE = 8       /* a HIP runtime error */
@@ -123,7 +123,7 @@ typedef struct atlas_attn_args {
     const float *softcap;       /* device [B] or NULL; 0 = no softcap for that sequence */
     float *out;                 /* device */
     float *lse;                 /* device or NULL */
-    void *workspace;            /* device scratch, >= the matching *_workspace_bytes() */
+    void *workspace;            /* device scratch, >= the matching *_workspace_bytes(), 16-byte aligned */
     size_t workspace_bytes;
 } atlas_attn_args;
 

@@ -91,7 +91,8 @@ def _valid_args(**over):
     ("head_dim", 96, 4), ("page_size", 0, 2), ("page_size", 24, 4), ("page_size", 8192, 4),
     ("num_phys_pages", 0, 2), ("max_pages_per_seq", 0, 2), ("split_tokens", -1, 3),
     ("max_pages_per_seq", 1 << 30, 3), ("q", None, 1), ("page_table", None, 1),
-    ("out", None, 1), ("workspace_bytes", 16, 5), ("scale", float("inf"), 3), ("scale", 0.0, 3),
+    ("out", None, 1), ("workspace_bytes", 16, 5), ("workspace", FAKE + 8, 5), ("scale", float("inf"), 3),
+    ("scale", 0.0, 3),
     ("scale", -0.5, 3),
 ])
 def test_decode_rejects_bad_arguments_before_launch(field, value, status):
