@@ -101,6 +101,7 @@ struct Plan {
 constexpr size_t kWorkspaceHeader = 256;  // validation-mode flags live here
 constexpr int kDefaultSplitTokens = 4096; // keys per split-KV work item by default
 constexpr int kMinItems = 2048;           // fewest work items (8 per CU) before spans shrink
+constexpr int kFillItems = 512;           // work items (two per CU) below which row chunks shrink
 
 int32_t check_shapes(const atlas_attn_args *a, bool decode, Plan *p)
 {
@@ -234,6 +235,13 @@ int32_t check_shapes(const atlas_attn_args *a, bool decode, Plan *p)
     } else {
         while (rpi < rows_per_head && rpi < 8)
             rpi <<= 1;
+        // Few rows over short contexts: smaller row chunks spread the call
+        // over more CUs (each work item's fold is a serial chain of memory
+        // round trips and per-key vector work, so fewer rows per item finish
+        // sooner).  Counted at the shortest spans (64 keys).
+        const int64_t spans_min = (max_ctx + 63) / 64;
+        while (rpi > 1 && (int64_t)a->batch * hkv * ((rows_per_head + rpi - 1) / rpi) * spans_min < kFillItems)
+            rpi >>= 1;
     }
     p->rows_per_item = rpi;
     p->n_chunks = (int)((rows_per_head + rpi - 1) / rpi);
