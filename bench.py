@@ -84,6 +84,10 @@ def parse():
                     help="skip the per-call timing of the three smaller workloads")
     ap.add_argument("--workloads-only", action="store_true",
                     help="diagnostic: time only the three smaller workloads (for a kernel trace of them)")
+    ap.add_argument("--report-warmup", type=int, default=5,
+                    help="warm-up calls before each report's timed calls (at least)")
+    ap.add_argument("--report-warmup-s", type=float, default=0.1,
+                    help="warm-up seconds before each report's timed calls (at least; 0: count only)")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="kept for the recorded profiling commands: the plain 256 MiB device copy "
                          "(HBM counter calibration and context) now always runs")
@@ -159,10 +163,17 @@ def prefill_setup(torch, workloads, np):
     return dict(w=w, lay=lay, k=k, v=v, q=q, pt=pt, ctx=ctx, kl=kl, vl=vl)
 
 
-def _median_call_us(torch, np, fn, calls=30, warm=5, warm_s=0.1):
+# Warm-up before each report's timed calls: at least REPORT_WARMUP[0] calls
+# and REPORT_WARMUP[1] seconds of them (--report-warmup, --report-warmup-s).
+REPORT_WARMUP = [5, 0.1]
+
+
+def _median_call_us(torch, np, fn, calls=30, warm=None, warm_s=None):
     """Median HIP-event time of `calls` back-to-back calls, after at least
     `warm` calls and `warm_s` seconds of them (the clocks ramp back up after
     host-only set-up phases)."""
+    warm = REPORT_WARMUP[0] if warm is None else warm
+    warm_s = REPORT_WARMUP[1] if warm_s is None else warm_s
     t0 = time.perf_counter()
     n = 0
     while n < warm or time.perf_counter() - t0 < warm_s:
@@ -684,6 +695,7 @@ def prefill_cpu_baseline(p, out, np, oracle, heads_per_kv=1, edge=512):
 
 def main():
     args = parse()
+    REPORT_WARMUP[:] = [max(0, args.report_warmup), max(0.0, args.report_warmup_s)]
     if args.gpus != 1:
         print(json.dumps({"error": "this library runs on one GPU; --gpus must be 1 (no multi-GPU path)"}))
         sys.exit(2)
