@@ -8,6 +8,7 @@ raises -- there is no other implementation behind these names.
 """
 from __future__ import annotations
 
+import contextlib
 import ctypes
 import os
 
@@ -229,9 +230,22 @@ def _ptr(t):
     return None if t is None else ctypes.c_void_p(t.data_ptr())
 
 
-def _stream(stream):
+_raw_stream = getattr(torch._C, "_cuda_getCurrentRawStream", None)
+
+
+def _current_stream_handle(device_index):
+    """Handle of torch's current stream on a device (the raw handle, without
+    building a Stream object, where torch offers it)."""
+    if _raw_stream is not None:
+        return _raw_stream(device_index)
+    return torch.cuda.current_stream(device_index).cuda_stream
+
+
+def _stream(stream, device):
+    """The stream argument of a call on `device`: the given stream, else
+    torch's current stream of that device."""
     if stream is None:
-        stream = torch.cuda.current_stream()
+        return ctypes.c_void_p(_current_stream_handle(device.index))
     return ctypes.c_void_p(stream.cuda_stream)
 
 
@@ -240,7 +254,7 @@ def _check(t, name, dtype=None, device=None, ndim=None):
         raise TypeError(f"{name} must be a torch.Tensor")
     if not t.is_cuda:
         raise ValueError(f"{name} must be on the GPU")
-    if device is not None and t.device != device:
+    if device is not None and t.get_device() != device.index:
         raise ValueError(f"{name} is on {t.device}, expected {device}")
     if dtype is not None and t.dtype != dtype:
         raise ValueError(f"{name} has dtype {t.dtype}, expected {dtype}")
@@ -341,26 +355,36 @@ def _attend(entry, ws_fn, q, k_pages, v_pages, page_table, context_lens, scale, 
     # Buffers the binding allocates belong to the stream the call runs on:
     # torch's caching allocator may hand a freed block to the next allocation
     # of the stream it was allocated on, so a workspace allocated on another
-    # stream could be reused while the kernels still use it.
-    run_stream = torch.cuda.current_stream(q.device) if stream is None else stream
-    with torch.cuda.stream(run_stream):
+    # stream could be reused while the kernels still use it.  Without a
+    # stream argument the call runs on torch's current stream of q's device,
+    # where torch.empty allocates anyway.
+    if not q.is_cuda:
+        raise ValueError("q must be on the GPU")
+    dev = q.device
+    if stream is None:
+        handle = _current_stream_handle(dev.index)
+        alloc = contextlib.nullcontext()   # torch.empty on dev uses dev's current stream
+    else:
+        handle = stream.cuda_stream
+        alloc = torch.cuda.stream(stream)
+    need_ws = workspace is None
+    with alloc:
         if out is None:
-            out = torch.empty((B, q_len, hq, d), dtype=torch.float32, device=q.device)
+            out = torch.empty((B, q_len, hq, d), dtype=torch.float32, device=dev)
         if lse is None and want_lse:
-            lse = torch.empty((B, q_len, hq), dtype=torch.float32, device=q.device)
-    args, keep = make_attn_args(q, k_pages, v_pages, page_table, context_lens, scale, out=out,
-                                lse=lse, **kw)
-    if workspace is None:
-        need = ws_fn(args)
-        with torch.cuda.stream(run_stream):
-            workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=q.device)
+            lse = torch.empty((B, q_len, hq), dtype=torch.float32, device=dev)
+        args, keep = make_attn_args(q, k_pages, v_pages, page_table, context_lens, scale, out=out,
+                                    lse=lse, **kw)
+        if need_ws:
+            workspace = torch.empty(max(ws_fn(args), 1), dtype=torch.uint8, device=dev)
+    if need_ws:
         args.workspace = _ptr(workspace)
         args.workspace_bytes = workspace.numel()
     else:
-        _check(workspace, "workspace", None, q.device)
+        _check(workspace, "workspace", None, dev)
         args.workspace = _ptr(workspace)
         args.workspace_bytes = workspace.numel() * workspace.element_size()
-    st = getattr(lib, entry)(ctypes.byref(args), *extra, _stream(run_stream))
+    st = getattr(lib, entry)(ctypes.byref(args), *extra, ctypes.c_void_p(handle))
     if st != ATLAS_OK:
         raise AtlasError(st, entry)
     return out, lse
@@ -408,7 +432,7 @@ def atlas_attend_decode_noalloc(q, k_pages, v_pages, page_table, context_lens, s
     args, keep = make_attn_args(q, k_pages, v_pages, page_table, context_lens, scale, head_map=head_map,
                                 window=window, sink_tokens=sink_tokens, softcap=softcap, out=out, lse=lse,
                                 split_tokens=split_tokens)
-    st = lib.atlas_attend_decode_noalloc(ctypes.byref(args), _stream(stream))
+    st = lib.atlas_attend_decode_noalloc(ctypes.byref(args), _stream(stream, q.device))
     if st != ATLAS_OK:
         raise AtlasError(st, "atlas_attend_decode_noalloc")
     return out, lse
@@ -481,7 +505,7 @@ def atlas_regenerate_pages(k_pages, v_pages, jobs, seed: int, layer: int = 0, st
     a.num_jobs = n_jobs
     a.jobs = _ptr(jobs) if n_jobs else None
     a.k_pages, a.v_pages = _ptr(k_pages), _ptr(v_pages)
-    st = lib.atlas_regenerate_pages(ctypes.byref(a), _stream(stream))
+    st = lib.atlas_regenerate_pages(ctypes.byref(a), _stream(stream, k_pages.device))
     if st != ATLAS_OK:
         raise AtlasError(st, "atlas_regenerate_pages")
 
@@ -512,7 +536,7 @@ def atlas_append_kv(k_pages, v_pages, k_new, v_new, page_table, start_pos, strea
     a.k_new, a.v_new = _ptr(k_new), _ptr(v_new)
     a.page_table, a.start_pos = _ptr(page_table), _ptr(start_pos)
     a.k_pages, a.v_pages = _ptr(k_pages), _ptr(v_pages)
-    st = lib.atlas_append_kv(ctypes.byref(a), _stream(stream))
+    st = lib.atlas_append_kv(ctypes.byref(a), _stream(stream, k_pages.device))
     if st != ATLAS_OK:
         raise AtlasError(st, "atlas_append_kv")
 
