@@ -189,6 +189,37 @@ def _median_call_us(torch, np, fn, calls=30, warm=None, warm_s=None):
     return float(np.median(t.ms())) * 1000.0
 
 
+def _call_stats_us(torch, np, fn, calls=50):
+    """(median, min) HIP-event time in us of `calls` back-to-back calls after
+    the report warm-up."""
+    warm, warm_s = REPORT_WARMUP
+    t0 = time.perf_counter()
+    n = 0
+    while n < warm or time.perf_counter() - t0 < warm_s:
+        fn()
+        n += 1
+        if n % 4 == 0:
+            torch.cuda.synchronize()
+    torch.cuda.synchronize()
+    t = Timer(torch)
+    for _ in range(calls):
+        t(fn)
+    torch.cuda.synchronize()
+    ms = np.array(t.ms())
+    return float(np.median(ms)) * 1000.0, float(ms.min()) * 1000.0
+
+
+def _oracle_timed(run, min_seconds):
+    """Call run() until at least min_seconds of timed work; returns (calls, seconds)."""
+    n, secs = 0, 0.0
+    while secs < min_seconds or n == 0:
+        t0 = time.perf_counter()
+        run()
+        secs += time.perf_counter() - t0
+        n += 1
+    return n, secs
+
+
 def _c_abi_call_us(torch, np, entry, args, calls=30):
     """Median time of one C-ABI call with prepared arguments (outputs and
     workspace already set): what a native caller pays per call, without the
@@ -441,12 +472,15 @@ def append_report(torch, np, workloads, atlas):
     return rep
 
 
-def workload_report(torch, np, workloads, atlas):
-    """The three smaller synthetic workloads, each timed per call (median of
-    30 after 5 warm-up calls): single-head decode (all pages resident, and
-    all 8 pages regenerated inside the call), the GQA short-query suffix
-    attention, and the mixed-length decode with window / sinks / softcap on
-    even sequences."""
+def workload_report(torch, np, workloads, atlas, oracle=None):
+    """The three smaller synthetic workloads, each timed per call (median and
+    minimum of 50 after the report warm-up): single-head decode (all pages
+    resident, and all 8 pages regenerated inside the call), the GQA
+    short-query suffix attention, and the mixed-length decode with window /
+    sinks / softcap on even sequences.  With the oracle module given, each
+    also gets a cpu_baseline: the oracle timed on the same inputs (the whole
+    workload, or a stated sample) in the workload's unit, checking the GPU
+    output it covers."""
     rep = {}
     # Single-head decode: 2 MiB of K/V, launch-latency bound.
     w = workloads.make("single_head_decode")
@@ -473,10 +507,13 @@ def workload_report(torch, np, workloads, atlas):
                 atlas.atlas_regenerate_pages(k, v, cold, seed=w.seed, layer=w.layer)
             return atlas.atlas_attend_decode(q, k, v, pt, ctx, w.scale, out=out, lse=lse, workspace=ws)[0]
         r = rep.setdefault("single_head_decode", {})
-        r[f"{mode}_us"] = round(_median_call_us(torch, np, call), 2)
+        med, mn = _call_stats_us(torch, np, call)
+        r[f"{mode}_us"], r[f"{mode}_us_min"] = round(med, 2), round(mn, 2)
         if mode == "resident":
             r["c_abi_us"] = round(_c_abi_call_us(torch, np, "atlas_attend_decode", atlas.make_attn_args(
-                q, k, v, pt, ctx, w.scale, out=out, lse=lse, workspace=ws)[0]), 2)
+                q, k, v, pt, ctx, w.scale, out=out, lse=lse, workspace=ws)[0], calls=50), 2)
+            if oracle is not None:
+                r["cpu_baseline"] = _oracle_single_head(w, q, out, np, oracle)
     kvb = int(w.context_lens.sum()) * w.hkv * w.head_dim * 4 * 2
     us = rep["single_head_decode"]["resident_us"]
     rep["single_head_decode"].update({"kv_bytes": kvb, "GBs": round(kvb / us / 1e3, 1),
@@ -496,15 +533,17 @@ def workload_report(torch, np, workloads, atlas):
     pargs, _ = atlas.make_attn_args(q, k, v, pt, ctx, w.scale)
     ws = torch.empty(max(1, atlas.atlas_prefill_workspace_bytes(pargs)), dtype=torch.uint8, device="cuda")
     call = lambda: atlas.atlas_attend_prefill(q, k, v, pt, ctx, w.scale, out=out, lse=lse, workspace=ws)[0]
-    us = _median_call_us(torch, np, call)
+    us, us_min = _call_stats_us(torch, np, call)
     c_us = _c_abi_call_us(torch, np, "atlas_attend_prefill", atlas.make_attn_args(
-        q, k, v, pt, ctx, w.scale, out=out, lse=lse, workspace=ws)[0])
+        q, k, v, pt, ctx, w.scale, out=out, lse=lse, workspace=ws)[0], calls=50)
     L = int(w.context_lens[0])
     pairs = w.hq * sum(L - w.q_len + i + 1 for i in range(w.q_len))
-    rep["gqa_short_query"] = {"us": round(us, 2), "c_abi_us": round(c_us, 2),
+    rep["gqa_short_query"] = {"us": round(us, 2), "us_min": round(us_min, 2), "c_abi_us": round(c_us, 2),
                               "kv_bytes": L * w.hkv * w.head_dim * 4 * 2,
                               "flop": 4 * w.head_dim * pairs,
                               "note": "latency bound (256 KiB of K/V); us per Python call, host overhead included; c_abi_us: one C-ABI call with prepared arguments"}
+    if oracle is not None:
+        rep["gqa_short_query"]["cpu_baseline"] = _oracle_short_query(w, lay, q, k, v, out, np, oracle, pairs)
     del k, v
     # Mixed-length decode with window / sinks / softcap on even sequences.
     w = workloads.make("mixed_decode")
@@ -516,19 +555,101 @@ def workload_report(torch, np, workloads, atlas):
     opt = lambda a, t: torch.from_numpy(a.astype(t)).cuda()
     win, snk, cap = opt(w.window, np.int32), opt(w.sinks, np.int32), opt(w.softcap, np.float32)
     out = torch.empty(workloads.query_shape(w), dtype=torch.float32, device="cuda")
-    us = _median_call_us(torch, np, lambda: atlas.atlas_attend_decode(
+    us, us_min = _call_stats_us(torch, np, lambda: atlas.atlas_attend_decode(
         q, k, v, pt, ctx, w.scale, window=win, sink_tokens=snk, softcap=cap, out=out))
     Ls = w.context_lens.astype(np.int64)
     Ws = w.window.astype(np.int64)
     Ss = w.sinks.astype(np.int64)
     vis = np.where(Ws > 0, np.minimum(Ws, Ls) + np.minimum(Ss, np.maximum(Ls - Ws, 0)), Ls)
     kvb = int(vis.sum()) * w.hkv * w.head_dim * 2 * 2
-    rep["mixed_decode"] = {"us": round(us, 1), "kv_bytes": kvb, "GBs": round(kvb / us / 1e3, 1),
-                           "frac_hbm": round(kvb / us / 1e3 / HBM_PEAK_GBS, 4),
+    rep["mixed_decode"] = {"us": round(us, 1), "us_min": round(us_min, 1), "kv_bytes": kvb,
+                           "GBs": round(kvb / us / 1e3, 1), "frac_hbm": round(kvb / us / 1e3 / HBM_PEAK_GBS, 4),
                            "note": "visible-key bytes (window + sinks on even sequences)"}
+    if oracle is not None:
+        rep["mixed_decode"]["cpu_baseline"] = _oracle_mixed_decode(torch, w, lay, q, k, v, out, vis, np, oracle)
     del k, v
     torch.cuda.empty_cache()
     return rep
+
+
+def _oracle_single_head(w, q, out, np, oracle, min_seconds=1.0):
+    """The oracle on the whole single-head decode (4096 keys, K/V from its own
+    generator, generation untimed), in KV GB/s."""
+    L = int(w.context_lens[0])
+    k = np.stack([oracle.regen_rows(w.seed, w.layer, 0, oracle.TENSOR_K, h, 0, L, w.head_dim) for h in range(w.hkv)])
+    v = np.stack([oracle.regen_rows(w.seed, w.layer, 0, oracle.TENSOR_V, h, 0, L, w.head_dim) for h in range(w.hkv)])
+    qh = q[0].cpu().numpy()
+    hm = oracle.default_head_map(w.hq, w.hkv)
+    pos = np.array([L - 1], np.int32)
+    ro, _ = oracle.attend(qh, k, v, pos, hm, w.scale)
+    err = np.abs(out[0].cpu().numpy().astype(np.float64) - ro)
+    if not np.all(err <= 2e-5 + 1e-4 * np.abs(ro)):
+        raise SystemExit(f"bench: GPU single-head decode disagrees with the oracle (max err {err.max():.3e})")
+    n, secs = _oracle_timed(lambda: oracle.attend(qh, k, v, pos, hm, w.scale), min_seconds)
+    kvb = k.nbytes + v.nbytes
+    return {"value": round(n * kvb / secs / 1e9, 3), "unit": "GB/s", "cores": oracle.num_threads(),
+            "cpu_model": _cpu_model(), "kind": "oracle",
+            "sample": f"whole workload (1 row x {L} keys, {kvb / 2**20:.0f} MiB fp32 K/V) x {n} calls, "
+                      f"{secs:.2f} s timed; K/V generation untimed; GPU output agreed (max abs err {err.max():.2e})"}
+
+
+def _oracle_short_query(w, lay, q, k_dev, v_dev, out, np, oracle, pairs, min_seconds=1.0):
+    """The oracle on the whole GQA short query (K/V read back from the arena
+    through the page table), in GFLOP/s over the visible pairs."""
+    L = int(w.context_lens[0])
+    k = oracle.gather_pages(k_dev.cpu().numpy(), lay.page_table[0], L, w.page_size)
+    v = oracle.gather_pages(v_dev.cpu().numpy(), lay.page_table[0], L, w.page_size)
+    qh = q[0].cpu().numpy()
+    hm = oracle.default_head_map(w.hq, w.hkv)
+    pos = np.arange(L - w.q_len, L, dtype=np.int32)
+    ro, _ = oracle.attend(qh, k, v, pos, hm, w.scale)
+    err = np.abs(out[0].cpu().numpy().astype(np.float64) - ro)
+    if not np.all(err <= 2e-5 + 1e-4 * np.abs(ro)):
+        raise SystemExit(f"bench: GPU short-query output disagrees with the oracle (max err {err.max():.3e})")
+    n, secs = _oracle_timed(lambda: oracle.attend(qh, k, v, pos, hm, w.scale), min_seconds)
+    flop = 4.0 * w.head_dim * pairs
+    return {"value": round(n * flop / secs / 1e9, 3), "unit": "GFLOP/s", "cores": oracle.num_threads(),
+            "cpu_model": _cpu_model(), "kind": "oracle",
+            "sample": f"whole workload ({w.q_len} queries x {w.hq} q-heads over {L} keys, {flop / 1e6:.2f} MFLOP) "
+                      f"x {n} calls, {secs:.2f} s timed; GPU output agreed (max abs err {err.max():.2e})"}
+
+
+def _oracle_mixed_decode(torch, w, lay, q, k_dev, v_dev, out, vis, np, oracle, seqs=(0, 1, 2, 3),
+                         min_seconds=1.0):
+    """The oracle on a sample of the mixed-length decode (sequences `seqs`:
+    windowed and plain ones), K/V read back from the arena through the page
+    table, in KV GB/s over those sequences' visible-key bytes (bf16, as the
+    GPU figure counts them)."""
+    P, D = w.page_size, w.head_dim
+    hm = oracle.default_head_map(w.hq, w.hkv)
+    o = out.cpu().numpy()
+    qh = q.float().cpu().numpy()
+    secs, kvb, max_err, lens = 0.0, 0, 0.0, []
+    for b in seqs:
+        L = int(w.context_lens[b])
+        n_pages = (L + P - 1) // P
+        ids = torch.from_numpy(lay.page_table[b, :n_pages].astype(np.int64)).cuda()
+        k = k_dev.index_select(0, ids).float().permute(1, 0, 2, 3).reshape(w.hkv, n_pages * P, D)[:, :L]
+        v = v_dev.index_select(0, ids).float().permute(1, 0, 2, 3).reshape(w.hkv, n_pages * P, D)[:, :L]
+        k, v = np.ascontiguousarray(k.cpu().numpy()), np.ascontiguousarray(v.cpu().numpy())
+        win, snk, cap = int(w.window[b]), int(w.sinks[b]), float(w.softcap[b])
+        pos = np.array([L - 1], np.int32)
+        ro, _ = oracle.attend(qh[b], k, v, pos, hm, w.scale, win, snk if win > 0 else 0, cap)
+        err = np.abs(o[b].astype(np.float64) - ro)
+        if not np.all(err <= 2e-3):
+            raise SystemExit(f"bench: GPU mixed decode disagrees with the oracle (seq {b}, max err {err.max():.3e})")
+        max_err = max(max_err, float(err.max()))
+        n, t = _oracle_timed(lambda: oracle.attend(qh[b], k, v, pos, hm, w.scale, win, snk if win > 0 else 0, cap),
+                             min_seconds / len(seqs))
+        secs += t / n
+        kvb += int(vis[b]) * w.hkv * D * 2 * 2
+        lens.append(L)
+        del k, v
+    return {"value": round(kvb / secs / 1e9, 3), "unit": "GB/s", "cores": oracle.num_threads(),
+            "cpu_model": _cpu_model(), "kind": "oracle",
+            "sample": f"sequences {list(seqs)} of 64 (lengths {lens}; even ones windowed), "
+                      f"{kvb / 1e6:.1f} MB of visible bf16 K/V per pass, each timed over >= "
+                      f"{min_seconds / len(seqs):.2f} s; GPU outputs agreed (max abs err {max_err:.2e})"}
 
 
 def cpu_baseline(d, out, np, oracle, min_seconds=3.0):
@@ -850,7 +971,10 @@ def main():
     if not args.no_workloads:
         # Every synthetic workload's throughput (the long-context decode and
         # the prefill are the step's own figures above).
-        wl = workload_report(torch, np, workloads, atlas)
+        wl_oracle = None
+        if not args.no_cpu_baseline:
+            import oracle as wl_oracle
+        wl = workload_report(torch, np, workloads, atlas, oracle=wl_oracle)
         wl["long_context_decode"] = {"us": round(dec_ms * 1000.0, 1), "kv_bytes": kv_bytes,
                                      "GBs": round(dec_gbs, 1), "frac_hbm": round(dec_gbs / HBM_PEAK_GBS, 4),
                                      "regen_us": round(regen_ms * 1000.0, 1)}
