@@ -14,7 +14,9 @@
 //                blocks before the lowest row's window start are skipped
 //                (except the blocks holding the sink keys); only blocks some
 //                row does not see whole apply the per-row mask; a softcap is
-//                applied to the scores before the mask;
+//                applied to the scores before the mask, each score carried
+//                as -1/(1 + 2^(k s)) (ordered like the capped logit) with the
+//                cap's affine map folded into the exponent's FMA;
 //   per wave   = 32 rows.  S^T = K Q^T on v_mfma_f32_32x32x16_bf16 (A = K
 //                from LDS, B = Q held in registers), so each lane owns one
 //                row's scores and the row max is lane-local plus one swap
@@ -39,10 +41,16 @@
 //
 // Modifications (MODS instances, atlas_attend_mods): non-causal rows take
 // every key block of the context, with only the block past the last key
-// masked; an ALiBi slope adds -slope |pos - j| (as -slope/scale |pos - j| in
-// the units of the raw product, after the softcap) and mask bits hide keys
-// per (row, key), both applied per element in every block (each lane loads
-// the two mask words of its row for the block ahead of the QK products).
+// masked.  Mask bits hide keys per (row, key): a pass over the workgroup's
+// mask rows lists the key blocks some row sees and marks those every row
+// sees whole, which skip the per-score mask bits; the others load each
+// lane's two mask words one block ahead, with the block's K/V.  An ALiBi
+// slope adds -slope |pos - j| (as -slope/scale |pos - j| in the units of the
+// raw product, after the softcap): one FMA per score for the per-key part,
+// the per-row part folded into the row max and the exponent's offset; the
+// key blocks then run outward from the diagonal (leftwards, then rightwards
+// for non-causal rows), so the first block holds nearly the row max and the
+// accumulator is seldom rescaled.
 //
 // Precondition of the fp16 P.V product: |V| <= 65504 (validation mode
 // checks it).  Scores use bf16 K and Q exactly (products are exact in fp32).
