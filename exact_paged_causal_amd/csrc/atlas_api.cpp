@@ -200,10 +200,12 @@ int32_t check_shapes(const atlas_attn_args *a, bool decode, Plan *p)
     if (p->path == Path::TiledPrefill || p->path == Path::TiledSplit) {
         // Key splits when the grid would not fill the chip once (fewer
         // workgroups than CUs, e.g. a short prefill chunk behind a long
-        // history): aim at about four per CU, at least 8 key blocks (512
-        // keys) per split, partial states within 1 GiB.  A full round (one
-        // 512-thread workgroup per CU) runs unsplit: measured, splitting it
-        // only adds the partial-state traffic.
+        // history): aim at about one round (one 512-thread workgroup per
+        // CU), at least 8 key blocks (512 keys) per split, partial states
+        // within 1 GiB.  Measured: four rounds of shorter runs spent a third
+        // of a 128-query chunk's time writing and merging partial states
+        // (139 against 90 us); a full round runs unsplit, since splitting it
+        // only adds that traffic.
         p->workspace = kWorkspaceHeader;
         p->tiled_npos = 256 / gmax;
         const int64_t n_qblocks = (a->q_len + p->tiled_npos - 1) / p->tiled_npos;
@@ -212,7 +214,7 @@ int32_t check_shapes(const atlas_attn_args *a, bool decode, Plan *p)
         p->split_blocks = 0;
         p->max_splits = 1;
         if (wgs < 256 && max_blocks > 16) {
-            const int64_t want = (1024 + wgs - 1) / wgs;
+            const int64_t want = (256 + wgs - 1) / wgs;
             int64_t sb = std::max<int64_t>(8, (max_blocks + want - 1) / want);
             const int64_t per_split = rows * (int64_t)(a->head_dim + 2) * 4;
             while ((max_blocks + sb - 1) / sb > 1 && per_split * ((max_blocks + sb - 1) / sb) > (INT64_C(1) << 30))
