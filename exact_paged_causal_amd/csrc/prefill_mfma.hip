@@ -245,13 +245,6 @@ __global__ __launch_bounds__(512) void prefill_kernel(PrefillArgs a)
     for (int t = 0; t < DT; ++t)
         acc[t] = f32x16{};
 
-    // Complete the query loads here, once: the asm "redefines" qf, so inside
-    // the loop the compiler knows no load into qf is pending and does not wait
-    // on the (prefetch) load counter before the first QK product.
-#pragma unroll
-    for (int s = 0; s < KS; ++s)
-        asm volatile("" : "+v"(qf[s]));
-
     // Key blocks the rows can see: with a window, the sink blocks and then
     // the blocks from the lowest row's window start to the diagonal (blocks
     // in between are skipped); otherwise every block up to the diagonal.
@@ -373,6 +366,13 @@ __global__ __launch_bounds__(512) void prefill_kernel(PrefillArgs a)
         fetch(run_block(0));
         stash(0);
     }
+    // Complete the query loads here, once, after the page ids and the first
+    // block's K/V were requested beside them: the asm "redefines" qf, so
+    // inside the loop the compiler knows no load into qf is pending and does
+    // not wait on the (prefetch) load counter before the first QK product.
+#pragma unroll
+    for (int s = 0; s < KS; ++s)
+        asm volatile("" : "+v"(qf[s]));
     __syncthreads();
 
     for (int it = 0; it < n_run; ++it) {
