@@ -63,6 +63,7 @@ constexpr int kBN = 64;                // keys per block
 constexpr int kPad = 24;               // row padding (elements): a 16-byte-odd row stride
 constexpr float kRescaleSlack = 8.0f;  // log2 units the running max may lag
 constexpr int kPidWindow = 1024;       // page ids staged in LDS at a time
+constexpr int kMaxListed = 1024;       // candidate key blocks a mask can thin out (longer: all computed)
 
 template <int D>
 struct alignas(16) SplitSmem {
@@ -193,6 +194,8 @@ __global__ __launch_bounds__(512) void prefill_split_kernel(PrefillArgs a)
 
     int pid_base = 0;
     auto stage_pids = [&](int first_page) {
+        if (MODS && first_page < 0)
+            first_page = 0;
         pid_base = first_page;
         const int last_page = key_hi >= 0 ? key_hi >> ps : -1;
         for (int t = tid; t < kPidWindow && first_page + t <= last_page; t += 512) {
@@ -290,31 +293,125 @@ __global__ __launch_bounds__(512) void prefill_split_kernel(PrefillArgs a)
     }
     auto block_at = [&](int it) { return tiled_block_at(tbk, c_lo + it); };
 
-    if (n_iter > 0)
-        stage_pids((block_at(0) * kBN) >> ps);
-    __syncthreads();
-    if (n_iter > 0) {
-        fetch(kpages, block_at(0));
+    // MODS with mask bits: the candidate blocks whose mask words are zero for
+    // every row of this workgroup are dropped; the rest are listed in order
+    // (wave 0 compacts the flags with a ballot) by their index in the
+    // candidate run, each marked full when every row's 64 bits are set (its
+    // mask bits are then not applied per score).  The tests are
+    // conservative: a listed block may still be wholly hidden by the causal
+    // or window rule.  The flags live in the V tile buffer until the first
+    // block is staged; the list (16-bit entries: index * 2 + partial) in
+    // LDS of its own.
+    __shared__ uint16_t s_lst[MODS ? kMaxListed : 1];
+    __shared__ int32_t s_count;
+    __shared__ int32_t s_pivot;
+    const bool alibi_on = MODS && a.mods.alibi != nullptr;
+    int n_run = n_iter;
+    bool listed = false;
+    // ALiBi: listed blocks whose first key is at or left of the last row's
+    // position (the blocks run outward from the diagonal, see below).
+    const int kb_diag = pos_hi >= 0 ? pos_hi / kBN : -1;
+    int n_left = 0;
+    if constexpr (MODS) {
+        if (a.mods.mask && n_iter > 0 && n_iter <= kMaxListed) {
+            listed = true;
+            uint8_t *s_need = reinterpret_cast<uint8_t *>(&sm.vl[0][0][0]);
+            uint8_t *s_part = s_need + kMaxListed;
+            static_assert(sizeof(sm.vl) >= 2 * kMaxListed, "block flags fit the V lo buffer");
+            for (int i = tid; i < n_iter; i += 512) {
+                s_need[i] = 0;
+                s_part[i] = 0;
+            }
+            __syncthreads();
+            const int rows_pos = i1 - i0;
+            const int wl = a.mods.mask_words - 1;
+            for (int idx = tid; idx < n_iter * rows_pos; idx += 512) {
+                const int pp = idx / n_iter;
+                const int c = idx - pp * n_iter;
+                const uint32_t *m = a.mods.mask + ((int64_t)b * a.q_len + i0 + pp) * a.mods.mask_words;
+                const int w = (block_at(c) * kBN) >> 5;
+                const uint32_t m0 = m[w < wl ? w : wl];
+                const uint32_t m1 = m[w + 1 < wl ? w + 1 : wl];
+                if ((m0 | m1) != 0u)
+                    s_need[c] = 1;
+                if ((m0 & m1) != ~0u || w + 1 > wl)
+                    s_part[c] = 1;
+            }
+            __syncthreads();
+            if (wave == 0) {
+                int base = 0, left = 0;
+                for (int c0 = 0; c0 < n_iter; c0 += 64) {
+                    const int c = c0 + lane;
+                    const bool f = c < n_iter && s_need[c];
+                    const uint64_t bal = __ballot(f);
+                    if (f)
+                        s_lst[base + __popcll(bal & ((1ull << lane) - 1ull))] = (uint16_t)(c * 2 + s_part[c]);
+                    base += __popcll(bal);
+                    left += __popcll(__ballot(f && block_at(c) <= kb_diag));
+                }
+                if (lane == 0) {
+                    s_count = base;
+                    s_pivot = left;
+                }
+            }
+            __syncthreads();
+            n_run = s_count;
+            n_left = s_pivot;
+        } else {
+            // Entries of this run of the ascending list at or left of kb_diag.
+            int le = kb_diag < 0 ? 0
+                     : kb_diag < tbk.n_sink ? kb_diag + 1
+                                            : tbk.n_sink + (kb_diag - tbk.first_win + 1);
+            le = le < tbk.n_sink ? (kb_diag < tbk.n_sink ? le : tbk.n_sink) : (le > tbk.n ? tbk.n : le);
+            le -= c_lo;
+            n_left = le < 0 ? 0 : (le > n_iter ? n_iter : le);
+        }
+    }
+    // Block order.  With ALiBi the bias falls with the distance from the
+    // row, so the blocks run from the diagonal leftwards and then rightwards
+    // (non-causal rows): the first block holds (nearly) the row max and the
+    // accumulator is rarely rescaled; forward otherwise.
+    const int d_last = alibi_on ? n_left - 1 : -1;
+    auto list_at = [&](int it) { return (MODS && it <= d_last) ? d_last - it : it; };
+    auto run_block = [&](int it) {
+        const int i = list_at(it);
+        return block_at((MODS && listed) ? s_lst[i] >> 1 : i);
+    };
+    auto is_partial = [&](int it) { return !(MODS && listed) || (s_lst[list_at(it)] & 1); };
+    // First page to stage for block kb when the walk goes backwards from it.
+    auto back_first = [&](int kbx) { return ((kbx * kBN + kBN - 1) >> ps) - kPidWindow + 1; };
+
+    if (n_run > 0)
+        stage_pids(d_last >= 0 ? back_first(run_block(0)) : (run_block(0) * kBN) >> ps);
+    __syncthreads();  // page ids staged; block flags no longer read
+    if (n_run > 0) {
+        fetch(kpages, run_block(0));
         stash(sm.kh[0], sm.kl[0], sm.kscale[0]);
-        fetch(vpages, block_at(0));
+        fetch(vpages, run_block(0));
         stash(sm.vh[0], sm.vl[0], nullptr);
     }
     __syncthreads();
 
-    for (int it = 0; it < n_iter; ++it) {
-        const int kb = block_at(it);
+    for (int it = 0; it < n_run; ++it) {
+        const int kb = run_block(it);
         const int cur = it & 1;
-        const bool more = it + 1 < n_iter;
-        const int kb_next = more ? block_at(it + 1) : kb;
-        if (more && (((kb_next * kBN + kBN - 1) >> ps) - pid_base) >= kPidWindow) {
+        const bool more = it + 1 < n_run;
+        const int kb_next = more ? run_block(it + 1) : kb;
+        if (more && ((((kb_next * kBN + kBN - 1) >> ps) - pid_base) >= kPidWindow ||
+                     (MODS && ((kb_next * kBN) >> ps) < pid_base))) {
+            // Uniform across the workgroup: move the page-id window.
             __syncthreads();
-            stage_pids((kb_next * kBN) >> ps);
+            stage_pids((MODS && kb_next < kb) ? back_first(kb_next) : (kb_next * kBN) >> ps);
             __syncthreads();
         }
         if (more)
             fetch(kpages, kb_next);
+        // MODS: the row's mask words for the block's two 32-key tiles (words
+        // past the row's end hold keys beyond every context and are
+        // clamped); full blocks need none.
+        const bool part = is_partial(it);
         uint32_t mw0 = ~0u, mw1 = ~0u;
-        if (MODS && mrow) {
+        if (MODS && mrow && part) {
             const int w = (kb * kBN) >> 5;
             const int wl = a.mods.mask_words - 1;
             mw0 = mrow[w < wl ? w : wl];
@@ -421,7 +518,7 @@ __global__ __launch_bounds__(512) void prefill_split_kernel(PrefillArgs a)
         // every block).
         const bool all_causal = k0 + kBN - 1 <= (causal ? pos_lo : key_hi);
         const bool all_window = W <= 0 || k0 > pos_hi - W || k0 + kBN - 1 < S;
-        if (!(all_causal && all_window) || (MODS && mrow)) {
+        if (!(all_causal && all_window) || (MODS && mrow && part)) {
 #pragma unroll
             for (int t = 0; t < 2; ++t)
 #pragma unroll

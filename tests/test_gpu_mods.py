@@ -129,6 +129,10 @@ CASES = [
     ("bf16", 4, 1, 64, 1, 3000, (3000,), False, True, None),
     ("bf16", 4, 1, 64, 1, 64, (3000,), True, True, 0.9),
     ("bf16", 4, 1, 64, 1, 1000, (3000,), False, True, 0.9),
+    ("f32", 4, 1, 64, 1, 64, (3000,), True, True, None),
+    ("f32", 4, 1, 64, 1, 3000, (3000,), False, True, None),
+    ("f32", 4, 1, 64, 1, 64, (3000,), True, True, 0.9),
+    ("f32", 4, 1, 64, 1, 1000, (3000,), False, True, 0.9),
 ]
 
 
@@ -186,20 +190,21 @@ def test_no_op_mods_equal_the_plain_call(dtype, q_len):
     assert torch.equal(o1, o2) and torch.equal(l1, l2)
 
 
-@pytest.mark.parametrize("causal", [True, False])
-def test_mods_causal_prefill_full_size(causal):
-    """The causal-prefill shape (S=8192, Hq=32, Hkv=8, D=128, bf16) with ALiBi
-    slopes, causal and non-causal: every row of one seeded q-head per K/V
-    head, and the first and last 512 rows of every q-head."""
-    w = workloads.make("causal_prefill")
-    say(f"[mods] causal_prefill shape with ALiBi, causal={causal}")
+@pytest.mark.parametrize("dtype,causal", [("bf16", True), ("bf16", False), ("f32", True)])
+def test_mods_causal_prefill_full_size(dtype, causal):
+    """The causal-prefill shape (S=8192, Hq=32, Hkv=8, D=128; bf16, and fp32
+    on the split-operand kernel) with ALiBi slopes, causal and non-causal:
+    every row of one seeded q-head per K/V head, and the first and last 512
+    rows of every q-head."""
+    w = workloads.make("causal_prefill", dtype=dtype)
+    say(f"[mods] causal_prefill shape with ALiBi, {dtype} causal={causal}")
     inp = H.build(w)
     slopes = alibi_slopes(w.hq)
     out, lse = run_mods(inp, causal, slopes, None)
     torch.cuda.synchronize()
     for rows, heads in H.full_size_blocks(w, seed=2):
         say(f"[mods] oracle on {len(rows)} rows x heads {heads.tolist()}")
-        check_mods(inp, out, lse, causal, slopes, None, f"full size causal={causal}", rows=rows, heads=heads)
+        check_mods(inp, out, lse, causal, slopes, None, f"full size {dtype} causal={causal}", rows=rows, heads=heads)
     assert not torch.isnan(out).any()
 
 
@@ -225,14 +230,16 @@ def test_block_sparse_document_mask(dtype):
     check_mods(inp, out, lse, True, None, mask, f"document mask {dtype}")
 
 
-def test_document_mask_full_size():
-    """The causal-prefill shape (S=8192, Hq=32, Hkv=8, D=128, bf16) packed with
-    four documents of 2048 tokens (a causal block-diagonal mask, as the
-    benchmark runs it): key blocks inside a document are wholly visible to a
-    query block's rows and skip the per-score mask.  Every row of one seeded
-    q-head per K/V head, and the first and last 512 rows of every q-head."""
-    w = workloads.make("causal_prefill")
-    say("[mods] causal_prefill shape with a 4 x 2048 document mask")
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+def test_document_mask_full_size(dtype):
+    """The causal-prefill shape (S=8192, Hq=32, Hkv=8, D=128; bf16, and fp32
+    on the split-operand kernel) packed with four documents of 2048 tokens (a
+    causal block-diagonal mask, as the benchmark runs it): key blocks inside
+    a document are wholly visible to a query block's rows and skip the
+    per-score mask.  Every row of one seeded q-head per K/V head, and the
+    first and last 512 rows of every q-head."""
+    w = workloads.make("causal_prefill", dtype=dtype)
+    say(f"[mods] causal_prefill shape with a 4 x 2048 document mask, {dtype}")
     inp = H.build(w)
     L = int(inp.layout.page_table.shape[1]) * w.page_size
     j = np.arange(L)
@@ -242,5 +249,27 @@ def test_document_mask_full_size():
     torch.cuda.synchronize()
     for rows, heads in H.full_size_blocks(w, seed=3):
         say(f"[mods] oracle on {len(rows)} rows x heads {heads.tolist()}")
-        check_mods(inp, out, lse, True, None, mask, "document mask full size", rows=rows, heads=heads)
+        check_mods(inp, out, lse, True, None, mask, f"document mask full size {dtype}", rows=rows, heads=heads)
+    assert not torch.isnan(out).any()
+
+
+def test_mask_past_the_listing_capacity_f32():
+    """fp32 tiled prefill with mask bits over more candidate key blocks than a
+    workgroup lists (1024 blocks of 64 keys): 8192 queries at the end of a
+    67000-token context, one q-head per K/V head (256 positions per
+    workgroup, 256 workgroups, no key splits), documents of 20000 tokens with
+    causal rows.  The first query blocks list their blocks; the later ones
+    compute every candidate block under the per-score mask.  Rows around the
+    document boundary and at both ends, every q-head."""
+    w = wl("f32", 8, 8, 64, 128, 8192, (67000,), seed=43)
+    say("[mods] fp32 mask past the listing capacity: ctx 67000, q_len 8192")
+    inp = H.build(w)
+    L = int(inp.layout.page_table.shape[1]) * w.page_size
+    j = np.arange(L)
+    pos = 67000 - w.q_len + np.arange(w.q_len)
+    mask = ((j[None, :] // 20000 == pos[:, None] // 20000) & (j[None, :] <= pos[:, None]))[None]
+    out, lse = run_mods(inp, True, None, mask)
+    torch.cuda.synchronize()
+    rows = np.r_[0:40, 60000 - int(pos[0]) - 40:60000 - int(pos[0]) + 40, w.q_len - 60:w.q_len]
+    check_mods(inp, out, lse, True, None, mask, "mask past the listing capacity", rows=rows)
     assert not torch.isnan(out).any()
