@@ -22,8 +22,8 @@ kernel (atlas_attend_decode_regen) instead of regenerated into scratch
 step's); the K/V append of a decode step and of a whole prefill history is
 timed under "next": "append_kv", the prefill shape with a window, sinks
 and a softcap under "next": "prefill_variants", and the same shape with
-fp32 Q/K/V (split fp16 operands on the matrix cores) under
-"next": "prefill_f32", and atlas_attend_mods on the same bf16 shape (ALiBi
+fp32 Q/K/V (split fp16 operands on the matrix cores, plain and with
+ALiBi or a document mask) under "next": "prefill_f32", and atlas_attend_mods on the same bf16 shape (ALiBi
 causal and non-causal, a block-diagonal document mask) under "next": "mods";
 the long-context decode through the hot-page cache (atlas_cache_plan ->
 regenerate admitted pages -> decode with the rest generated in the kernel)
@@ -302,11 +302,23 @@ def prefill_variants_report(torch, np, p, atlas, calls=10):
             "note": "window 4096 + 4 sinks + softcap 50 on the causal-prefill shape; visible pairs only"}
 
 
+def _document_mask(torch, np, S, words, doc=2048):
+    """Packed causal block-diagonal mask of S query rows over words * 32 keys:
+    documents of `doc` tokens, query i at position i."""
+    j = np.arange(words * 32)
+    qpos = np.arange(S)
+    keep = (j[None, :] // doc == qpos[:, None] // doc) & (j[None, :] <= qpos[:, None])
+    bits = np.packbits(keep, axis=-1, bitorder="little").view("<u4").astype(np.uint32).view(np.int32)
+    return torch.from_numpy(np.ascontiguousarray(bits)[None]).cuda()
+
+
 def prefill_f32_report(torch, np, workloads, atlas, calls=10):
     """The causal-prefill shape (S=8192, Hq=32, Hkv=8, D=128, pages of 128)
     with fp32 Q/K/V: the tiled kernel on split fp16 operands.  TFLOP/s counts
     the method's 4 D flop per (q-head, visible pair); each of its products
-    issues three fp16 matrix products, so the matrix cores run 3x that."""
+    issues three fp16 matrix products, so the matrix cores run 3x that.  The
+    same shape through atlas_attend_mods: ALiBi on causal rows, and four
+    2048-token documents under a causal block-diagonal mask."""
     w = workloads.make("causal_prefill", dtype="f32")
     lay = workloads.page_layout(w)
     k, v = _arena(torch, workloads, np, w, lay)
@@ -320,9 +332,20 @@ def prefill_f32_report(torch, np, workloads, atlas, calls=10):
     S = w.q_len
     flops = 4.0 * w.head_dim * w.hq * S * (S + 1) / 2
     tf = flops / us / 1e6
+    slopes = torch.tensor(2.0 ** (-8.0 * (np.arange(w.hq) + 1) / w.hq), dtype=torch.float32, device="cuda")
+    doc = 2048
+    mask = _document_mask(torch, np, S, (int(pt.shape[1]) * w.page_size + 31) // 32, doc)
+    mods = {}
+    for name, kw, pairs in (("alibi_causal", dict(alibi_slopes=slopes), S * (S + 1) / 2),
+                            ("document_mask", dict(mask_bits=mask), (S // doc) * doc * (doc + 1) / 2)):
+        mcall = lambda: atlas.atlas_attend_mods(q, k, v, pt, ctx, w.scale, out=out, lse=lse, **kw)
+        mus = _median_call_us(torch, np, mcall, calls=calls)
+        fl = 4.0 * w.head_dim * w.hq * pairs
+        mods[name] = {"us": round(mus, 1), "flop": fl, "TFLOPs": round(fl / mus / 1e6, 1)}
     return {"us": round(us, 1), "flop": flops, "TFLOPs": round(tf, 1),
-            "frac_mfma_fp16": round(3.0 * tf / BF16_PEAK_TFLOPS, 4),
-            "note": "fp32 Q/K/V; every product as three fp16 matrix products (hi.hi + lo.hi + hi.lo)"}
+            "frac_mfma_fp16": round(3.0 * tf / BF16_PEAK_TFLOPS, 4), "mods": mods,
+            "note": "fp32 Q/K/V; every product as three fp16 matrix products (hi.hi + lo.hi + hi.lo); "
+                    "mods TFLOP/s over visible pairs"}
 
 
 def mods_report(torch, np, p, atlas, calls=10):
@@ -336,12 +359,7 @@ def mods_report(torch, np, p, atlas, calls=10):
     S, hq, d = pw.q_len, pw.hq, pw.head_dim
     slopes = torch.tensor(2.0 ** (-8.0 * (np.arange(hq) + 1) / hq), dtype=torch.float32, device="cuda")
     doc = 2048
-    words = (int(p["pt"].shape[1]) * pw.page_size + 31) // 32
-    j = np.arange(words * 32)
-    qpos = np.arange(S)
-    keep = (j[None, :] // doc == qpos[:, None] // doc) & (j[None, :] <= qpos[:, None])
-    bits = np.packbits(keep, axis=-1, bitorder="little").view("<u4").astype(np.uint32).view(np.int32)
-    mask = torch.from_numpy(np.ascontiguousarray(bits)[None]).cuda()
+    mask = _document_mask(torch, np, S, (int(p["pt"].shape[1]) * pw.page_size + 31) // 32, doc)
     out = torch.empty(1, S, hq, d, dtype=torch.float32, device="cuda")
     lse = torch.empty(1, S, hq, dtype=torch.float32, device="cuda")
     rep = {}

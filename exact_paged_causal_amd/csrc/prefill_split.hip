@@ -325,17 +325,32 @@ __global__ __launch_bounds__(512) void prefill_split_kernel(PrefillArgs a)
             __syncthreads();
             const int rows_pos = i1 - i0;
             const int wl = a.mods.mask_words - 1;
-            for (int idx = tid; idx < n_iter * rows_pos; idx += 512) {
-                const int pp = idx / n_iter;
-                const int c = idx - pp * n_iter;
-                const uint32_t *m = a.mods.mask + ((int64_t)b * a.q_len + i0 + pp) * a.mods.mask_words;
-                const int w = (block_at(c) * kBN) >> 5;
-                const uint32_t m0 = m[w < wl ? w : wl];
-                const uint32_t m1 = m[w + 1 < wl ? w + 1 : wl];
-                if ((m0 | m1) != 0u)
-                    s_need[c] = 1;
-                if ((m0 & m1) != ~0u || w + 1 > wl)
-                    s_part[c] = 1;
+            const int total = n_iter * rows_pos;
+            // kLoads (row, block) pairs per thread in flight at a time.
+            constexpr int kLoads = 4;
+            for (int base = 0; base < total; base += 512 * kLoads) {
+                uint32_t m0[kLoads], m1[kLoads];
+                int cc[kLoads], ww[kLoads];
+#pragma unroll
+                for (int u = 0; u < kLoads; ++u) {
+                    const int idx = base + 512 * u + tid;
+                    const int ix = idx < total ? idx : 0;
+                    const int pp = ix / n_iter;
+                    cc[u] = idx < total ? ix - pp * n_iter : -1;
+                    const uint32_t *m = a.mods.mask + ((int64_t)b * a.q_len + i0 + pp) * a.mods.mask_words;
+                    ww[u] = (block_at(ix - pp * n_iter) * kBN) >> 5;
+                    m0[u] = m[ww[u] < wl ? ww[u] : wl];
+                    m1[u] = m[ww[u] + 1 < wl ? ww[u] + 1 : wl];
+                }
+#pragma unroll
+                for (int u = 0; u < kLoads; ++u) {
+                    if (cc[u] < 0)
+                        continue;
+                    if ((m0[u] | m1[u]) != 0u)
+                        s_need[cc[u]] = 1;
+                    if ((m0[u] & m1[u]) != ~0u || ww[u] + 1 > wl)
+                        s_part[cc[u]] = 1;
+                }
             }
             __syncthreads();
             if (wave == 0) {
