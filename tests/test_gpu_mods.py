@@ -122,9 +122,10 @@ CASES = [
     ("f32", 8, 2, 128, 16, 100, (100, 300), False, True, 0.7),    # fp32 tiled
     ("f32", 4, 1, 64, 32, 70, (500,), True, True, None),
     ("f32", 2, 2, 128, 128, 257, (3000,), False, False, 0.4),
-    # ALiBi walks the key blocks outward from the diagonal: over 3000
-    # one-token pages the page-id window moves backwards (and forwards again
-    # for non-causal rows), with and without a listed mask
+    # ALiBi walks the key blocks outward from the diagonal (here over 3000
+    # one-token pages, in key splits of 8 blocks), with and without a listed
+    # mask; test_alibi_walk_moves_the_page_window runs unsplit walks that
+    # move the page-id window
     ("bf16", 4, 1, 64, 1, 64, (3000,), True, True, None),
     ("bf16", 4, 1, 64, 1, 3000, (3000,), False, True, None),
     ("bf16", 4, 1, 64, 1, 64, (3000,), True, True, 0.9),
@@ -272,4 +273,51 @@ def test_mask_past_the_listing_capacity_f32():
     torch.cuda.synchronize()
     rows = np.r_[0:40, 60000 - int(pos[0]) - 40:60000 - int(pos[0]) + 40, w.q_len - 60:w.q_len]
     check_mods(inp, out, lse, True, None, mask, "mask past the listing capacity", rows=rows)
+    assert not torch.isnan(out).any()
+
+
+WALK_CASES = [
+    # (dtype, q_len, causal, mask): 8192 one-token pages per sequence
+    ("bf16", 8192, True, False),
+    ("bf16", 4096, False, True),
+    ("f32", 8192, True, True),
+    ("f32", 4096, False, False),
+]
+
+
+@pytest.mark.parametrize("case", WALK_CASES, ids=lambda c: f"{c[0]}-q{c[1]}-{'c' if c[2] else 'nc'}"
+                                                           f"{'-mask' if c[3] else ''}")
+def test_alibi_walk_moves_the_page_window(case):
+    """ALiBi rows walk their key blocks from the diagonal leftwards (then
+    rightwards for non-causal rows).  With one-token pages and one q-head per
+    K/V head (256 positions per workgroup, 8 K/V heads, 256 workgroups: no
+    key splits), a workgroup's keys span up to 8192 pages, so the page-id
+    window (2048 entries bf16, 1024 fp32) moves backwards during the walk
+    and forwards again past the diagonal.  With a mask, the listed walk
+    skips every block whose keys are hidden from all rows (one block in
+    five) and applies the mask bits on the others."""
+    dtype, q_len, causal, masked = case
+    B = 8192 // q_len
+    w = wl(dtype, 8, 8, 64, 1, q_len, (8192,) * B, seed=45)
+    # the plan has no key splits: its workspace is the 256-byte header alone
+    from exact_paged_causal_amd import atlas as A
+    a = A.AttnArgs()
+    a.q_dtype = a.kv_dtype = 1 if dtype == "bf16" else 0
+    a.batch, a.q_len, a.num_q_heads, a.num_kv_heads, a.head_dim = B, q_len, 8, 8, 64
+    a.page_size, a.num_phys_pages, a.max_pages_per_seq, a.scale = 1, 8192 * B, 8192, w.scale
+    assert A.atlas_prefill_workspace_bytes(a) == 256
+    say(f"[mods] ALiBi walk over 8192 one-token pages, {dtype} q_len={q_len} causal={causal} mask={masked}")
+    inp = H.build(w)
+    slopes = alibi_slopes(8)
+    mask = None
+    if masked:
+        i = np.arange(q_len)[:, None]
+        j = np.arange(8192)[None, :]
+        keep = ((j // 64) % 5 != 2) & ((j * 7 + i * 3) % 10 != 0)
+        keep |= j == (8192 - q_len + i)
+        mask = np.broadcast_to(keep, (B, q_len, 8192))
+    out, lse = run_mods(inp, causal, slopes, mask)
+    torch.cuda.synchronize()
+    rows = np.r_[0:16, q_len // 2 - 8:q_len // 2 + 8, q_len - 48:q_len]
+    check_mods(inp, out, lse, causal, slopes, mask, f"walk {case}", rows=rows)
     assert not torch.isnan(out).any()
