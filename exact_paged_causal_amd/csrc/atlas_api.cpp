@@ -101,6 +101,7 @@ struct Plan {
 constexpr size_t kWorkspaceHeader = 256;  // validation-mode flags live here
 constexpr int kDefaultSplitTokens = 4096; // keys per split-KV work item by default
 constexpr int kMinItems = 2048;           // fewest work items (8 per CU) before spans shrink
+constexpr int kSingleSplitKeys = 256;     // contexts up to this length take one split per row (no merge)
 constexpr int kFillItems = 512;           // work items (two per CU) below which row chunks shrink
 
 int32_t check_shapes(const atlas_attn_args *a, bool decode, Plan *p)
@@ -257,6 +258,13 @@ int32_t check_shapes(const atlas_attn_args *a, bool decode, Plan *p)
         if (T > max_t_by_lds)
             return fail(ATLAS_ERR_RANGE, "split_tokens %d spans more than %d pages", a->split_tokens,
                         atlas::kMaxSplitPages - 2);
+    } else if (max_ctx <= kSingleSplitKeys && !a->sink_tokens && kSingleSplitKeys <= max_t_by_lds) {
+        // Short contexts: one split per row, finished by the fold itself, so
+        // no merge is launched.  Measured (C-ABI call, four shapes at 256
+        // keys): 11.7-13.8 us with 64-key splits and the merge against
+        // 8.7-11.9 us; at 512 keys the longer serial fold no longer pays for
+        // every shape, at 1024 it loses.
+        T = kSingleSplitKeys;
     } else {
         // Long spans amortise a work item's set-up (page ids, query, final
         // combine); shorter ones only while the grid would be too small to
@@ -553,6 +561,10 @@ int32_t attend(const atlas_attn_args *a, void *stream_ptr, bool decode, const Re
                                              : atlas::launch_split_valu(k, stream);
     if (e != hipSuccess)
         return fail(ATLAS_ERR_DEVICE, "split launch: %s", hipGetErrorString(e));
+    // One split per row: the fold wrote the final rows (merge_row.h,
+    // write_single_split).
+    if (p.max_splits == 1)
+        return ok();
     e = atlas::launch_merge(k, stream);
     if (e != hipSuccess)
         return fail(ATLAS_ERR_DEVICE, "merge launch: %s", hipGetErrorString(e));

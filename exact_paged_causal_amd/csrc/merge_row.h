@@ -46,6 +46,20 @@ __device__ __forceinline__ int merge_split_count(const SplitArgs &a, int b, int 
     return plan.n_splits;
 }
 
+// A call whose plan gives every row one split (max_splits == 1) needs no
+// merge: the fold writes each row's final output and lse itself, with the
+// merge's own arithmetic for a single split (its weight 2^0 = 1, its sum L =
+// l), so the bits are those the merge would write.  l = 0 (nothing visible)
+// gives NaN and lse = -inf.
+__device__ __forceinline__ void write_single_split(const SplitArgs &a, int64_t row_id, int d, float m, float l,
+                                                   float acc)
+{
+    const bool any = l > 0.0f;
+    a.out[row_id * a.head_dim + d] = any ? acc * (1.0f / l) : __builtin_nanf("");
+    if (d == 0 && a.lse)
+        a.lse[row_id] = any ? (m + log2f(l)) * kLn2 : -INFINITY;
+}
+
 // One wave merges output row row_id = (b * q_len + i) * hq + h over its n
 // splits: lanes over splits for the maximum and the denominator, then lanes
 // over dims for the weighted sum in split order (each split's weight is the

@@ -48,6 +48,7 @@
 // placeholder load reads row 0 of page 0 of the K/V head, which stays cached.
 #include "device.h"
 #include "kernels.h"
+#include "merge_row.h"
 #include "philox.h"
 
 namespace atlas {
@@ -139,8 +140,19 @@ __global__ __launch_bounds__(256) void split_mfma_kernel(SplitArgs a)
     const bool causal = !MODS || a.mods.causal;
     const SplitPlan plan = causal ? plan_splits(cr.pos_min, cr.pos_max, W, S, a.split_tokens)
                                   : plan_splits(ctx - 1, ctx - 1, 0, 0, a.split_tokens);
-    if (split >= plan.n_splits)
+    if (split >= plan.n_splits) {
+        // Without a merge, the rows of a chunk that sees no key are written
+        // here (once, by split 0).
+        if (a.max_splits == 1 && plan.n_splits == 0) {
+            for (int idx = tid; idx < (cr.r1 - cr.r0) * D; idx += 256) {
+                const int row = cr.r0 + idx / D;
+                const int hh = a.groups.list[gstart + row % gsize];
+                write_single_split(a, ((int64_t)b * a.q_len + row / gsize) * a.hq + hh, idx % D, -INFINITY, 0.0f,
+                                   0.0f);
+            }
+        }
         return;
+    }
     int ka, kb;
     split_range(plan, split, a.split_tokens, &ka, &kb);
 
@@ -426,6 +438,10 @@ __global__ __launch_bounds__(256) void split_mfma_kernel(SplitArgs a)
         }
         const int i = row / gsize;
         const int hh = a.groups.list[gstart + row % gsize];
+        if (a.max_splits == 1) {
+            write_single_split(a, ((int64_t)b * a.q_len + i) * a.hq + hh, d, mm, ls, as);
+            continue;
+        }
         const int64_t slot = (((int64_t)b * a.q_len + i) * a.hq + hh) * a.max_splits + split;
         a.ws_acc[slot * D + d] = as;
         if (d == 0) {

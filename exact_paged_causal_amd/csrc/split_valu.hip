@@ -42,6 +42,7 @@
 
 #include "device.h"
 #include "kernels.h"
+#include "merge_row.h"
 #include "philox.h"
 
 namespace atlas {
@@ -105,8 +106,18 @@ __global__ __launch_bounds__(256) void split_valu_kernel(SplitArgs a)
     const bool causal = !MODS || a.mods.causal;
     const SplitPlan plan = causal ? plan_splits(cr.pos_min, cr.pos_max, W, S, a.split_tokens)
                                   : plan_splits(ctx - 1, ctx - 1, 0, 0, a.split_tokens);
-    if (split >= plan.n_splits)
+    if (split >= plan.n_splits) {
+        // Without a merge, the rows of a chunk that sees no key are written
+        // here (once, by split 0).
+        if (a.max_splits == 1 && plan.n_splits == 0) {
+            for (int idx = tid; idx < (cr.r1 - cr.r0) * D; idx += 256) {
+                const int rr = cr.r0 + idx / D;
+                const int h = a.groups.list[gstart + rr % gsize];
+                write_single_split(a, ((int64_t)b * a.q_len + rr / gsize) * a.hq + h, idx % D, -INFINITY, 0.0f, 0.0f);
+            }
+        }
         return;
+    }
     int ka, kb;
     split_range(plan, split, a.split_tokens, &ka, &kb);
 
@@ -397,6 +408,10 @@ __global__ __launch_bounds__(256) void split_valu_kernel(SplitArgs a)
         const int i = rr / gsize;
         const int h = a.groups.list[gstart + rr % gsize];
         const int64_t row_id = ((int64_t)b * a.q_len + i) * a.hq + h;
+        if (a.max_splits == 1) {
+            write_single_split(a, row_id, d, mm, ls, as);
+            continue;
+        }
         const int64_t slot = row_id * a.max_splits + split;
         a.ws_acc[slot * D + d] = as;
         if (d == 0) {

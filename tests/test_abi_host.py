@@ -374,3 +374,25 @@ def test_tiled_block_list_is_the_visible_blocks(planner, pos_lo, pos_hi, w, s):
     want = sorted({k // 64 for k in _union_visible(pos_lo, pos_hi, w, s if w > 0 else 0)})
     assert got == want
 
+
+
+def test_short_contexts_plan_one_split_per_row():
+    """Contexts up to 256 keys without a sink array plan one split per row
+    (the fold writes the rows and no merge runs): the workspace holds one
+    partial state per row.  257 keys, or a sink array, plan several."""
+    from exact_paged_causal_amd import atlas as A
+    sinks = (ctypes.c_int32 * 2)(0, 0)
+    win = (ctypes.c_int32 * 2)(8, 8)
+    for q_len, fn in ((1, A.lib.atlas_decode_workspace_bytes), (16, A.lib.atlas_prefill_workspace_bytes)):
+        rows = 2 * q_len * 8
+        per_split = rows * (64 + 2) * 4
+        for ctx, page, extra, splits in ((256, 16, {}, 1), (64, 64, {}, 1), (256, 1, {}, 1),
+                                         (256, 16, {"window": ctypes.addressof(win)}, 1),
+                                         (272, 16, {}, None), (256, 16, {"window": ctypes.addressof(win),
+                                                                         "sink_tokens": ctypes.addressof(sinks)}, None)):
+            a = _valid_args(q_len=q_len, page_size=page, max_pages_per_seq=ctx // page, num_phys_pages=4096, **extra)
+            n = fn(ctypes.byref(a))
+            if splits == 1:
+                assert n == 256 + per_split, (q_len, ctx, page, extra, n)
+            else:
+                assert n >= 256 + 2 * per_split, (q_len, ctx, page, extra, n)
