@@ -102,6 +102,8 @@ constexpr size_t kWorkspaceHeader = 256;  // validation-mode flags live here
 constexpr int kDefaultSplitTokens = 4096; // keys per split-KV work item by default
 constexpr int kMinItems = 2048;           // fewest work items (8 per CU) before spans shrink
 constexpr int kSingleSplitKeys = 256;     // contexts up to this length take one split per row (no merge)
+constexpr int kMinSplitTokens = 128;      // shortest default split
+constexpr int kMaxSplitsPerRow = 32;      // default splits lengthen until a row has at most this many
 constexpr int kFillItems = 512;           // work items (two per CU) below which row chunks shrink
 
 int32_t check_shapes(const atlas_attn_args *a, bool decode, Plan *p)
@@ -268,10 +270,20 @@ int32_t check_shapes(const atlas_attn_args *a, bool decode, Plan *p)
     } else {
         // Long spans amortise a work item's set-up (page ids, query, final
         // combine); shorter ones only while the grid would be too small to
-        // fill the chip.
+        // fill the chip, down to 128 keys and to at most 32 splits per row:
+        // past those, the per-split set-up and the merge's traffic cost more
+        // than the extra work items gain.  Measured (C-ABI calls over 35
+        // shapes of 1 to 64 rows per K/V head and 512 to 8192 keys): the
+        // same or faster than halving down to 64 keys for 2048 work items
+        // everywhere but three 512-key shapes (within 0.4 us), and up to
+        // 1.8x faster in between (16 queries x 8 heads over 8192 keys 50.3
+        // -> 27.8 us).  Large calls (the grid full at 2048-key splits or
+        // longer) plan as before.
         T = kDefaultSplitTokens;
-        while (T > 64 && items_per_split * ((max_ctx + T - 1) / T) < kMinItems)
+        while (T > kMinSplitTokens && items_per_split * ((max_ctx + T - 1) / T) < kMinItems)
             T /= 2;
+        while (T < kDefaultSplitTokens && (max_ctx + T - 1) / T > kMaxSplitsPerRow)
+            T *= 2;
         if (T > max_t_by_lds)
             T = max_t_by_lds;
     }
