@@ -100,7 +100,8 @@ struct Plan {
 
 constexpr size_t kWorkspaceHeader = 256;  // validation-mode flags live here
 constexpr int kDefaultSplitTokens = 4096; // keys per split-KV work item by default
-constexpr int kMinItems = 2048;           // fewest work items (8 per CU) before spans shrink
+constexpr int kMinItemsVector = 2048;     // fewest work items before spans shrink: fp32 K/V (8 per CU)
+constexpr int kMinItemsMatrix = 512;      // bf16 K/V, the matrix-core fold (2 per CU)
 constexpr int kSingleSplitKeys = 256;     // contexts up to this length take one split per row (no merge)
 constexpr int kMinSplitTokens = 128;      // shortest default split
 constexpr int kMaxSplitsPerRow = 32;      // default splits lengthen until a row has at most this many
@@ -269,18 +270,24 @@ int32_t check_shapes(const atlas_attn_args *a, bool decode, Plan *p)
         T = kSingleSplitKeys;
     } else {
         // Long spans amortise a work item's set-up (page ids, query, final
-        // combine); shorter ones only while the grid would be too small to
-        // fill the chip, down to 128 keys and to at most 32 splits per row:
-        // past those, the per-split set-up and the merge's traffic cost more
-        // than the extra work items gain.  Measured (C-ABI calls over 35
-        // shapes of 1 to 64 rows per K/V head and 512 to 8192 keys): the
-        // same or faster than halving down to 64 keys for 2048 work items
-        // everywhere but three 512-key shapes (within 0.4 us), and up to
-        // 1.8x faster in between (16 queries x 8 heads over 8192 keys 50.3
-        // -> 27.8 us).  Large calls (the grid full at 2048-key splits or
-        // longer) plan as before.
+        // combine); shorter ones only while the call would have fewer work
+        // items than eight per CU for the vector fold (fp32 K/V) or two per
+        // CU for the matrix-core fold (bf16 K/V), down to 128 keys and to at
+        // most 32 splits per row: past those, the per-split set-up and the
+        // merge's traffic cost more than the extra work items gain.  The
+        // plan does not depend on whether the fold generates cold pages, so
+        // generating and reading the same pages give the same bits.
+        // Measured (C-ABI calls over 60 shapes of 1 to 128 rows per K/V head
+        // and 512 to 32768 keys) against halving down to 64 keys for eight
+        // items per CU: within 3 % or faster everywhere, up to 1.8x faster
+        // for mid-size calls (16 fp32 queries x 8 q-heads over 8192 keys
+        // 50.3 -> 27.8 us; a bf16 batch of 16 x 64 q-heads over 2048 keys
+        // 53.2 -> 32.6 us).  Generating bf16 decodes gain as much (a batch
+        // of 16 over 2048 keys 108.7 -> 72.6 us); generating fp32 ones lose
+        // up to 44 % with two items per CU, hence eight for fp32.
+        const int64_t min_items = a->kv_dtype == ATLAS_DTYPE_BF16 ? kMinItemsMatrix : kMinItemsVector;
         T = kDefaultSplitTokens;
-        while (T > kMinSplitTokens && items_per_split * ((max_ctx + T - 1) / T) < kMinItems)
+        while (T > kMinSplitTokens && items_per_split * ((max_ctx + T - 1) / T) < min_items)
             T /= 2;
         while (T < kDefaultSplitTokens && (max_ctx + T - 1) / T > kMaxSplitsPerRow)
             T *= 2;
