@@ -33,7 +33,8 @@
 // other halves the next instruction wanted from cache), which ruled out
 // non-temporal loads for K there.
 // At the end the 4 waves' states are combined in LDS and one (m, l, acc)
-// partial per row is written; merge.hip finishes.
+// partial per row is written; merge.hip finishes (with one split per row,
+// the fold writes the output and lse itself, merge_row.h).
 //
 // fp32 queries over the bf16 cache (QF32 instances): each query element is
 // carried as a bf16 high part and a bf16 remainder (~16 significant bits

@@ -7,6 +7,9 @@
 // state (running max m, sum l, accumulator acc) -- CFR-Atlas README: each
 // page is folded into online softmax; CPUAttn README "Operator model": a
 // split is allowed because a structured merge (merge.hip) recombines it.
+// When the plan gives every row one split (short contexts), the work item's
+// state is the row's final state and the fold writes the output and lse
+// itself, with the merge's own arithmetic (merge_row.h): no merge runs.
 //
 // Lane layout.  A K or V row of D elements is read by a group of R lanes
 // (R = 16 for 256-byte rows, 8 for 128-byte rows), each lane loading NL
@@ -386,7 +389,8 @@ __global__ __launch_bounds__(256) void split_valu_kernel(SplitArgs a)
     }
     __syncthreads();
 
-    // Combine the 4 waves and write this split's partial state per row.
+    // Combine the 4 waves and write this split's partial state per row (or,
+    // with one split per row, the row's output and lse).
     for (int idx = tid; idx < MC * D; idx += 256) {
         const int r = idx / D;
         const int d = idx - r * D;
