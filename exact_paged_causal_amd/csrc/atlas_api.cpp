@@ -100,8 +100,8 @@ struct Plan {
 
 constexpr size_t kWorkspaceHeader = 256;  // validation-mode flags live here
 constexpr int kDefaultSplitTokens = 4096; // keys per split-KV work item by default
-constexpr int kMinItemsVector = 2048;     // fewest work items before spans shrink: fp32 K/V (8 per CU)
-constexpr int kMinItemsMatrix = 512;      // bf16 K/V, the matrix-core fold (2 per CU)
+constexpr int kMinItemsVector = 2048;     // work items (8 per CU) the vector fold's large plans aim at
+constexpr int kMinItemsMatrix = 512;      // work items (2 per CU) the other plans aim at
 constexpr int kSingleSplitKeys = 256;     // contexts up to this length take one split per row (no merge)
 constexpr int kMinSplitTokens = 128;      // shortest default split
 constexpr int kMaxSplitsPerRow = 32;      // default splits lengthen until a row has at most this many
@@ -271,26 +271,41 @@ int32_t check_shapes(const atlas_attn_args *a, bool decode, Plan *p)
     } else {
         // Long spans amortise a work item's set-up (page ids, query, final
         // combine); shorter ones only while the call would have fewer work
-        // items than eight per CU for the vector fold (fp32 K/V) or two per
-        // CU for the matrix-core fold (bf16 K/V), down to 128 keys and to at
-        // most 32 splits per row: past those, the per-split set-up and the
-        // merge's traffic cost more than the extra work items gain.  The
-        // plan does not depend on whether the fold generates cold pages, so
-        // generating and reading the same pages give the same bits.
+        // items than it needs, down to 128 keys and to at most 32 splits per
+        // row: past those, the per-split set-up and the merge's traffic
+        // cost more than the extra work items gain.  The matrix-core fold
+        // (bf16 K/V) starts at 4096 keys and wants two items per CU.  The
+        // vector fold (fp32 K/V) keeps the plan for eight items per CU from
+        // 4096 keys when that plan's splits are 1024 keys or longer (large
+        // calls: the long-context decode, long fp32 prefills); otherwise it
+        // takes two items per CU from 512 keys.  The plan does not depend on
+        // whether the fold generates cold pages, so generating and reading
+        // the same pages give the same bits.
         // Measured (C-ABI calls over 60 shapes of 1 to 128 rows per K/V head
-        // and 512 to 32768 keys) against halving down to 64 keys for eight
-        // items per CU: within 3 % or faster everywhere, up to 1.8x faster
-        // for mid-size calls (16 fp32 queries x 8 q-heads over 8192 keys
-        // 50.3 -> 27.8 us; a bf16 batch of 16 x 64 q-heads over 2048 keys
-        // 53.2 -> 32.6 us).  Generating bf16 decodes gain as much (a batch
-        // of 16 over 2048 keys 108.7 -> 72.6 us); generating fp32 ones lose
-        // up to 44 % with two items per CU, hence eight for fp32.
-        const int64_t min_items = a->kv_dtype == ATLAS_DTYPE_BF16 ? kMinItemsMatrix : kMinItemsVector;
-        T = kDefaultSplitTokens;
-        while (T > kMinSplitTokens && items_per_split * ((max_ctx + T - 1) / T) < min_items)
-            T /= 2;
-        while (T < kDefaultSplitTokens && (max_ctx + T - 1) / T > kMaxSplitsPerRow)
-            T *= 2;
+        // and 512 to 32768 keys, and 60 fp32 reading and generating calls)
+        // against halving from 4096 down to 64 keys for eight items per CU:
+        // up to 1.8x faster for mid-size calls (16 fp32 queries x 8 q-heads
+        // over 8192 keys 50.3 -> 27.8 us; a bf16 batch of 16 x 64 q-heads
+        // over 2048 keys 53.2 -> 32.6 us; an fp32 batch of 8 x 64 q-heads
+        // over 2048 keys 50.4 -> 40.3 us, generating 93.0 -> 74.1 us),
+        // within run-to-run spread or a few per cent elsewhere.  Generating
+        // fp32 decodes lost up to 44 % with splits of 2048 keys where 512
+        // served (2 x 32768 keys 77.6 -> 112 us), hence the 512-key start.
+        auto pick = [&](int64_t start, int64_t min_items) {
+            int64_t t = start;
+            while (t > kMinSplitTokens && items_per_split * ((max_ctx + t - 1) / t) < min_items)
+                t /= 2;
+            while (t < kDefaultSplitTokens && (max_ctx + t - 1) / t > kMaxSplitsPerRow)
+                t *= 2;
+            return t;
+        };
+        if (a->kv_dtype == ATLAS_DTYPE_BF16) {
+            T = pick(kDefaultSplitTokens, kMinItemsMatrix);
+        } else {
+            T = pick(kDefaultSplitTokens, kMinItemsVector);
+            if (T < 1024)
+                T = pick(512, kMinItemsMatrix);
+        }
         if (T > max_t_by_lds)
             T = max_t_by_lds;
     }

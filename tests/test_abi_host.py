@@ -399,15 +399,20 @@ def test_short_contexts_plan_one_split_per_row():
 
 
 def test_split_plan_depends_on_the_cache_dtype():
-    """Default splits: the matrix-core fold (bf16 cache) aims at two work
-    items per CU, the vector fold (fp32 cache) at eight, both no shorter than
-    128 keys and at most 32 per row.  4 sequences x 32 q-heads over 8 K/V
-    heads, 8192 keys: bf16 plans 16 splits of 512 keys, fp32 32 of 256 (an
-    fp32 query over the bf16 cache plans as bf16).  The plan is the same for
-    the decode that generates cold pages, so the workspace serves both."""
+    """Default splits, never shorter than 128 keys nor more than 32 per row.
+    The matrix-core fold (bf16 cache, also under an fp32 query) aims at two
+    work items per CU from 4096 keys; the vector fold (fp32 cache) keeps the
+    plan for eight per CU when its splits come out 1024 keys or longer, and
+    otherwise aims at two per CU from 512 keys.  8 x 32 q-heads over 8 K/V
+    heads at 65536 keys: fp32 32 splits of 2048, bf16 16 of 4096; 4 x 32
+    q-heads at 8192 keys: 16 splits of 512 for either.  The plan is the same
+    for the decode that generates cold pages, so one workspace serves both."""
     from exact_paged_causal_amd import atlas as A
-    rows = 4 * 32
-    for q_dt, kv_dt, splits in ((1, 1, 16), (0, 1, 16), (0, 0, 32)):
-        a = _valid_args(q_dtype=q_dt, kv_dtype=kv_dt, batch=4, num_q_heads=32, num_kv_heads=8, head_dim=128,
-                        page_size=16, max_pages_per_seq=512, num_phys_pages=1 << 16)
-        assert A.lib.atlas_decode_workspace_bytes(ctypes.byref(a)) == 256 + rows * splits * (128 + 2) * 4, (q_dt, kv_dt)
+    for batch, d, pages, cases in ((8, 64, 128, ((0, 0, 32), (1, 1, 16), (0, 1, 16))),
+                                   (4, 128, 512, ((0, 0, 16), (1, 1, 16), (0, 1, 16)))):
+        rows = batch * 32
+        for q_dt, kv_dt, splits in cases:
+            a = _valid_args(q_dtype=q_dt, kv_dtype=kv_dt, batch=batch, num_q_heads=32, num_kv_heads=8, head_dim=d,
+                            page_size=512 if pages == 128 else 16, max_pages_per_seq=pages, num_phys_pages=1 << 16)
+            assert A.lib.atlas_decode_workspace_bytes(ctypes.byref(a)) == 256 + rows * splits * (d + 2) * 4, \
+                (batch, q_dt, kv_dt)
