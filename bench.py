@@ -550,6 +550,8 @@ def workload_report(torch, np, workloads, atlas, oracle=None):
         if mode == "resident":
             r["c_abi_us"] = round(_c_abi_call_us(torch, np, "atlas_attend_decode", atlas.make_attn_args(
                 q, k, v, pt, ctx, w.scale, out=out, lse=lse, workspace=ws)[0], calls=50), 2)
+            prep = atlas.prepare_attend("decode", q, k, v, pt, ctx, w.scale, out=out, lse=lse, workspace=ws)
+            r["prepared_us"] = round(_median_call_us(torch, np, prep, calls=50), 2)
             if oracle is not None:
                 r["cpu_baseline"] = _oracle_single_head(w, q, out, np, oracle)
     kvb = int(w.context_lens.sum()) * w.hkv * w.head_dim * 4 * 2
@@ -558,7 +560,8 @@ def workload_report(torch, np, workloads, atlas, oracle=None):
                                       "frac_hbm": round(kvb / us / 1e3 / HBM_PEAK_GBS, 4),
                                       "note": "launch-latency bound (2 MiB of K/V); *_us are per Python "
                                               "call, host overhead included (c_abi_us: one C-ABI call with "
-                                              "prepared arguments); cold regenerates all 8 pages in the call"})
+                                              "prepared arguments; prepared_us: a prepare_attend call from "
+                                              "Python); cold regenerates all 8 pages in the call"})
     # GQA short-query suffix attention (16 queries at positions 240..255).
     w = workloads.make("gqa_short_query")
     lay = workloads.page_layout(w)
@@ -574,12 +577,17 @@ def workload_report(torch, np, workloads, atlas, oracle=None):
     us, us_min = _call_stats_us(torch, np, call)
     c_us = _c_abi_call_us(torch, np, "atlas_attend_prefill", atlas.make_attn_args(
         q, k, v, pt, ctx, w.scale, out=out, lse=lse, workspace=ws)[0], calls=50)
+    prep = atlas.prepare_attend("prefill", q, k, v, pt, ctx, w.scale, out=out, lse=lse, workspace=ws)
+    p_us = _median_call_us(torch, np, prep, calls=50)
     L = int(w.context_lens[0])
     pairs = w.hq * sum(L - w.q_len + i + 1 for i in range(w.q_len))
     rep["gqa_short_query"] = {"us": round(us, 2), "us_min": round(us_min, 2), "c_abi_us": round(c_us, 2),
+                              "prepared_us": round(p_us, 2),
                               "kv_bytes": L * w.hkv * w.head_dim * 4 * 2,
                               "flop": 4 * w.head_dim * pairs,
-                              "note": "latency bound (256 KiB of K/V); us per Python call, host overhead included; c_abi_us: one C-ABI call with prepared arguments"}
+                              "note": "latency bound (256 KiB of K/V); us per Python call, host overhead included; "
+                                      "c_abi_us: one C-ABI call with prepared arguments; prepared_us: a "
+                                      "prepare_attend call from Python"}
     if oracle is not None:
         rep["gqa_short_query"]["cpu_baseline"] = _oracle_short_query(w, lay, q, k, v, out, np, oracle, pairs)
     del k, v

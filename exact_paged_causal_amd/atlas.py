@@ -481,6 +481,64 @@ def atlas_attend_mods(q, k_pages, v_pages, page_table, context_lens, scale, *, c
                    softcap=softcap, split_tokens=split_tokens, want_lse=want_lse)
 
 
+class PreparedAttend:
+    """One attention call with fixed tensors, checked and marshalled once.
+
+    Calling it issues the C-ABI call again with the same arguments: the
+    tensors' contents (queries, cache pages, page table, lengths, variant
+    arrays) may change between calls, their shapes, dtypes and storage may
+    not, and the object keeps them alive.  Runs on the given stream, else on
+    torch's current stream of the tensors' device at each call.  Returns
+    (out, lse)."""
+
+    def __init__(self, entry, args, keep, stream, device_index, out, lse):
+        self._entry = entry
+        self._fn = getattr(lib, entry)
+        self._args = args
+        self._ref = ctypes.byref(args)
+        self._keep = keep
+        self._stream = stream
+        self._dev = device_index
+        self.out, self.lse = out, lse
+
+    def __call__(self):
+        handle = self._stream.cuda_stream if self._stream is not None else _current_stream_handle(self._dev)
+        st = self._fn(self._ref, ctypes.c_void_p(handle))
+        if st != ATLAS_OK:
+            raise AtlasError(st, self._entry)
+        return self.out, self.lse
+
+
+def prepare_attend(kind: str, q, k_pages, v_pages, page_table, context_lens, scale, *, out, lse=None,
+                   workspace=None, stream=None, head_map=None, window=None, sink_tokens=None, softcap=None,
+                   split_tokens=0) -> PreparedAttend:
+    """A repeatable atlas_attend_decode (kind "decode") or atlas_attend_prefill
+    (kind "prefill") call over fixed tensors: the checks and the argument
+    structure are done here once (and the workspace allocated, if none is
+    given), so each call costs only the C-ABI call.  For loops that reuse
+    the same buffers with new contents.  `out` is required."""
+    fns = {"decode": ("atlas_attend_decode", atlas_decode_workspace_bytes),
+           "prefill": ("atlas_attend_prefill", atlas_prefill_workspace_bytes)}
+    if kind not in fns:
+        raise ValueError(f"kind must be 'decode' or 'prefill', got {kind!r}")
+    entry, ws_fn = fns[kind]
+    if out is None:
+        raise ValueError("a prepared call writes to a fixed out tensor")
+    args, keep = make_attn_args(q, k_pages, v_pages, page_table, context_lens, scale, head_map=head_map,
+                                window=window, sink_tokens=sink_tokens, softcap=softcap, out=out, lse=lse,
+                                split_tokens=split_tokens)
+    dev = q.device
+    if workspace is None:
+        with (torch.cuda.stream(stream) if stream is not None else contextlib.nullcontext()):
+            workspace = torch.empty(max(ws_fn(args), 1), dtype=torch.uint8, device=dev)
+    else:
+        _check(workspace, "workspace", None, dev)
+    args.workspace = _ptr(workspace)
+    args.workspace_bytes = workspace.numel() * workspace.element_size()
+    keep += [q, k_pages, v_pages, page_table, context_lens, out, lse, workspace, window, sink_tokens, softcap]
+    return PreparedAttend(entry, args, keep, stream, dev.index, out, lse)
+
+
 def atlas_regenerate_pages(k_pages, v_pages, jobs, seed: int, layer: int = 0, stream=None):
     """Regenerate whole pages into the arenas.  jobs: int32 [n][3] device tensor of
     (seq, logical_page, phys_page)."""

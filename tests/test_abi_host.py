@@ -416,3 +416,14 @@ def test_split_plan_depends_on_the_cache_dtype():
                             page_size=512 if pages == 128 else 16, max_pages_per_seq=pages, num_phys_pages=1 << 16)
             assert A.lib.atlas_decode_workspace_bytes(ctypes.byref(a)) == 256 + rows * splits * (d + 2) * 4, \
                 (batch, q_dt, kv_dt)
+
+
+def test_prepare_attend_rejects_bad_arguments_before_touching_tensors():
+    """prepare_attend: an unknown kind or a missing out tensor is refused
+    first (ValueError), before any tensor is inspected."""
+    import pytest as _pt
+    from exact_paged_causal_amd import atlas as A
+    with _pt.raises(ValueError, match="kind"):
+        A.prepare_attend("bogus", None, None, None, None, None, 0.1, out=None)
+    with _pt.raises(ValueError, match="out"):
+        A.prepare_attend("decode", None, None, None, None, None, 0.1, out=None)
