@@ -237,6 +237,24 @@ def _c_abi_call_us(torch, np, entry, args, calls=30):
     return _median_call_us(torch, np, call, calls=calls)
 
 
+def _graph10_us(torch, np, prep):
+    """Time per call of a HIP graph holding ten copies of a prepared call
+    (as a model step's layers would be captured), captured on a side stream
+    after an eager call there."""
+    side = torch.cuda.Stream()
+    with torch.cuda.stream(side):
+        prep()
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g, stream=side):
+        for _ in range(10):
+            prep()
+    torch.cuda.synchronize()
+    us = _median_call_us(torch, np, g.replay, calls=50) / 10
+    del g
+    return us
+
+
 def _arena(torch, workloads, np, w, lay):
     """Device K/V arenas of a non-regenerated workload: seeded logical pages
     scattered to their physical ids."""
@@ -552,6 +570,7 @@ def workload_report(torch, np, workloads, atlas, oracle=None):
                 q, k, v, pt, ctx, w.scale, out=out, lse=lse, workspace=ws)[0], calls=50), 2)
             prep = atlas.prepare_attend("decode", q, k, v, pt, ctx, w.scale, out=out, lse=lse, workspace=ws)
             r["prepared_us"] = round(_median_call_us(torch, np, prep, calls=50), 2)
+            r["graph10_us"] = round(_graph10_us(torch, np, prep), 2)
             if oracle is not None:
                 r["cpu_baseline"] = _oracle_single_head(w, q, out, np, oracle)
     kvb = int(w.context_lens.sum()) * w.hkv * w.head_dim * 4 * 2
@@ -561,7 +580,8 @@ def workload_report(torch, np, workloads, atlas, oracle=None):
                                       "note": "launch-latency bound (2 MiB of K/V); *_us are per Python "
                                               "call, host overhead included (c_abi_us: one C-ABI call with "
                                               "prepared arguments; prepared_us: a prepare_attend call from "
-                                              "Python); cold regenerates all 8 pages in the call"})
+                                              "Python; graph10_us: per call in a HIP graph of ten); cold "
+                                              "regenerates all 8 pages in the call"})
     # GQA short-query suffix attention (16 queries at positions 240..255).
     w = workloads.make("gqa_short_query")
     lay = workloads.page_layout(w)
@@ -579,15 +599,17 @@ def workload_report(torch, np, workloads, atlas, oracle=None):
         q, k, v, pt, ctx, w.scale, out=out, lse=lse, workspace=ws)[0], calls=50)
     prep = atlas.prepare_attend("prefill", q, k, v, pt, ctx, w.scale, out=out, lse=lse, workspace=ws)
     p_us = _median_call_us(torch, np, prep, calls=50)
+    g_us = _graph10_us(torch, np, prep)
     L = int(w.context_lens[0])
     pairs = w.hq * sum(L - w.q_len + i + 1 for i in range(w.q_len))
     rep["gqa_short_query"] = {"us": round(us, 2), "us_min": round(us_min, 2), "c_abi_us": round(c_us, 2),
-                              "prepared_us": round(p_us, 2),
+                              "prepared_us": round(p_us, 2), "graph10_us": round(g_us, 2),
                               "kv_bytes": L * w.hkv * w.head_dim * 4 * 2,
                               "flop": 4 * w.head_dim * pairs,
                               "note": "latency bound (256 KiB of K/V); us per Python call, host overhead included; "
                                       "c_abi_us: one C-ABI call with prepared arguments; prepared_us: a "
-                                      "prepare_attend call from Python"}
+                                      "prepare_attend call from Python; graph10_us: per call in a HIP graph "
+                                      "of ten"}
     if oracle is not None:
         rep["gqa_short_query"]["cpu_baseline"] = _oracle_short_query(w, lay, q, k, v, out, np, oracle, pairs)
     del k, v
