@@ -68,3 +68,43 @@ def test_graph_replays_equal_eager_calls(dtype, q_len, lens):
         torch.cuda.synchronize()
         assert torch.equal(got_o, ref_o) and torch.equal(got_l, ref_l), f"replay {rep}"
         assert torch.isfinite(scratch)
+
+
+def test_graph_of_the_allocation_free_decode():
+    """atlas_attend_decode_noalloc, whose callers are the ones that cannot
+    allocate (graph capture among them), captured after one eager call on
+    the capture stream (which looks up the library's array) and replayed
+    with new queries and lengths: every replay equals the workspace decode
+    bit for bit."""
+    import exact_paged_causal_amd as atlas
+    if os.environ.get("ATLAS_VALIDATE", "") not in ("", "0"):
+        pytest.skip("the allocation-free decode refuses validation mode")
+    print("[graph] allocation-free decode", flush=True)
+    w = workloads.Workload("graph_noalloc", seed=74, batch=3, hq=16, hkv=4, head_dim=128, page_size=16,
+                           dtype="bf16", q_len=1, context_lens=np.asarray([2500, 600, 77], np.int32),
+                           scale=1.0 / math.sqrt(128), shuffle_pages=True)
+    inp = H.build(w)
+    q = inp.q.clone()
+    ctx = inp.context_lens.clone()
+    out = torch.empty(w.batch, 1, w.hq, 128, dtype=torch.float32, device="cuda")
+    lse = torch.empty(w.batch, 1, w.hq, dtype=torch.float32, device="cuda")
+    side = torch.cuda.Stream()
+    with torch.cuda.stream(side):
+        atlas.atlas_attend_decode_noalloc(q, inp.k, inp.v, inp.page_table, ctx, w.scale, out=out, lse=lse)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g, stream=side):
+        atlas.atlas_attend_decode_noalloc(q, inp.k, inp.v, inp.page_table, ctx, w.scale, out=out, lse=lse)
+    torch.cuda.synchronize()
+    gen = torch.Generator(device="cuda")
+    gen.manual_seed(6)
+    for rep in range(3):
+        q.copy_(torch.randn(q.shape, generator=gen, device="cuda", dtype=torch.float32).to(q.dtype))
+        ctx[1] = 600 - 50 * rep
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        got_o, got_l = out.clone(), lse.clone()
+        ref_o, ref_l = atlas.atlas_attend_decode(q, inp.k, inp.v, inp.page_table, ctx, w.scale)
+        torch.cuda.synchronize()
+        assert torch.equal(got_o, ref_o) and torch.equal(got_l, ref_l), f"replay {rep}"
