@@ -211,13 +211,15 @@ int32_t atlas_attend_decode(const atlas_attn_args *args, void *stream);
 
 /*
  * Prefill / cache-backed short queries: q_len >= 1 queries per sequence, the
- * suffix of the history (requires q_len <= L_b).  bf16 with q_len >= 64 runs
+ * suffix of the history (requires q_len <= L_b).  A tiled call is one with
+ * q_len >= 64, or with q_len >= 16 and batch * q_len * max_pages_per_seq *
+ * page_size at least 2^17 (bf16) or 2^16 (fp32).  A tiled bf16 call runs
  * the tiled matrix-core kernel (query x key tiles with causal block-stop:
  * each query tile stops at the last key tile its last row can see, and with
  * a window it also skips the key tiles before its first row's window, except
  * those holding sink keys).  Its P.V product runs in fp16 with
  * fp32 accumulation, so it requires |V| <= 65504 (validation mode checks
- * this and returns ATLAS_ERR_RANGE).  fp32 with q_len >= 64 runs the same
+ * this and returns ATLAS_ERR_RANGE).  A tiled fp32 call runs the same
  * tiling on the fp16 matrix cores with every operand split into two fp16
  * parts (hi = fp16(x), lo = fp16(x - hi)) and each product taken as
  * hi.hi + lo.hi + hi.lo, which keeps fp32 accuracy (CPUAttn defines the
@@ -265,10 +267,11 @@ typedef struct atlas_attn_mods {
 /*
  * atlas_attend_prefill with modifications (mods may be NULL: no
  * modification).  Same arguments, workspace (atlas_prefill_workspace_bytes)
- * and outputs; q_len >= 1.  bf16 with q_len >= 64 runs the tiled
- * matrix-core kernel (non-causal rows take every key block of the context;
- * masked and biased elements are applied per element inside the tiles);
- * every other case runs the split-KV kernels.
+ * and outputs; q_len >= 1.  Tiled calls (as for atlas_attend_prefill) run
+ * the tiled kernels (non-causal rows take every key block of the context;
+ * a mask's fully hidden key blocks are skipped, masked and biased elements
+ * are applied per element inside the others); every other case runs the
+ * split-KV kernels.
  */
 int32_t atlas_attend_mods(const atlas_attn_args *args, const atlas_attn_mods *mods, void *stream);
 
