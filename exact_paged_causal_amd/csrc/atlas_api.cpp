@@ -190,17 +190,27 @@ int32_t check_shapes(const atlas_attn_args *a, bool decode, Plan *p)
 
     // Path: the tiled kernels for prefills with one dtype throughout
     // (window / sinks / softcap included; fp32 on split fp16 operands) from
-    // 64 queries on, and from 16 queries when the call is large enough
-    // (batch x queries x key bound at least 2^17 for bf16, 2^16 for fp32);
-    // else the split-KV kernels (matrix cores for a bf16 cache, an fp32
-    // query included; vector ALUs for fp32), whose row chunks each re-read
-    // their K/V head's keys.  Measured with 16 to 48 queries over 2048 to
-    // 32768 keys (1 and 4 sequences): the tiled kernels up to 2.8x (bf16)
-    // and 9.6x (fp32) faster (fp32, 4 x 48 queries over 32768 keys: 3877
-    // -> 405 us); below the bounds the split kernels were up to 26 %
-    // faster (one sequence of 16 fp32 queries over 2048 keys).
+    // 64 queries on, and from 2 queries when the split-KV kernels would need
+    // several row chunks per K/V head (queries x largest group above 32 rows
+    // for a bf16 cache, 16 rows per chunk; above 8 for fp32, at most 8 per
+    // chunk) and the call is large enough (batch x queries x key bound at
+    // least 2^17 for bf16, 2^16 for fp32); else the split-KV kernels
+    // (matrix cores for a bf16 cache, an fp32 query included; vector ALUs
+    // for fp32).  Each row chunk of a split kernel re-reads its K/V head's
+    // keys, so its time grows with the chunk count, while a tiled query block
+    // covers up to 256 rows in one pass over the keys.  Measured with 3 to 48
+    // queries, groups of 1, 4 and 8, over 2048 to 32768 keys (1 and 4
+    // sequences): the tiled kernels were up to 2.8x (bf16) and 9.6x (fp32)
+    // faster from 3 chunks (bf16) or 2 chunks (fp32) on (fp32, 4 x 48
+    // queries over 32768 keys: 3877 -> 405 us), and up to 47 % (bf16) and
+    // 96 % (fp32) slower with fewer chunks; below the size bounds the split
+    // kernels were up to 26 % faster (one sequence of 16 fp32 queries over
+    // 2048 keys).
     const int64_t pairs = (int64_t)a->batch * a->q_len * max_ctx;
-    const bool tile = a->q_len >= 64 || (a->q_len >= 16 && pairs >= (qb ? (INT64_C(1) << 17) : (INT64_C(1) << 16)));
+    const int64_t head_rows = (int64_t)a->q_len * gmax;
+    const bool tile = a->q_len >= 64 ||
+                      (a->q_len >= 2 && head_rows > (kvb ? 32 : 8) &&
+                       pairs >= (kvb ? (INT64_C(1) << 17) : (INT64_C(1) << 16)));
     if (!decode && qb && kvb && tile)
         p->path = Path::TiledPrefill;
     else if (!decode && qf && kvf && tile)
@@ -243,23 +253,22 @@ int32_t check_shapes(const atlas_attn_args *a, bool decode, Plan *p)
     }
 
     // Split-KV plan: rows of a K/V head per work item, then keys per split.
-    const int64_t rows_per_head = (int64_t)a->q_len * gmax;
     int rpi = 1;
     if (p->path == Path::SplitMfma) {
         rpi = 16;  // the matrix-core fold always takes 16 rows (MFMA width)
     } else {
-        while (rpi < rows_per_head && rpi < 8)
+        while (rpi < head_rows && rpi < 8)
             rpi <<= 1;
         // Few rows over short contexts: smaller row chunks spread the call
         // over more CUs (each work item's fold is a serial chain of memory
         // round trips and per-key vector work, so fewer rows per item finish
         // sooner).  Counted at the shortest spans (64 keys).
         const int64_t spans_min = (max_ctx + 63) / 64;
-        while (rpi > 1 && (int64_t)a->batch * hkv * ((rows_per_head + rpi - 1) / rpi) * spans_min < kFillItems)
+        while (rpi > 1 && (int64_t)a->batch * hkv * ((head_rows + rpi - 1) / rpi) * spans_min < kFillItems)
             rpi >>= 1;
     }
     p->rows_per_item = rpi;
-    p->n_chunks = (int)((rows_per_head + rpi - 1) / rpi);
+    p->n_chunks = (int)((head_rows + rpi - 1) / rpi);
     const int64_t items_per_split = (int64_t)a->batch * hkv * p->n_chunks;
     const int64_t max_t_by_lds = (int64_t)(atlas::kMaxSplitPages - 2) << p->page_shift;
     int64_t T;
@@ -518,6 +527,11 @@ int32_t attend(const atlas_attn_args *a, void *stream_ptr, bool decode, const Re
             k.ws_acc = reinterpret_cast<float *>(ws);
             k.ws_ml = reinterpret_cast<float *>(ws + (size_t)p.rows_total * p.max_splits * a->head_dim * sizeof(float));
         }
+        if (std::getenv("ATLAS_DEBUG"))
+            std::fprintf(stderr, "atlas: tiled prefill (%s) positions/block=%d split_blocks=%d max_splits=%d "
+                                 "workspace=%zu\n",
+                         p.path == Path::TiledPrefill ? "bf16" : "fp32", p.tiled_npos, p.split_blocks,
+                         p.max_splits, p.workspace);
         hipError_t e = p.path == Path::TiledPrefill ? atlas::launch_prefill_mfma(k, stream)
                                                      : atlas::launch_prefill_split(k, stream);
         if (e == hipSuccess && p.split_blocks > 0) {

@@ -43,6 +43,9 @@
  * void*, NULL = the null stream) and never synchronise the host, except in
  * validation mode (environment ATLAS_VALIDATE=1), which copies the device
  * page table and lengths to the host and checks them before launching.
+ * With the environment variable ATLAS_DEBUG set, each attention call prints
+ * one line to stderr naming the kernels it chose (tiled or split-KV) and
+ * their plan.
  *
  * Errors.  Every check of host-visible arguments runs before any launch: on
  * an error nothing is launched and no output is written.  The detail of the
@@ -212,8 +215,10 @@ int32_t atlas_attend_decode(const atlas_attn_args *args, void *stream);
 /*
  * Prefill / cache-backed short queries: q_len >= 1 queries per sequence, the
  * suffix of the history (requires q_len <= L_b).  A tiled call is one with
- * q_len >= 64, or with q_len >= 16 and batch * q_len * max_pages_per_seq *
- * page_size at least 2^17 (bf16) or 2^16 (fp32).  A tiled bf16 call runs
+ * q_len >= 64, or with q_len >= 2, q_len * G above 32 rows for a bf16
+ * cache or above 8 for fp32 (G = the largest number of q-heads reading one
+ * K/V head), and batch * q_len * max_pages_per_seq * page_size at least
+ * 2^17 (bf16) or 2^16 (fp32).  A tiled bf16 call runs
  * the tiled matrix-core kernel (query x key tiles with causal block-stop:
  * each query tile stops at the last key tile its last row can see, and with
  * a window it also skips the key tiles before its first row's window, except
