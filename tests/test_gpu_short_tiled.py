@@ -6,8 +6,11 @@ for fp32) and the call covers at least 2^17 (bf16) or 2^16 (fp32) query-key
 pairs; otherwise it runs the split-KV kernels.  Each case asserts which
 kernels ran (the ATLAS_DEBUG line) and checks every query row and q-head of
 every sequence against the oracle, with plain calls, per-sequence window /
-sink / softcap variants and modifications (non-causal rows, ALiBi slopes,
-mask bits).  NaN-poisoned arenas, shuffled pages; each case prints itself
+sink / softcap variants, modifications (non-causal rows, ALiBi slopes,
+mask bits), 256 q-heads over one K/V head (one query position per
+workgroup, with key splits: 65 to 115 partial states per row, so the merge
+goes past its first 64) and an uneven head map (the largest group sets the
+rows).  NaN-poisoned arenas, shuffled pages; each case prints itself
 first."""
 import math
 
@@ -58,6 +61,13 @@ CASES = [
      dict(causal=True, alibi=False, density=0.5)),
     ("bf16-g4-q6-mask-alibi", "bf16", 64, 64, 8, 2, 6, (20000,), "split",
      dict(causal=True, alibi=True, density=0.95)),
+    # one query position per workgroup (256 q-heads over one K/V head), with key splits
+    ("bf16-g256-q2-keysplits", "bf16", 64, 256, 256, 1, 2, (66000,), "tiled", {}),
+    ("f32-g256-q2-keysplits", "f32", 64, 64, 256, 1, 2, (33000,), "tiled", {}),
+    # uneven head map: groups of 5, 3 and 1 q-heads, the largest sets the rows
+    ("bf16-map5-q7", "bf16", 64, 16, 9, 3, 7, (20000,), "tiled", dict(head_map=[0, 1, 0, 2, 0, 1, 0, 0, 1])),
+    ("bf16-map5-q6", "bf16", 64, 16, 9, 3, 6, (24000,), "split", dict(head_map=[0, 1, 0, 2, 0, 1, 0, 0, 1])),
+    ("f32-map5-q2", "f32", 128, 64, 9, 3, 2, (33000,), "tiled", dict(head_map=[0, 1, 0, 2, 0, 1, 0, 0, 1])),
 ]
 
 
@@ -85,13 +95,14 @@ def test_short_query_block_matches_oracle(c, capfd, monkeypatch):
                 mask[b, np.arange(w.q_len), int(w.context_lens[b]) - w.q_len + np.arange(w.q_len)] = True
         out, lse = run_mods(inp, ex["causal"], slopes, mask)
     else:
-        out, lse = H.run(inp, entry="prefill")
+        out, lse = H.run(inp, entry="prefill", head_map=ex.get("head_map"))
     torch.cuda.synchronize()
     monkeypatch.delenv("ATLAS_DEBUG")
     err = capfd.readouterr().err
+    print(err.strip(), flush=True)
     want = "atlas: tiled prefill" if route == "tiled" else "atlas: split-KV prefill"
     assert want in err, f"{name}: expected the {route} kernels, stderr: {err!r}"
     if "causal" in ex:
         check_mods(inp, out, lse, ex["causal"], slopes, mask, name)
     else:
-        H.check_against_oracle(inp, out, lse, what=name)
+        H.check_against_oracle(inp, out, lse, head_map=ex.get("head_map"), what=name)
