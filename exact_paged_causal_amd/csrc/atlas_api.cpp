@@ -104,7 +104,7 @@ constexpr int kMinItemsVector = 2048;     // work items (8 per CU) the vector fo
 constexpr int kMinItemsMatrix = 512;      // work items (2 per CU) the other plans aim at
 constexpr int kSingleSplitKeys = 256;     // contexts up to this length take one split per row (no merge)
 constexpr int kMinSplitTokens = 128;      // shortest default split
-constexpr int kMaxSplitsPerRow = 32;      // default splits lengthen until a row has at most this many
+constexpr int kMaxSplitsPerRow = 32;      // default splits lengthen until a row has at most this many (more for calls with few items)
 constexpr int kFillItems = 512;           // work items (two per CU) below which row chunks shrink
 
 int32_t check_shapes(const atlas_attn_args *a, bool decode, Plan *p)
@@ -309,11 +309,20 @@ int32_t check_shapes(const atlas_attn_args *a, bool decode, Plan *p)
         // within run-to-run spread or a few per cent elsewhere.  Generating
         // fp32 decodes lost up to 44 % with splits of 2048 keys where 512
         // served (2 x 32768 keys 77.6 -> 112 us), hence the 512-key start.
+        // Calls with few (sequence, K/V head, row chunk) items (one or two
+        // sequences over few K/V heads) may take more than 32 splits per
+        // row, as many as two work items per CU need: their rows are few, so
+        // the merge's extra states cost little (past 64 splits a row is
+        // merged by eight waves).  Measured: one sequence of 8 fp32 q-heads
+        // over one K/V head and 131072 keys 275 -> 67 us, a bf16 one of 64
+        // q-heads 69 -> 40 us.
+        const int64_t max_splits_row =
+            std::max<int64_t>(kMaxSplitsPerRow, (kFillItems + items_per_split - 1) / items_per_split);
         auto pick = [&](int64_t start, int64_t min_items) {
             int64_t t = start;
             while (t > kMinSplitTokens && items_per_split * ((max_ctx + t - 1) / t) < min_items)
                 t /= 2;
-            while (t < kDefaultSplitTokens && (max_ctx + t - 1) / t > kMaxSplitsPerRow)
+            while (t < kDefaultSplitTokens && (max_ctx + t - 1) / t > max_splits_row)
                 t *= 2;
             return t;
         };

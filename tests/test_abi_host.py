@@ -399,8 +399,8 @@ def test_short_contexts_plan_one_split_per_row():
 
 
 def test_split_plan_depends_on_the_cache_dtype():
-    """Default splits, never shorter than 128 keys nor more than 32 per row.
-    The matrix-core fold (bf16 cache, also under an fp32 query) aims at two
+    """Default splits, never shorter than 128 keys nor (for calls with at
+    least 16 work items per split) more than 32 per row.  The matrix-core fold (bf16 cache, also under an fp32 query) aims at two
     work items per CU from 4096 keys; the vector fold (fp32 cache) keeps the
     plan for eight per CU when its splits come out 1024 keys or longer, and
     otherwise aims at two per CU from 512 keys.  8 x 32 q-heads over 8 K/V
@@ -416,6 +416,25 @@ def test_split_plan_depends_on_the_cache_dtype():
                             page_size=512 if pages == 128 else 16, max_pages_per_seq=pages, num_phys_pages=1 << 16)
             assert A.lib.atlas_decode_workspace_bytes(ctypes.byref(a)) == 256 + rows * splits * (d + 2) * 4, \
                 (batch, q_dt, kv_dt)
+
+
+def test_few_item_calls_take_more_splits_per_row():
+    """A call with few (sequence, K/V head, row chunk) items per split may
+    exceed 32 splits per row, up to what two work items per CU (512) need:
+    one sequence of 8 fp32 q-heads over one K/V head at 131072 keys takes
+    512 splits of 256 keys; a bf16 single head the same; two bf16 sequences
+    at 32768 keys 256 splits of 128; with 16 items per split (2 sequences x
+    8 K/V heads) the cap stays 32."""
+    from exact_paged_causal_amd import atlas as A
+    for q_dt, kv_dt, batch, hq, hkv, d, pages, splits in ((0, 0, 1, 8, 1, 128, 1024, 512),
+                                                         (1, 1, 1, 1, 1, 128, 1024, 512),
+                                                         (1, 1, 2, 1, 1, 64, 256, 256),
+                                                         (1, 1, 2, 8, 8, 128, 1024, 32)):
+        a = _valid_args(q_dtype=q_dt, kv_dtype=kv_dt, batch=batch, num_q_heads=hq, num_kv_heads=hkv, head_dim=d,
+                        page_size=128, max_pages_per_seq=pages, num_phys_pages=1 << 16)
+        rows = batch * hq
+        assert A.lib.atlas_decode_workspace_bytes(ctypes.byref(a)) == 256 + rows * splits * (d + 2) * 4, \
+            (q_dt, batch, hq, hkv, pages)
 
 
 def test_prepare_attend_rejects_bad_arguments_before_touching_tensors():
