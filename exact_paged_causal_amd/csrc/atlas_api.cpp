@@ -190,13 +190,16 @@ int32_t check_shapes(const atlas_attn_args *a, bool decode, Plan *p)
 
     // Path: the tiled kernels for prefills with one dtype throughout
     // (window / sinks / softcap included; fp32 on split fp16 operands) from
-    // 64 queries on, and from 2 queries when the split-KV kernels would need
+    // 64 queries on, and below that when the split-KV kernels would need
     // several row chunks per K/V head (queries x largest group above 32 rows
     // for a bf16 cache, 16 rows per chunk; above 8 for fp32, at most 8 per
     // chunk) and the call is large enough (batch x queries x key bound at
-    // least 2^17 for bf16, 2^16 for fp32); else the split-KV kernels
-    // (matrix cores for a bf16 cache, an fp32 query included; vector ALUs
-    // for fp32).  Each row chunk of a split kernel re-reads its K/V head's
+    // least 2^17, or 2^16 for fp32 with two or more queries); else the
+    // split-KV kernels (matrix cores for a bf16 cache, an fp32 query
+    // included; vector ALUs for fp32).  Decode calls always take the
+    // split-KV kernels, so that they match the fused-regeneration decode
+    // (which only those kernels implement) bit for bit; one query through
+    // the prefill entry follows the rule above.  Each row chunk of a split kernel re-reads its K/V head's
     // keys, so its time grows with the chunk count, while a tiled query block
     // covers up to 256 rows in one pass over the keys.  Measured with 3 to 48
     // queries, groups of 1, 4 and 8, over 2048 to 32768 keys (1 and 4
@@ -205,12 +208,17 @@ int32_t check_shapes(const atlas_attn_args *a, bool decode, Plan *p)
     // queries over 32768 keys: 3877 -> 405 us), and up to 47 % (bf16) and
     // 96 % (fp32) slower with fewer chunks; below the size bounds the split
     // kernels were up to 26 % faster (one sequence of 16 fp32 queries over
-    // 2048 keys).
+    // 2048 keys).  One query (1 to 16 sequences over 8192 to 131072 keys, 48
+    // to 128 q-heads over 1 or 2 K/V heads for bf16, 16 to 128 over 1 to 8
+    // for fp32): the tiled kernels up to 2.0x (bf16, 8 x 128 q-heads over
+    // one K/V head at 32768 keys, 86.9 -> 46.5 us) and 2.3x faster (fp32) at
+    // 2^17 pairs and above (within 5 % either way on the largest fp32
+    // calls, 8 to 16 sequences of 131072 keys over 4 or 8 K/V heads), and up
+    // to 93 % slower (fp32) below: their fixed cost is spread over few rows.
     const int64_t pairs = (int64_t)a->batch * a->q_len * max_ctx;
     const int64_t head_rows = (int64_t)a->q_len * gmax;
-    const bool tile = a->q_len >= 64 ||
-                      (a->q_len >= 2 && head_rows > (kvb ? 32 : 8) &&
-                       pairs >= (kvb ? (INT64_C(1) << 17) : (INT64_C(1) << 16)));
+    const int64_t min_pairs = (kvb || a->q_len == 1) ? (INT64_C(1) << 17) : (INT64_C(1) << 16);
+    const bool tile = a->q_len >= 64 || (head_rows > (kvb ? 32 : 8) && pairs >= min_pairs);
     if (!decode && qb && kvb && tile)
         p->path = Path::TiledPrefill;
     else if (!decode && qf && kvf && tile)

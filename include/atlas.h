@@ -208,6 +208,9 @@ size_t atlas_prefill_workspace_bytes(const atlas_attn_args *args);
  * for all q-heads of that K/V head, and a log-sum-exp merge combines the
  * states of each (sequence, q-head) in a fixed span order (deterministic:
  * the same arguments give the same bits, whatever the physical page order).
+ * Decode always runs these split-KV kernels, so that its results equal
+ * those of atlas_attend_decode_regen bit for bit; a single query through
+ * atlas_attend_prefill may take the tiled kernels instead (see there).
  * Arguments as described above; workspace >= atlas_decode_workspace_bytes().
  */
 int32_t atlas_attend_decode(const atlas_attn_args *args, void *stream);
@@ -215,10 +218,10 @@ int32_t atlas_attend_decode(const atlas_attn_args *args, void *stream);
 /*
  * Prefill / cache-backed short queries: q_len >= 1 queries per sequence, the
  * suffix of the history (requires q_len <= L_b).  A tiled call is one with
- * q_len >= 64, or with q_len >= 2, q_len * G above 32 rows for a bf16
- * cache or above 8 for fp32 (G = the largest number of q-heads reading one
- * K/V head), and batch * q_len * max_pages_per_seq * page_size at least
- * 2^17 (bf16) or 2^16 (fp32).  A tiled bf16 call runs
+ * q_len >= 64, or with q_len * G above 32 rows for a bf16 cache or above 8
+ * for fp32 (G = the largest number of q-heads reading one K/V head) and
+ * batch * q_len * max_pages_per_seq * page_size at least 2^17 (2^16 for
+ * fp32 with q_len >= 2).  A tiled bf16 call runs
  * the tiled matrix-core kernel (query x key tiles with causal block-stop:
  * each query tile stops at the last key tile its last row can see, and with
  * a window it also skips the key tiles before its first row's window, except

@@ -1,9 +1,11 @@
-"""GPU parity of short query blocks (2 to 63 queries per sequence) on both
+"""GPU parity of short query blocks (1 to 63 queries per sequence) on both
 sides of the tiled-kernel routing bound.  A prefill of fewer than 64 queries
 runs the tiled kernels when the split-KV kernels would need several row
 chunks per K/V head (queries x group above 32 rows for a bf16 cache, above 8
-for fp32) and the call covers at least 2^17 (bf16) or 2^16 (fp32) query-key
-pairs; otherwise it runs the split-KV kernels.  Each case asserts which
+for fp32) and the call covers at least 2^17 query-key pairs (2^16 for fp32
+with two or more queries); otherwise it runs the split-KV kernels.  The
+decode entry always runs the split-KV kernels, also where a single query
+through the prefill entry is tiled.  Each case asserts which
 kernels ran (the ATLAS_DEBUG line) and checks every query row and q-head of
 every sequence against the oracle, with plain calls, per-sequence window /
 sink / softcap variants, modifications (non-causal rows, ALiBi slopes,
@@ -68,6 +70,13 @@ CASES = [
     ("bf16-map5-q7", "bf16", 64, 16, 9, 3, 7, (20000,), "tiled", dict(head_map=[0, 1, 0, 2, 0, 1, 0, 0, 1])),
     ("bf16-map5-q6", "bf16", 64, 16, 9, 3, 6, (24000,), "split", dict(head_map=[0, 1, 0, 2, 0, 1, 0, 0, 1])),
     ("f32-map5-q2", "f32", 128, 64, 9, 3, 2, (33000,), "tiled", dict(head_map=[0, 1, 0, 2, 0, 1, 0, 0, 1])),
+    # one query through the prefill entry: tiled from 2^17 pairs for either dtype
+    ("bf16-g64-q1", "bf16", 128, 64, 64, 1, 1, (70000, 70000), "tiled", {}),
+    ("bf16-g64-q1-small", "bf16", 64, 64, 64, 1, 1, (32768, 32768), "split", {}),
+    ("f32-g32-q1", "f32", 64, 128, 32, 1, 1, (70000, 70000), "tiled", {}),
+    ("f32-g32-q1-small", "f32", 64, 16, 32, 1, 1, (32768, 32768), "split", {}),
+    ("bf16-g48-q1-var", "bf16", 128, 16, 48, 1, 1, (140000,), "tiled",
+     dict(window=(30000,), sinks=(3,), softcap=(20.0,))),
 ]
 
 
@@ -106,3 +115,28 @@ def test_short_query_block_matches_oracle(c, capfd, monkeypatch):
         check_mods(inp, out, lse, ex["causal"], slopes, mask, name)
     else:
         H.check_against_oracle(inp, out, lse, head_map=ex.get("head_map"), what=name)
+
+
+@pytest.mark.parametrize("dt", ["bf16", "f32"])
+def test_decode_entry_keeps_split_kernels(dt, capfd, monkeypatch):
+    """The shape that the prefill entry runs tiled (one query, 64 or 32
+    q-heads over one K/V head, 2 x 70000 keys) runs the split-KV kernels
+    through the decode entry; both match the oracle."""
+    hq = 64 if dt == "bf16" else 32
+    w = workloads.Workload(f"short_decode_{dt}", seed=880, batch=2, hq=hq, hkv=1, head_dim=64, page_size=64,
+                           dtype=dt, q_len=1, context_lens=np.asarray((70000, 70000), np.int32), scale=0.125,
+                           shuffle_pages=True)
+    print(f"[short-tiled] decode entry {dt}", flush=True)
+    inp = H.build(w, poison=True)
+    capfd.readouterr()
+    monkeypatch.setenv("ATLAS_DEBUG", "1")
+    out_d, lse_d = H.run(inp, entry="decode")
+    out_p, lse_p = H.run(inp, entry="prefill")
+    torch.cuda.synchronize()
+    monkeypatch.delenv("ATLAS_DEBUG")
+    err = capfd.readouterr().err
+    print(err.strip(), flush=True)
+    lines = err.strip().splitlines()
+    assert "atlas: split-KV decode" in lines[0] and "atlas: tiled prefill" in lines[1], err
+    H.check_against_oracle(inp, out_d, lse_d, what=f"decode entry {dt}")
+    H.check_against_oracle(inp, out_p, lse_p, what=f"prefill entry {dt}")
