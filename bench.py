@@ -28,7 +28,10 @@ causal and non-causal, a block-diagonal document mask) under "next": "mods";
 the long-context decode through the hot-page cache (atlas_cache_plan ->
 regenerate admitted pages -> decode with the rest generated in the kernel)
 under "next": "hot_cache"; short prefill chunks behind a 32768-token history
-(the tiled kernels with key splits) under "next": "chunked_prefill".
+(the tiled kernels with key splits) under "next": "chunked_prefill";
+single-sequence decodes over 131072 keys (many splits per row) and single
+queries from 128 q-heads per K/V head (decode and prefill entries) under
+"next": "few_item".
 A plain 256 MiB device-to-device copy is timed last as context for the HBM
 figures ("hbm_context"); the small workloads also report one C-ABI call
 with prepared arguments ("c_abi_us") beside the Python-call time.
@@ -497,6 +500,42 @@ def chunked_prefill_report(torch, np, workloads, atlas, calls=10):
         rep[f"{dtype}_q{q_len}_L{L}"] = {"us": round(us, 1), "flop": fl, "TFLOPs": round(fl / us / 1e6, 1)}
         del k, v
     rep["note"] = "tiled prefill with key splits + LSE merge (workgroups per query block x splits)"
+    return rep
+
+
+def few_item_report(torch, np, workloads, atlas, calls=10):
+    """Calls with few (sequence, K/V head) work items over long contexts
+    (D=128, pages of 128): single-sequence decodes over 131072 keys, which
+    the split plan spreads over up to 512 splits per row (merged by eight
+    waves per row past 64), and 8 single queries from 128 q-heads over one
+    K/V head at 32768 keys through the decode entry (split-KV folds) and
+    the prefill entry (tiled kernels).  GB/s of visible K/V."""
+    rep = {}
+    for name, dtype, entry, B, hq, hkv, L in (("decode_f32_h8x1_B1_L131072", "f32", "decode", 1, 8, 1, 131072),
+                                             ("decode_bf16_h32x8_B1_L131072", "bf16", "decode", 1, 32, 8, 131072),
+                                             ("decode_bf16_h64x1_B1_L131072", "bf16", "decode", 1, 64, 1, 131072),
+                                             ("decode_bf16_h128x1_B8_L32768", "bf16", "decode", 8, 128, 1, 32768),
+                                             ("prefill_q1_bf16_h128x1_B8_L32768", "bf16", "prefill", 8, 128, 1,
+                                              32768)):
+        w = workloads.make("causal_prefill", dtype=dtype, q_len=1, batch=B, hq=hq, hkv=hkv,
+                           context_lens=np.full(B, L, np.int32))
+        lay = workloads.page_layout(w)
+        k, v = _arena(torch, workloads, np, w, lay)
+        q = workloads.randn(workloads.query_shape(w), seed=3, dtype=dtype, device="cuda")
+        pt = torch.from_numpy(lay.page_table).cuda()
+        ctx = torch.from_numpy(w.context_lens).cuda()
+        args, _ = atlas.make_attn_args(q, k, v, pt, ctx, w.scale)
+        wsb = atlas.atlas_decode_workspace_bytes(args) if entry == "decode" else atlas.atlas_prefill_workspace_bytes(args)
+        ws = torch.empty(max(wsb, 1), dtype=torch.uint8, device="cuda")
+        out = torch.empty(workloads.query_shape(w), dtype=torch.float32, device="cuda")
+        lse = torch.empty(B, 1, hq, dtype=torch.float32, device="cuda")
+        fn = atlas.atlas_attend_decode if entry == "decode" else atlas.atlas_attend_prefill
+        call = lambda: fn(q, k, v, pt, ctx, w.scale, out=out, lse=lse, workspace=ws)
+        us = _median_call_us(torch, np, call, calls=calls)
+        kv_bytes = 2.0 * B * L * hkv * w.head_dim * (4 if dtype == "f32" else 2)
+        rep[name] = {"us": round(us, 1), "GBps": round(kv_bytes / us / 1e3, 1)}
+        del k, v
+    rep["note"] = "few work items per split: plan of up to 512 splits per row; one query, 128 q-heads per K/V head"
     return rep
 
 
@@ -1035,6 +1074,7 @@ def main():
             result["next"]["prefill_f32"] = prefill_f32_report(torch, np, workloads, atlas)
             result["next"]["mods"] = mods_report(torch, np, p, atlas)
             result["next"]["chunked_prefill"] = chunked_prefill_report(torch, np, workloads, atlas)
+            result["next"]["few_item"] = few_item_report(torch, np, workloads, atlas)
         print("bench: fused regeneration timed", file=sys.stderr, flush=True)
     if not args.no_workloads:
         # Every synthetic workload's throughput (the long-context decode and
