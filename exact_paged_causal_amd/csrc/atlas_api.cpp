@@ -298,8 +298,9 @@ int32_t check_shapes(const atlas_attn_args *a, bool decode, Plan *p)
         // Long spans amortise a work item's set-up (page ids, query, final
         // combine); shorter ones only while the call would have fewer work
         // items than it needs, down to 128 keys and to at most 32 splits per
-        // row: past those, the per-split set-up and the merge's traffic
-        // cost more than the extra work items gain.  The matrix-core fold
+        // row (more for calls with few work items, below): past those, the
+        // per-split set-up and the merge's traffic cost more than the extra
+        // work items gain.  The matrix-core fold
         // (bf16 K/V) starts at 4096 keys and wants two items per CU.  The
         // vector fold (fp32 K/V) keeps the plan for eight items per CU from
         // 4096 keys when that plan's splits are 1024 keys or longer (large
