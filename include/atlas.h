@@ -205,7 +205,8 @@ size_t atlas_prefill_workspace_bytes(const atlas_attn_args *args);
  * equal full-K/V attention; the CPUAttn README ("Operator model") allows a
  * split over keys only with a structured merge.  Here each (sequence, K/V
  * head, span of keys) work item folds its keys into an online-softmax state
- * for all q-heads of that K/V head, and a log-sum-exp merge combines the
+ * for the q-heads of that K/V head (up to 16 of them per work item on the
+ * matrix cores, 8 on the vector ALUs), and a log-sum-exp merge combines the
  * states of each (sequence, q-head) in a fixed span order (deterministic:
  * the same arguments give the same bits, whatever the physical page order).
  * Decode always runs these split-KV kernels, so that its results equal
@@ -218,7 +219,7 @@ int32_t atlas_attend_decode(const atlas_attn_args *args, void *stream);
 /*
  * Prefill / cache-backed short queries: q_len >= 1 queries per sequence, the
  * suffix of the history (requires q_len <= L_b).  A tiled call is one with
- * q_len >= 64, or with q_len * G above 32 rows for a bf16 cache or above 8
+ * q and K/V of one dtype and q_len >= 64, or with q_len * G above 32 rows for a bf16 cache or above 8
  * for fp32 (G = the largest number of q-heads reading one K/V head) and
  * batch * q_len * max_pages_per_seq * page_size at least 2^17 (2^16 for
  * fp32 with q_len >= 2).  A tiled bf16 call runs
